@@ -1,0 +1,176 @@
+"""CPU oracle for the AsyncSpade sparse decode step (fp64, plain, slow).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` may import this package.  It shares no
+code with the HIP library in ``query_aware_sparse_amd`` and never calls it.
+
+The arithmetic lives in ``asp_oracle.c`` (compiled with gcc, no fast-math);
+this module only builds it, marshals numpy arrays through ctypes and shapes
+the results.  Each wrapper names the definition it follows; the C file states
+the readings adopted where the pages are silent.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "asp_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libasp_oracle.so")
+
+KV_BF16 = 0
+KV_F32 = 1
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, IEEE semantics kept)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    Dbl = ctypes.c_double
+    lib.oracle_num_threads.restype = I
+    lib.oracle_predict_one.argtypes = [I, I, I, Dbl, P, P, P, P, P, P]
+    lib.oracle_predict_one.restype = I
+    lib.oracle_predict.argtypes = [I, I, I, I, P, P, P, Dbl, P]
+    lib.oracle_predict.restype = I
+    lib.oracle_push.argtypes = [I, I, I, I, P, P, P, P]
+    lib.oracle_push.restype = None
+    lib.oracle_score.argtypes = [I, I, I, I, I, I, P, P, P, P]
+    lib.oracle_score.restype = None
+    lib.oracle_select.argtypes = [I, I, I, I, P, P, P, P]
+    lib.oracle_select.restype = None
+    lib.oracle_attend.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P]
+    lib.oracle_attend.restype = I
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _kv(a: np.ndarray):
+    """K/V arrays: float32 values, or uint16 raw bfloat16 bit patterns."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float32:
+        return a, KV_F32
+    if a.dtype == np.uint16 or a.dtype == np.int16:
+        return a.view(np.uint16), KV_BF16
+    raise TypeError("K/V must be float32 or uint16 (bfloat16 bits), got %s" % a.dtype)
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def predict_one(lags, W: int, lam: float):
+    """Predictor for one head.  ``lags[j]`` is q_{t-j} (row 0 newest).
+
+    Returns (q_pred[D], windows list, beta[nw][p], alpha[nw][p]) in fp64.
+    """
+    lags = _c(lags, np.float64)
+    n, D = lags.shape
+    q = np.zeros(D, np.float64)
+    win = np.zeros(3, np.int32)
+    nw = np.zeros(1, np.int32)
+    beta = np.zeros((3, W), np.float64)
+    alpha = np.zeros((3, W), np.float64)
+    rc = _load().oracle_predict_one(n, D, W, float(lam), _ptr(lags) if n else None, _ptr(q),
+                                    _ptr(win), _ptr(nw), _ptr(beta), _ptr(alpha))
+    if rc != 0:
+        raise ArithmeticError("oracle_predict_one: singular ridge system")
+    k = int(nw[0])
+    windows = [int(w) for w in win[:k]]
+    betas = [beta[i, : windows[i] - 1].copy() for i in range(k)]
+    alphas = [alpha[i, : windows[i] - 1].copy() for i in range(k)]
+    return q, windows, betas, alphas
+
+
+def predict(q_hist, newest, length, lam: float):
+    """q_hist[B][Hq][W][D] fp32 ring, newest[B], len[B] -> q_pred[B][Hq][D] fp64."""
+    q_hist = _c(q_hist, np.float32)
+    B, Hq, W, D = q_hist.shape
+    newest = _c(newest, np.int32)
+    length = _c(length, np.int32)
+    out = np.zeros((B, Hq, D), np.float64)
+    rc = _load().oracle_predict(B, Hq, W, D, _ptr(q_hist), _ptr(newest), _ptr(length), float(lam), _ptr(out))
+    if rc != 0:
+        raise ArithmeticError("oracle_predict: singular ridge system")
+    return out
+
+
+def push(q_cur, q_hist, newest, length):
+    """Returns (q_hist, newest, len) after pushing q_cur[B][Hq][D]; inputs untouched."""
+    q_hist = np.array(q_hist, dtype=np.float32, copy=True, order="C")
+    newest = np.array(newest, dtype=np.int32, copy=True)
+    length = np.array(length, dtype=np.int32, copy=True)
+    q_cur = _c(q_cur, np.float32)
+    B, Hq, W, D = q_hist.shape
+    _load().oracle_push(B, Hq, W, D, _ptr(q_cur), _ptr(q_hist), _ptr(newest), _ptr(length))
+    return q_hist, newest, length
+
+
+def score(q_pred, k, seq_lens):
+    """q_pred[B][Hq][D] fp32, K[B][Hkv][T_cap][D] -> scores[B][Hkv][T_cap] fp64 (NaN past seq_len)."""
+    q_pred = _c(q_pred, np.float32)
+    k, kvd = _kv(k)
+    B, Hkv, T_cap, D = k.shape
+    Hq = q_pred.shape[1]
+    seq_lens = _c(seq_lens, np.int32)
+    out = np.empty((B, Hkv, T_cap), np.float64)
+    _load().oracle_score(B, Hq, Hkv, D, T_cap, kvd, _ptr(q_pred), _ptr(k), _ptr(seq_lens), _ptr(out))
+    return out
+
+
+def select(scores, seq_lens, C: int):
+    """scores[B][Hkv][T_cap] (any float dtype, widened to fp64) -> (idx[B][Hkv][C], n_sel[B][Hkv])."""
+    scores = _c(scores, np.float64)
+    B, Hkv, T_cap = scores.shape
+    seq_lens = _c(seq_lens, np.int32)
+    idx = np.empty((B, Hkv, C), np.int32)
+    n_sel = np.empty((B, Hkv), np.int32)
+    _load().oracle_select(B, Hkv, T_cap, int(C), _ptr(scores), _ptr(seq_lens), _ptr(idx), _ptr(n_sel))
+    return idx, n_sel
+
+
+def attend(q, k, v, idx, n_sel):
+    """q[B][Hq][D] fp32, K/V[B][Hkv][T_cap][D], idx[B][Hkv][C], n_sel[B][Hkv] -> out[B][Hq][D] fp64."""
+    q = _c(q, np.float32)
+    k, kvd = _kv(k)
+    v, kvd2 = _kv(v)
+    if kvd != kvd2:
+        raise TypeError("K and V must share a dtype")
+    B, Hkv, T_cap, D = k.shape
+    Hq = q.shape[1]
+    idx = _c(idx, np.int32)
+    C = idx.shape[2]
+    n_sel = _c(n_sel, np.int32)
+    out = np.empty((B, Hq, D), np.float64)
+    rc = _load().oracle_attend(B, Hq, Hkv, D, T_cap, kvd, C, _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
+                               _ptr(n_sel), _ptr(out))
+    if rc != 0:
+        raise IndexError("oracle_attend: selected index outside [0, T_cap)")
+    return out
