@@ -1,0 +1,191 @@
+/*
+ * asp.h -- C ABI of libasp.so, the MI355X (gfx950) AsyncSpade sparse decode step.
+ *
+ * The step predicts each query head's next query from a ring of its recent
+ * queries, scores every cached key of each KV head against the prediction,
+ * keeps the top-C tokens per (sequence, KV head), and runs decode attention
+ * with the actual query over only those tokens.  Selection for the next step
+ * can run on a second HIP stream while this step's attention runs.
+ *
+ * Sources: [card] the Hugging Face dataset card "Reproduction: AsyncSpade --
+ * Efficient Test-Time Scaling with Asynchronous Sparse Decoding"; [summary] the
+ * atlas.scime.ai research-map page on AsyncSpade; [abstract] the arXiv
+ * 2510.07486 abstract.  Where the pages leave a step open, the reading taken is
+ * stated at the entry point that implements it.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers owned by the caller, dense and
+ *    row-major in the layout given.  K and V base pointers must be 16-byte
+ *    aligned; float arrays 4-byte aligned.
+ *  - A "unit" is one (sequence b, KV head g); G = n_q_heads / n_kv_heads query
+ *    heads h = g*G .. g*G+G-1 share KV head g.
+ *  - The library allocates nothing, frees nothing, keeps no state between calls
+ *    and never waits on the host: work is enqueued on the given stream(s) and
+ *    the call returns.  Calls are re-entrant; two calls that write the same
+ *    buffers (or share a workspace) must be ordered by the caller.
+ *  - Arguments are validated on the host before anything is enqueued; on any
+ *    error nothing is enqueued.  Values that live in device memory (seq_lens,
+ *    hist_newest, hist_len, idx, n_sel) cannot be checked on the host: the
+ *    kernels clamp them into range (a length to [0, t_cap], a ring slot modulo
+ *    W, a count to [0, W] or [0, C]; an index outside [0, t_cap) is skipped),
+ *    so a bad value gives unspecified results but never an out-of-bounds access.
+ *  - ASP_ERR_HIP is returned when a kernel launch or an event/stream call fails.
+ *  - No C++ exception crosses this interface.
+ */
+#ifndef ASP_H
+#define ASP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ASP_OK = 0,
+  ASP_ERR_INVALID_ARG = 1, /* a dimension, config value or pointer is invalid */
+  ASP_ERR_UNSUPPORTED = 2, /* valid in principle, not implemented (e.g. head_dim 96) */
+  ASP_ERR_WORKSPACE = 3,   /* ws is NULL or ws_bytes < asp_workspace_size(...) */
+  ASP_ERR_HIP = 4          /* a HIP launch / event / stream call failed */
+} asp_status;
+
+typedef enum { ASP_KV_BF16 = 0, ASP_KV_F32 = 1 } asp_kv_dtype;
+
+/* Problem shape.  batch >= 0 (0 is a no-op); n_q_heads % n_kv_heads == 0 with
+ * G in {1, 2, 4, 8}; head_dim in {64, 128}; 1 <= t_cap <= 4194304 (the
+ * allocated token stride of K and V); kv_dtype an asp_kv_dtype. */
+typedef struct {
+  int32_t batch;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t t_cap;
+  int32_t kv_dtype;
+} asp_dims;
+
+/* Method configuration.  window W: ring length, a multiple of 4 in [4, 64];
+ * top_c C: tokens kept per unit, 1 <= C <= t_cap; lambda: ridge penalty,
+ * finite and > 0. */
+typedef struct {
+  int32_t window;
+  int32_t top_c;
+  double lambda;
+} asp_cfg;
+
+typedef enum {
+  ASP_OP_PUSH = 0,
+  ASP_OP_PREDICT = 1,
+  ASP_OP_SCORE = 2,
+  ASP_OP_SELECT = 3,
+  ASP_OP_DECODE = 4,
+  ASP_OP_STEP = 5
+} asp_op;
+
+/* Bytes of device workspace the entry point for `op` needs (0 if none), or 0
+ * when dims/cfg are invalid.  Host only. */
+size_t asp_workspace_size(const asp_dims* dims, const asp_cfg* cfg, asp_op op);
+
+/* Static English text for a status code.  Host only; never NULL. */
+const char* asp_status_string(asp_status status);
+
+/* Ring push (the window of recent queries slides by one; [summary], summary
+ * paragraph).  q_cur[B][Hq][D] fp32 is written into slot
+ * (hist_newest[b] + 1) mod W of q_hist[B][Hq][W][D] fp32; hist_newest[b]
+ * becomes that slot and hist_len[b] becomes min(hist_len[b] + 1, W).  Lag j
+ * of sequence b is slot (hist_newest[b] - j) mod W.  An empty ring is
+ * hist_len = 0 with any hist_newest. */
+asp_status asp_push_query(const asp_dims* dims, const asp_cfg* cfg, const float* q_cur, float* q_hist,
+                          int32_t* hist_newest, int32_t* hist_len, hipStream_t stream);
+
+/* Next-query prediction ([summary] "Approach"; [abstract], first component;
+ * [card] "What reproduces": linear one-step-ahead ridge prediction over a
+ * recent window).  For every (b, h), from the n = hist_len[b] queries in the
+ * ring (q_t newest):
+ *   windows: w in {W, W/2, W/4} with 2 <= w <= n;
+ *   per window, p = w - 1 scalar lag weights beta solve the ridge problem
+ *     q_t ~ sum_{j=1..p} beta_j q_{t-j} over the D coordinates, i.e.
+ *     (Gram(q_{t-1..t-p}) + lambda I) beta = (<q_{t-j}, q_t>)_j;
+ *   alpha = softmax(beta); q_hat_w = sum_j alpha_j q_{t+1-j};
+ *   q_pred = mean over the windows of q_hat_w;
+ *   no window (n = 1): q_pred = q_t; n = 0: q_pred = 0.
+ * The Gram matrix and the solve are computed in fp64 (one Cholesky factor
+ * serves all windows: a smaller window's system is a leading block).
+ * Output q_pred[B][Hq][D] fp32. */
+asp_status asp_predict_query(const asp_dims* dims, const asp_cfg* cfg, const float* q_hist,
+                             const int32_t* hist_newest, const int32_t* hist_len, float* q_pred,
+                             hipStream_t stream);
+
+/* Token-level key scoring ([summary] "Approach"; [abstract]: token-level, not
+ * page-level, selection).  For i < seq_lens[b]:
+ *   scores[b][g][i] = max over the G query heads h of g of q_pred[b][h] . K[b][g][i]
+ * accumulated in fp32 (no 1/sqrt(D): a ranking is scale-free).  Entries at
+ * i >= seq_lens[b] are not written.  q_pred[B][Hq][D] fp32,
+ * k[B][Hkv][t_cap][D] in dims->kv_dtype, scores[B][Hkv][t_cap] fp32. */
+asp_status asp_score_keys(const asp_dims* dims, const float* q_pred, const void* k, const int32_t* seq_lens,
+                          float* scores, hipStream_t stream);
+
+/* Exact top-C selection per unit ([card] "Key finding": C = 2k tokens; [summary]
+ * "Key results").  C_eff = min(C, seq_lens[b]); the C_eff tokens i < seq_lens[b]
+ * that come first when ordered by score descending, then index ascending (ties
+ * go to the lower index; NaN ranks as -inf; -0 ties with +0), are written to
+ * idx[b][g][0..C_eff) in ascending index order, idx[b][g][C_eff..C) = -1, and
+ * n_sel[b][g] = C_eff.  scores[B][Hkv][t_cap] fp32, idx[B][Hkv][C] int32,
+ * n_sel[B][Hkv] int32.  ws/ws_bytes: asp_workspace_size(ASP_OP_SELECT) bytes
+ * (NULL allowed when that is 0). */
+asp_status asp_select_topc(const asp_dims* dims, const asp_cfg* cfg, const float* scores, const int32_t* seq_lens,
+                           int32_t* idx, int32_t* n_sel, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Sparse decode attention over the selected tokens ([card] "Layout" and "Key
+ * finding": attention over the top-C tokens only).  For every (b, h), with
+ * g = h / G and S = idx[b][g][0..n_sel[b][g]):
+ *   out[b][h] = sum_{i in S} exp(s_i - m) V[b][g][i] / sum_{i in S} exp(s_i - m),
+ *   s_i = q[b][h] . K[b][g][i] / sqrt(D), m = max s_i;
+ * out = 0 when S is empty.  Accumulation is fp32 (online softmax over
+ * split-K partials merged by log-sum-exp).  q[B][Hq][D] fp32, k/v
+ * [B][Hkv][t_cap][D] in dims->kv_dtype, out[B][Hq][D] fp32.
+ * ws/ws_bytes: asp_workspace_size(ASP_OP_DECODE) bytes. */
+asp_status asp_sparse_decode(const asp_dims* dims, const asp_cfg* cfg, const float* q, const void* k, const void* v,
+                             const int32_t* idx, const int32_t* n_sel, float* out, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
+
+/* One decode step of one layer ([abstract], second component; [summary]
+ * "Approach": selection for the next step is taken off the decode critical
+ * path and overlapped with the current step's attention).
+ *
+ * Pipelined mode (idx_cur != NULL): attention with the actual query q_cur over
+ * the selection idx_cur/n_sel_cur (made by the previous step) writes out; and,
+ * independently, q_cur is pushed into the ring, the next query is predicted,
+ * keys are scored and the next step's selection is written to
+ * idx_next/n_sel_next.
+ *  - sel_stream NULL or equal to attn_stream: everything runs in that order on
+ *    attn_stream; the events are ignored (may be NULL).
+ *  - otherwise: q_ready is recorded on attn_stream (after whatever produced
+ *    q_cur) and sel_stream waits for it; attn_stream waits for idx_cur_ready
+ *    when it is not NULL; the attention runs on attn_stream and the selection
+ *    work on sel_stream, concurrently; idx_next_ready is recorded on
+ *    sel_stream when not NULL.  q_ready must be a valid event.  The caller
+ *    swaps idx/n_sel buffers and events between steps; because sel_stream
+ *    waits for q_ready, the selection of step t never overwrites the buffer
+ *    that step t-1's attention read.
+ * Bootstrap mode (idx_cur == NULL): everything runs on attn_stream: push,
+ * predict, score, select into idx_next, then attention over idx_next.
+ * Results of both modes do not depend on the stream arrangement (the kernels
+ * are deterministic).
+ * Shapes as in the entry points above; ws/ws_bytes:
+ * asp_workspace_size(ASP_OP_STEP) bytes, used by both streams (disjoint
+ * regions), so it must not be shared with a concurrent step. */
+asp_status asp_step(const asp_dims* dims, const asp_cfg* cfg, const float* q_cur, float* q_hist,
+                    int32_t* hist_newest, int32_t* hist_len, const void* k, const void* v,
+                    const int32_t* seq_lens, const int32_t* idx_cur, const int32_t* n_sel_cur,
+                    int32_t* idx_next, int32_t* n_sel_next, float* out, void* ws, size_t ws_bytes,
+                    hipStream_t attn_stream, hipStream_t sel_stream, hipEvent_t q_ready,
+                    hipEvent_t idx_cur_ready, hipEvent_t idx_next_ready);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ASP_H */

@@ -340,7 +340,7 @@ int oracle_attend(int B, int Hq, int Hkv, int D, int T_cap, int kv_dtype, int C,
     for (int j = 0; j < n; ++j) if (sel[j] < 0 || sel[j] >= T_cap) bad = 1;
     if (bad) { rc = -1; continue; }
     const float* qh = q + (size_t)uh * D;
-    double* s = (double*)malloc(sizeof(double) * (size_t)n);
+    double* s = (double*)malloc(sizeof(double) * (size_t)(unsigned)n);
     double m = -INFINITY;
     for (int j = 0; j < n; ++j) {
       double acc = 0.0;

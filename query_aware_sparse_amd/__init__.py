@@ -1,1 +1,254 @@
-# empty
+"""Python binding of libasp.so, the MI355X (gfx950) AsyncSpade sparse decode step.
+
+Argument marshalling only: every function below checks tensor shapes, dtypes
+and devices, then calls the C entry point of the same name (include/asp.h) on
+raw device pointers and a HIP stream.  All arithmetic runs in the HIP kernels.
+PyTorch supplies device memory and streams.  There is no fallback: if the HIP
+library is not built, every call raises ``AspError``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "AspError", "Dims", "Cfg", "HipEvent", "library_path", "load",
+    "OP_PUSH", "OP_PREDICT", "OP_SCORE", "OP_SELECT", "OP_DECODE", "OP_STEP",
+    "KV_BF16", "KV_F32",
+    "asp_workspace_size", "asp_status_string", "asp_push_query", "asp_predict_query", "asp_score_keys",
+    "asp_select_topc", "asp_sparse_decode", "asp_step",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libasp.so")
+
+OP_PUSH, OP_PREDICT, OP_SCORE, OP_SELECT, OP_DECODE, OP_STEP = range(6)
+KV_BF16, KV_F32 = 0, 1
+_STATUS_NAMES = {0: "ASP_OK", 1: "ASP_ERR_INVALID_ARG", 2: "ASP_ERR_UNSUPPORTED", 3: "ASP_ERR_WORKSPACE",
+                 4: "ASP_ERR_HIP"}
+
+
+class AspError(RuntimeError):
+    def __init__(self, msg: str, status: Optional[int] = None):
+        super().__init__(msg)
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    """asp_dims: batch, n_q_heads, n_kv_heads, head_dim, t_cap, kv_dtype."""
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("t_cap", ctypes.c_int32), ("kv_dtype", ctypes.c_int32)]
+
+    @property
+    def group(self) -> int:
+        return self.n_q_heads // self.n_kv_heads
+
+
+class Cfg(ctypes.Structure):
+    """asp_cfg: window (ring length W), top_c (C), lam (ridge lambda)."""
+    _fields_ = [("window", ctypes.c_int32), ("top_c", ctypes.c_int32), ("lam", ctypes.c_double)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libasp.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise AspError("libasp.so is not built (%s); run __graft_entry__.build()" % _LIB_PATH)
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    D, C = ctypes.POINTER(Dims), ctypes.POINTER(Cfg)
+    lib.asp_workspace_size.argtypes = [D, C, ctypes.c_int]
+    lib.asp_workspace_size.restype = SZ
+    lib.asp_status_string.argtypes = [ctypes.c_int]
+    lib.asp_status_string.restype = ctypes.c_char_p
+    lib.asp_push_query.argtypes = [D, C, P, P, P, P, P]
+    lib.asp_predict_query.argtypes = [D, C, P, P, P, P, P]
+    lib.asp_score_keys.argtypes = [D, P, P, P, P, P]
+    lib.asp_select_topc.argtypes = [D, C, P, P, P, P, P, SZ, P]
+    lib.asp_sparse_decode.argtypes = [D, C, P, P, P, P, P, P, P, SZ, P]
+    lib.asp_step.argtypes = [D, C, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P, P, P, P, P]
+    for name in ("asp_push_query", "asp_predict_query", "asp_score_keys", "asp_select_topc",
+                 "asp_sparse_decode", "asp_step"):
+        getattr(lib, name).restype = I32
+    _lib = lib
+    return lib
+
+
+# ----------------------------------------------------------------------------- helpers
+
+def _stream_handle(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t: torch.Tensor, name: str, shape, dtype):
+    if not isinstance(t, torch.Tensor):
+        raise AspError("%s must be a torch.Tensor" % name)
+    if not t.is_cuda:
+        raise AspError("%s must be a device tensor" % name)
+    if t.dtype != dtype:
+        raise AspError("%s must have dtype %s, got %s" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise AspError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise AspError("%s must be contiguous" % name)
+
+
+def _kv_dtype(d: Dims) -> torch.dtype:
+    return torch.bfloat16 if d.kv_dtype == KV_BF16 else torch.float32
+
+
+def _raise(name: str, status: int):
+    if status != 0:
+        text = load().asp_status_string(status).decode()
+        raise AspError("%s: %s (%s)" % (name, _STATUS_NAMES.get(status, status), text), status)
+
+
+def _ws(ws: Optional[torch.Tensor]):
+    if ws is None:
+        return None, 0
+    if not ws.is_cuda or not ws.is_contiguous():
+        raise AspError("workspace must be a contiguous device tensor")
+    return ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size()
+
+
+class HipEvent:
+    """A HIP event (timing disabled), for asp_step's stream ordering."""
+
+    _hip = None
+
+    def __init__(self):
+        if HipEvent._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so")
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventCreateWithFlags.restype = ctypes.c_int
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            hip.hipEventDestroy.restype = ctypes.c_int
+            HipEvent._hip = hip
+        h = ctypes.c_void_p()
+        rc = HipEvent._hip.hipEventCreateWithFlags(ctypes.byref(h), 0x2)  # hipEventDisableTiming
+        if rc != 0:
+            raise AspError("hipEventCreateWithFlags failed (%d)" % rc)
+        self.handle = h
+
+    def __del__(self):
+        if getattr(self, "handle", None) and HipEvent._hip is not None:
+            HipEvent._hip.hipEventDestroy(self.handle)
+            self.handle = None
+
+
+def _ev(e: Optional[HipEvent]):
+    return None if e is None else e.handle
+
+
+# ----------------------------------------------------------------------------- entry points
+
+def asp_workspace_size(dims: Dims, cfg: Cfg, op: int) -> int:
+    return int(load().asp_workspace_size(ctypes.byref(dims), ctypes.byref(cfg), int(op)))
+
+
+def asp_status_string(status: int) -> str:
+    return load().asp_status_string(int(status)).decode()
+
+
+def asp_push_query(dims: Dims, cfg: Cfg, q_cur, q_hist, hist_newest, hist_len, stream=None) -> None:
+    B, Hq, W, D = dims.batch, dims.n_q_heads, cfg.window, dims.head_dim
+    _check(q_cur, "q_cur", (B, Hq, D), torch.float32)
+    _check(q_hist, "q_hist", (B, Hq, W, D), torch.float32)
+    _check(hist_newest, "hist_newest", (B,), torch.int32)
+    _check(hist_len, "hist_len", (B,), torch.int32)
+    _raise("asp_push_query", load().asp_push_query(ctypes.byref(dims), ctypes.byref(cfg), _ptr(q_cur), _ptr(q_hist),
+                                                   _ptr(hist_newest), _ptr(hist_len), _stream_handle(stream)))
+
+
+def asp_predict_query(dims: Dims, cfg: Cfg, q_hist, hist_newest, hist_len, q_pred, stream=None) -> None:
+    B, Hq, W, D = dims.batch, dims.n_q_heads, cfg.window, dims.head_dim
+    _check(q_hist, "q_hist", (B, Hq, W, D), torch.float32)
+    _check(hist_newest, "hist_newest", (B,), torch.int32)
+    _check(hist_len, "hist_len", (B,), torch.int32)
+    _check(q_pred, "q_pred", (B, Hq, D), torch.float32)
+    _raise("asp_predict_query", load().asp_predict_query(ctypes.byref(dims), ctypes.byref(cfg), _ptr(q_hist),
+                                                         _ptr(hist_newest), _ptr(hist_len), _ptr(q_pred),
+                                                         _stream_handle(stream)))
+
+
+def asp_score_keys(dims: Dims, q_pred, k, seq_lens, scores, stream=None) -> None:
+    B, Hq, Hkv, D, T = dims.batch, dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.t_cap
+    _check(q_pred, "q_pred", (B, Hq, D), torch.float32)
+    _check(k, "k", (B, Hkv, T, D), _kv_dtype(dims))
+    _check(seq_lens, "seq_lens", (B,), torch.int32)
+    _check(scores, "scores", (B, Hkv, T), torch.float32)
+    _raise("asp_score_keys", load().asp_score_keys(ctypes.byref(dims), _ptr(q_pred), _ptr(k), _ptr(seq_lens),
+                                                   _ptr(scores), _stream_handle(stream)))
+
+
+def asp_select_topc(dims: Dims, cfg: Cfg, scores, seq_lens, idx, n_sel, ws=None, stream=None) -> None:
+    B, Hkv, T, C = dims.batch, dims.n_kv_heads, dims.t_cap, cfg.top_c
+    _check(scores, "scores", (B, Hkv, T), torch.float32)
+    _check(seq_lens, "seq_lens", (B,), torch.int32)
+    _check(idx, "idx", (B, Hkv, C), torch.int32)
+    _check(n_sel, "n_sel", (B, Hkv), torch.int32)
+    wp, wb = _ws(ws)
+    _raise("asp_select_topc", load().asp_select_topc(ctypes.byref(dims), ctypes.byref(cfg), _ptr(scores),
+                                                     _ptr(seq_lens), _ptr(idx), _ptr(n_sel), wp, wb,
+                                                     _stream_handle(stream)))
+
+
+def asp_sparse_decode(dims: Dims, cfg: Cfg, q, k, v, idx, n_sel, out, ws, stream=None) -> None:
+    B, Hq, Hkv, D, T, C = dims.batch, dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.t_cap, cfg.top_c
+    _check(q, "q", (B, Hq, D), torch.float32)
+    _check(k, "k", (B, Hkv, T, D), _kv_dtype(dims))
+    _check(v, "v", (B, Hkv, T, D), _kv_dtype(dims))
+    _check(idx, "idx", (B, Hkv, C), torch.int32)
+    _check(n_sel, "n_sel", (B, Hkv), torch.int32)
+    _check(out, "out", (B, Hq, D), torch.float32)
+    wp, wb = _ws(ws)
+    _raise("asp_sparse_decode", load().asp_sparse_decode(ctypes.byref(dims), ctypes.byref(cfg), _ptr(q), _ptr(k),
+                                                         _ptr(v), _ptr(idx), _ptr(n_sel), _ptr(out), wp, wb,
+                                                         _stream_handle(stream)))
+
+
+def asp_step(dims: Dims, cfg: Cfg, q_cur, q_hist, hist_newest, hist_len, k, v, seq_lens, idx_cur, n_sel_cur,
+             idx_next, n_sel_next, out, ws, attn_stream=None, sel_stream=None, q_ready: Optional[HipEvent] = None,
+             idx_cur_ready: Optional[HipEvent] = None, idx_next_ready: Optional[HipEvent] = None) -> None:
+    B, Hq, Hkv, D, T = dims.batch, dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.t_cap
+    W, C = cfg.window, cfg.top_c
+    _check(q_cur, "q_cur", (B, Hq, D), torch.float32)
+    _check(q_hist, "q_hist", (B, Hq, W, D), torch.float32)
+    _check(hist_newest, "hist_newest", (B,), torch.int32)
+    _check(hist_len, "hist_len", (B,), torch.int32)
+    _check(k, "k", (B, Hkv, T, D), _kv_dtype(dims))
+    _check(v, "v", (B, Hkv, T, D), _kv_dtype(dims))
+    _check(seq_lens, "seq_lens", (B,), torch.int32)
+    if idx_cur is not None:
+        _check(idx_cur, "idx_cur", (B, Hkv, C), torch.int32)
+        _check(n_sel_cur, "n_sel_cur", (B, Hkv), torch.int32)
+    _check(idx_next, "idx_next", (B, Hkv, C), torch.int32)
+    _check(n_sel_next, "n_sel_next", (B, Hkv), torch.int32)
+    _check(out, "out", (B, Hq, D), torch.float32)
+    wp, wb = _ws(ws)
+    attn = _stream_handle(attn_stream)
+    sel = None if sel_stream is None else _stream_handle(sel_stream)
+    _raise("asp_step", load().asp_step(ctypes.byref(dims), ctypes.byref(cfg), _ptr(q_cur), _ptr(q_hist),
+                                       _ptr(hist_newest), _ptr(hist_len), _ptr(k), _ptr(v), _ptr(seq_lens),
+                                       _ptr(idx_cur), _ptr(n_sel_cur), _ptr(idx_next), _ptr(n_sel_next), _ptr(out),
+                                       wp, wb, attn, sel, _ev(q_ready), _ev(idx_cur_ready), _ev(idx_next_ready)))

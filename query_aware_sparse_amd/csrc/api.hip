@@ -1,0 +1,222 @@
+// C ABI of libasp.so: host-side validation, workspace layout and the order in
+// which the kernels are enqueued.  See include/asp.h for the contract of every
+// entry point.
+#include <math.h>
+
+#include "../../include/asp.h"
+#include "asp_internal.h"
+
+using asp::Shape;
+
+namespace {
+
+constexpr int32_t kMaxTCap = 1 << 22;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+asp_status check_dims(const asp_dims* d, Shape* s) {
+  if (d == nullptr) return ASP_ERR_INVALID_ARG;
+  if (d->batch < 0 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->t_cap < 1 || d->t_cap > kMaxTCap)
+    return ASP_ERR_INVALID_ARG;
+  if (d->n_q_heads % d->n_kv_heads != 0) return ASP_ERR_INVALID_ARG;
+  const int G = d->n_q_heads / d->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return ASP_ERR_UNSUPPORTED;
+  if (d->head_dim < 1) return ASP_ERR_INVALID_ARG;
+  if (d->head_dim != 64 && d->head_dim != 128) return ASP_ERR_UNSUPPORTED;
+  if (d->kv_dtype != ASP_KV_BF16 && d->kv_dtype != ASP_KV_F32) return ASP_ERR_INVALID_ARG;
+  // Grid limits: units index gridDim.y of the streaming kernels.
+  if ((int64_t)d->batch * d->n_kv_heads > 65535 || (int64_t)d->batch * d->n_q_heads > (1 << 24))
+    return ASP_ERR_UNSUPPORTED;
+  s->B = d->batch;
+  s->Hq = d->n_q_heads;
+  s->Hkv = d->n_kv_heads;
+  s->G = G;
+  s->D = d->head_dim;
+  s->T_cap = d->t_cap;
+  s->kv = d->kv_dtype == ASP_KV_BF16 ? 0 : 1;
+  s->W = 0;
+  s->C = 0;
+  s->lambda = 0.0;
+  return ASP_OK;
+}
+
+asp_status check_cfg(const asp_cfg* c, Shape* s) {
+  if (c == nullptr) return ASP_ERR_INVALID_ARG;
+  if (c->window < 4 || c->window > 64 || c->window % 4 != 0) return ASP_ERR_INVALID_ARG;
+  if (c->top_c < 1 || c->top_c > s->T_cap) return ASP_ERR_INVALID_ARG;
+  if (!(c->lambda > 0.0) || !isfinite(c->lambda)) return ASP_ERR_INVALID_ARG;
+  s->W = c->window;
+  s->C = c->top_c;
+  s->lambda = c->lambda;
+  return ASP_OK;
+}
+
+asp_status check_all(const asp_dims* d, const asp_cfg* c, Shape* s) {
+  asp_status st = check_dims(d, s);
+  if (st != ASP_OK) return st;
+  return check_cfg(c, s);
+}
+
+struct StepLayout {
+  size_t q_pred, scores, partials, total;
+};
+
+StepLayout step_layout(const Shape& s) {
+  StepLayout l;
+  l.q_pred = 0;
+  l.scores = align_up(l.q_pred + (size_t)s.B * s.Hq * s.D * sizeof(float));
+  l.partials = align_up(l.scores + (size_t)s.B * s.Hkv * s.T_cap * sizeof(float));
+  l.total = align_up(l.partials + asp::attend_partials_bytes(s));
+  return l;
+}
+
+size_t ws_bytes_for(const Shape& s, asp_op op) {
+  switch (op) {
+    case ASP_OP_DECODE: return align_up(asp::attend_partials_bytes(s));
+    case ASP_OP_STEP: return step_layout(s).total;
+    default: return 0;
+  }
+}
+
+asp_status hip_status(hipError_t e) { return e == hipSuccess ? ASP_OK : ASP_ERR_HIP; }
+
+#define ASP_TRY_HIP(expr)                          \
+  do {                                             \
+    if ((expr) != hipSuccess) return ASP_ERR_HIP;  \
+  } while (0)
+
+asp_status run_selection(const Shape& s, const float* q_cur, float* q_hist, int32_t* newest, int32_t* len,
+                         const void* k, const int32_t* seq_lens, int32_t* idx, int32_t* n_sel, float* q_pred,
+                         float* scores, hipStream_t st) {
+  ASP_TRY_HIP(asp::launch_push(s, q_cur, q_hist, newest, len, st));
+  ASP_TRY_HIP(asp::launch_predict(s, q_hist, newest, len, q_pred, st));
+  ASP_TRY_HIP(asp::launch_score(s, q_pred, k, seq_lens, scores, st));
+  ASP_TRY_HIP(asp::launch_select(s, scores, seq_lens, idx, n_sel, st));
+  return ASP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t asp_workspace_size(const asp_dims* dims, const asp_cfg* cfg, asp_op op) {
+  Shape s;
+  if (check_all(dims, cfg, &s) != ASP_OK) return 0;
+  return ws_bytes_for(s, op);
+}
+
+const char* asp_status_string(asp_status status) {
+  switch (status) {
+    case ASP_OK: return "ok";
+    case ASP_ERR_INVALID_ARG: return "invalid argument (dimension, configuration value or null pointer)";
+    case ASP_ERR_UNSUPPORTED: return "unsupported shape (head_dim must be 64 or 128, GQA group 1, 2, 4 or 8)";
+    case ASP_ERR_WORKSPACE: return "workspace missing or smaller than asp_workspace_size()";
+    case ASP_ERR_HIP: return "a HIP kernel launch, event or stream call failed";
+  }
+  return "unknown status";
+}
+
+asp_status asp_push_query(const asp_dims* dims, const asp_cfg* cfg, const float* q_cur, float* q_hist,
+                          int32_t* hist_newest, int32_t* hist_len, hipStream_t stream) {
+  Shape s;
+  asp_status st = check_all(dims, cfg, &s);
+  if (st != ASP_OK) return st;
+  if (!q_cur || !q_hist || !hist_newest || !hist_len) return ASP_ERR_INVALID_ARG;
+  return hip_status(asp::launch_push(s, q_cur, q_hist, hist_newest, hist_len, stream));
+}
+
+asp_status asp_predict_query(const asp_dims* dims, const asp_cfg* cfg, const float* q_hist,
+                             const int32_t* hist_newest, const int32_t* hist_len, float* q_pred,
+                             hipStream_t stream) {
+  Shape s;
+  asp_status st = check_all(dims, cfg, &s);
+  if (st != ASP_OK) return st;
+  if (!q_hist || !hist_newest || !hist_len || !q_pred) return ASP_ERR_INVALID_ARG;
+  return hip_status(asp::launch_predict(s, q_hist, hist_newest, hist_len, q_pred, stream));
+}
+
+asp_status asp_score_keys(const asp_dims* dims, const float* q_pred, const void* k, const int32_t* seq_lens,
+                          float* scores, hipStream_t stream) {
+  Shape s;
+  asp_status st = check_dims(dims, &s);
+  if (st != ASP_OK) return st;
+  if (!q_pred || !k || !seq_lens || !scores) return ASP_ERR_INVALID_ARG;
+  return hip_status(asp::launch_score(s, q_pred, k, seq_lens, scores, stream));
+}
+
+asp_status asp_select_topc(const asp_dims* dims, const asp_cfg* cfg, const float* scores, const int32_t* seq_lens,
+                           int32_t* idx, int32_t* n_sel, void* ws, size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  asp_status st = check_all(dims, cfg, &s);
+  if (st != ASP_OK) return st;
+  if (!scores || !seq_lens || !idx || !n_sel) return ASP_ERR_INVALID_ARG;
+  const size_t need = ws_bytes_for(s, ASP_OP_SELECT);
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return ASP_ERR_WORKSPACE;
+  return hip_status(asp::launch_select(s, scores, seq_lens, idx, n_sel, stream));
+}
+
+asp_status asp_sparse_decode(const asp_dims* dims, const asp_cfg* cfg, const float* q, const void* k, const void* v,
+                             const int32_t* idx, const int32_t* n_sel, float* out, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  Shape s;
+  asp_status st = check_all(dims, cfg, &s);
+  if (st != ASP_OK) return st;
+  if (!q || !k || !v || !idx || !n_sel || !out) return ASP_ERR_INVALID_ARG;
+  const size_t need = ws_bytes_for(s, ASP_OP_DECODE);
+  if (ws == nullptr || ws_bytes < need) return ASP_ERR_WORKSPACE;
+  return hip_status(asp::launch_attend(s, q, k, v, idx, n_sel, out, ws, stream));
+}
+
+asp_status asp_step(const asp_dims* dims, const asp_cfg* cfg, const float* q_cur, float* q_hist,
+                    int32_t* hist_newest, int32_t* hist_len, const void* k, const void* v,
+                    const int32_t* seq_lens, const int32_t* idx_cur, const int32_t* n_sel_cur,
+                    int32_t* idx_next, int32_t* n_sel_next, float* out, void* ws, size_t ws_bytes,
+                    hipStream_t attn_stream, hipStream_t sel_stream, hipEvent_t q_ready,
+                    hipEvent_t idx_cur_ready, hipEvent_t idx_next_ready) {
+  Shape s;
+  asp_status st = check_all(dims, cfg, &s);
+  if (st != ASP_OK) return st;
+  if (!q_cur || !q_hist || !hist_newest || !hist_len || !k || !v || !seq_lens || !idx_next || !n_sel_next || !out)
+    return ASP_ERR_INVALID_ARG;
+  if ((idx_cur == nullptr) != (n_sel_cur == nullptr)) return ASP_ERR_INVALID_ARG;
+  const bool pipelined = idx_cur != nullptr;
+  const bool two_streams = pipelined && sel_stream != nullptr && sel_stream != attn_stream;
+  if (two_streams && q_ready == nullptr) return ASP_ERR_INVALID_ARG;
+  const StepLayout lay = step_layout(s);
+  if (ws == nullptr || ws_bytes < lay.total) return ASP_ERR_WORKSPACE;
+  unsigned char* base = static_cast<unsigned char*>(ws);
+  float* q_pred = reinterpret_cast<float*>(base + lay.q_pred);
+  float* scores = reinterpret_cast<float*>(base + lay.scores);
+  void* partials = base + lay.partials;
+
+  if (!pipelined) {
+    st = run_selection(s, q_cur, q_hist, hist_newest, hist_len, k, seq_lens, idx_next, n_sel_next, q_pred, scores,
+                       attn_stream);
+    if (st != ASP_OK) return st;
+    ASP_TRY_HIP(asp::launch_attend(s, q_cur, k, v, idx_next, n_sel_next, out, partials, attn_stream));
+    if (idx_next_ready) ASP_TRY_HIP(hipEventRecord(idx_next_ready, attn_stream));
+    return ASP_OK;
+  }
+  if (!two_streams) {
+    ASP_TRY_HIP(asp::launch_attend(s, q_cur, k, v, idx_cur, n_sel_cur, out, partials, attn_stream));
+    st = run_selection(s, q_cur, q_hist, hist_newest, hist_len, k, seq_lens, idx_next, n_sel_next, q_pred, scores,
+                       attn_stream);
+    if (st != ASP_OK) return st;
+    if (idx_next_ready) ASP_TRY_HIP(hipEventRecord(idx_next_ready, attn_stream));
+    return ASP_OK;
+  }
+  // Two streams: the selection stream starts once q_cur exists and the previous
+  // step's attention (which read the buffer idx_next now overwrites) is done.
+  ASP_TRY_HIP(hipEventRecord(q_ready, attn_stream));
+  ASP_TRY_HIP(hipStreamWaitEvent(sel_stream, q_ready, 0));
+  if (idx_cur_ready) ASP_TRY_HIP(hipStreamWaitEvent(attn_stream, idx_cur_ready, 0));
+  ASP_TRY_HIP(asp::launch_attend(s, q_cur, k, v, idx_cur, n_sel_cur, out, partials, attn_stream));
+  st = run_selection(s, q_cur, q_hist, hist_newest, hist_len, k, seq_lens, idx_next, n_sel_next, q_pred, scores,
+                     sel_stream);
+  if (st != ASP_OK) return st;
+  if (idx_next_ready) ASP_TRY_HIP(hipEventRecord(idx_next_ready, sel_stream));
+  return ASP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// Internal declarations shared by the HIP translation units of libasp.so.
+// Nothing here is part of the public C ABI (include/asp.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace asp {
+
+// Validated problem shape, as the kernels see it.
+struct Shape {
+  int B, Hq, Hkv, G, D, T_cap, kv;  // kv: 0 = bf16, 1 = fp32
+  int W, C;
+  double lambda;
+};
+
+// Attention split size: tokens handled by one workgroup of the split-K
+// attention kernel (depends on the KV row size: 4 waves x 16 loads x keys per load).
+int attend_tokens_per_block(int D, int kv);
+int attend_num_splits(const Shape& s);
+size_t attend_partials_bytes(const Shape& s);
+
+hipError_t launch_push(const Shape& s, const float* q_cur, float* q_hist, int32_t* newest, int32_t* len,
+                       hipStream_t st);
+hipError_t launch_predict(const Shape& s, const float* q_hist, const int32_t* newest, const int32_t* len,
+                          float* q_pred, hipStream_t st);
+hipError_t launch_score(const Shape& s, const float* q_pred, const void* k, const int32_t* seq_lens,
+                        float* scores, hipStream_t st);
+hipError_t launch_select(const Shape& s, const float* scores, const int32_t* seq_lens, int32_t* idx,
+                         int32_t* n_sel, hipStream_t st);
+hipError_t launch_attend(const Shape& s, const float* q, const void* k, const void* v, const int32_t* idx,
+                         const int32_t* n_sel, float* out, void* partials, hipStream_t st);
+
+// ---------------------------------------------------------------- device helpers
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+// Cross-lane moves inside a 16-lane DPP row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int DPP_QUAD_XOR1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_MIRROR = 0x140;
+
+// Sum over aligned groups of N lanes (N in {1, 2, 4, 8, 16, 32, 64}); every lane
+// of a group receives the group's sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp_f<DPP_QUAD_XOR1>(x);
+  if constexpr (N >= 4) x += dpp_f<DPP_QUAD_XOR2>(x);
+  if constexpr (N >= 8) x += dpp_f<DPP_ROW_HALF_MIRROR>(x);
+  if constexpr (N >= 16) x += dpp_f<DPP_ROW_MIRROR>(x);
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  if constexpr (N >= 2) x = fmaxf(x, dpp_f<DPP_QUAD_XOR1>(x));
+  if constexpr (N >= 4) x = fmaxf(x, dpp_f<DPP_QUAD_XOR2>(x));
+  if constexpr (N >= 8) x = fmaxf(x, dpp_f<DPP_ROW_HALF_MIRROR>(x));
+  if constexpr (N >= 16) x = fmaxf(x, dpp_f<DPP_ROW_MIRROR>(x));
+  if constexpr (N >= 32) x = fmaxf(x, __shfl_xor(x, 16));
+  if constexpr (N >= 64) x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+}  // namespace asp

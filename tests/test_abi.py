@@ -1,0 +1,122 @@
+"""The C ABI: libasp.so loads, exports every function include/asp.h declares, and
+rejects invalid arguments on the host before touching the GPU (CPU only: no
+compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import query_aware_sparse_amd as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "asp.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(asp_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(A.library_path()):
+        pytest.fail("libasp.so is not built; run __graft_entry__.build()")
+    return A.load()
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted([
+        "asp_workspace_size", "asp_status_string", "asp_push_query", "asp_predict_query", "asp_score_keys",
+        "asp_select_topc", "asp_sparse_decode", "asp_step"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(A.library_path())
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert A.asp_status_string(code)
+    assert A.asp_status_string(77) == "unknown status"
+
+
+def _dims(**kw):
+    base = dict(batch=8, n_q_heads=32, n_kv_heads=8, head_dim=128, t_cap=32768, kv_dtype=A.KV_BF16)
+    base.update(kw)
+    return A.Dims(**base)
+
+
+def test_workspace_sizes(lib):
+    d, c = _dims(), A.Cfg(16, 2048, 1e-2)
+    assert A.asp_workspace_size(d, c, A.OP_PUSH) == 0
+    assert A.asp_workspace_size(d, c, A.OP_SCORE) == 0
+    dec = A.asp_workspace_size(d, c, A.OP_DECODE)
+    step = A.asp_workspace_size(d, c, A.OP_STEP)
+    assert dec > 0 and dec % 256 == 0
+    # the step holds the predicted queries, the score rows and the attention partials
+    assert step >= 8 * 32 * 128 * 4 + 8 * 8 * 32768 * 4 + dec
+    assert A.asp_workspace_size(_dims(head_dim=96), c, A.OP_STEP) == 0
+
+
+BAD_DIMS = [
+    (dict(batch=-1), 1), (dict(n_q_heads=0), 1), (dict(n_kv_heads=3), 1), (dict(n_q_heads=48, n_kv_heads=8), 2),
+    (dict(n_q_heads=128, n_kv_heads=8), 2), (dict(head_dim=96), 2), (dict(head_dim=0), 1), (dict(t_cap=0), 1),
+    (dict(t_cap=(1 << 22) + 1), 1), (dict(kv_dtype=5), 1),
+]
+BAD_CFG = [
+    (A.Cfg(6, 64, 1e-2), 1), (A.Cfg(0, 64, 1e-2), 1), (A.Cfg(68, 64, 1e-2), 1), (A.Cfg(16, 0, 1e-2), 1),
+    (A.Cfg(16, 40000, 1e-2), 1), (A.Cfg(16, 64, 0.0), 1), (A.Cfg(16, 64, -1.0), 1),
+    (A.Cfg(16, 64, float("nan")), 1), (A.Cfg(16, 64, float("inf")), 1),
+]
+
+
+def _call_score(lib, d):
+    one = ctypes.c_void_p(16)   # never dereferenced: validation fails first
+    return lib.asp_score_keys(ctypes.byref(d), one, one, one, one, None)
+
+
+def _call_select(lib, d, c, ws=None, nbytes=0):
+    one = ctypes.c_void_p(16)
+    return lib.asp_select_topc(ctypes.byref(d), ctypes.byref(c), one, one, one, one, ws, nbytes, None)
+
+
+def _call_decode(lib, d, c, ws=None, nbytes=0, null_out=False):
+    one = ctypes.c_void_p(16)
+    return lib.asp_sparse_decode(ctypes.byref(d), ctypes.byref(c), one, one, one, one, one,
+                                 None if null_out else one, ws, nbytes, None)
+
+
+@pytest.mark.parametrize("kw,code", BAD_DIMS)
+def test_invalid_dims_rejected_before_any_launch(lib, kw, code):
+    assert _call_score(lib, _dims(**kw)) == code
+    assert _call_select(lib, _dims(**kw), A.Cfg(16, 64, 1e-2)) == code
+
+
+@pytest.mark.parametrize("cfg,code", BAD_CFG)
+def test_invalid_cfg_rejected_before_any_launch(lib, cfg, code):
+    assert _call_select(lib, _dims(), cfg) == code
+    assert _call_decode(lib, _dims(), cfg, ctypes.c_void_p(256), 1 << 30) == code
+
+
+def test_null_pointers_and_short_workspace_rejected(lib):
+    d, c = _dims(), A.Cfg(16, 2048, 1e-2)
+    assert lib.asp_score_keys(ctypes.byref(d), None, ctypes.c_void_p(16), ctypes.c_void_p(16),
+                              ctypes.c_void_p(16), None) == 1
+    assert _call_decode(lib, d, c, ctypes.c_void_p(256), 1 << 30, null_out=True) == 1
+    need = A.asp_workspace_size(d, c, A.OP_DECODE)
+    assert _call_decode(lib, d, c, None, 0) == 3
+    assert _call_decode(lib, d, c, ctypes.c_void_p(256), need - 1) == 3
+    assert lib.asp_score_keys(None, None, None, None, None, None) == 1
+    one = ctypes.c_void_p(16)
+    # asp_step: idx_cur without n_sel_cur; missing workspace
+    args = [ctypes.byref(d), ctypes.byref(c)] + [one] * 7  # q_cur .. seq_lens
+    #                   idx_cur n_sel_cur idx_nx nsel_nx out  ws    ws_bytes  attn  sel   events
+    assert lib.asp_step(*args, one, None, one, one, one, one, 1 << 40, None, None, None, None, None) == 1
+    assert lib.asp_step(*args, None, None, one, one, one, None, 0, None, None, None, None, None) == 3
+    # two distinct streams need a q_ready event
+    assert lib.asp_step(*args, one, one, one, one, one, one, 1 << 40, ctypes.c_void_p(1), ctypes.c_void_p(2),
+                        None, None, None) == 1
