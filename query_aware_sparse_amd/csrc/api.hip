@@ -59,14 +59,17 @@ asp_status check_all(const asp_dims* d, const asp_cfg* c, Shape* s) {
 }
 
 struct StepLayout {
-  size_t q_pred, scores, partials, total;
+  size_t q_pred, scores, hist, partials, total;
 };
 
+// Workspace of asp_step: predicted queries, score rows and coarse histograms
+// (selection stream), attention partials (attention stream).
 StepLayout step_layout(const Shape& s) {
   StepLayout l;
   l.q_pred = 0;
   l.scores = align_up(l.q_pred + (size_t)s.B * s.Hq * s.D * sizeof(float));
-  l.partials = align_up(l.scores + (size_t)s.B * s.Hkv * s.T_cap * sizeof(float));
+  l.hist = align_up(l.scores + (size_t)s.B * s.Hkv * s.T_cap * sizeof(float));
+  l.partials = align_up(l.hist + (size_t)s.B * s.Hkv * asp::HIST_BINS * sizeof(uint32_t));
   l.total = align_up(l.partials + asp::attend_partials_bytes(s));
   return l;
 }
@@ -86,13 +89,15 @@ asp_status hip_status(hipError_t e) { return e == hipSuccess ? ASP_OK : ASP_ERR_
     if ((expr) != hipSuccess) return ASP_ERR_HIP;  \
   } while (0)
 
+// Selection work of one step: three launches.  The predictor pushes q_cur into
+// every head's ring slot and clears the coarse histograms; the score launch
+// fills the histograms; the select launch uses them and advances the ring.
 asp_status run_selection(const Shape& s, const float* q_cur, float* q_hist, int32_t* newest, int32_t* len,
                          const void* k, const int32_t* seq_lens, int32_t* idx, int32_t* n_sel, float* q_pred,
-                         float* scores, hipStream_t st) {
-  ASP_TRY_HIP(asp::launch_push(s, q_cur, q_hist, newest, len, st));
-  ASP_TRY_HIP(asp::launch_predict(s, q_hist, newest, len, q_pred, st));
-  ASP_TRY_HIP(asp::launch_score(s, q_pred, k, seq_lens, scores, st));
-  ASP_TRY_HIP(asp::launch_select(s, scores, seq_lens, idx, n_sel, st));
+                         float* scores, uint32_t* hist, hipStream_t st) {
+  ASP_TRY_HIP(asp::launch_predict(s, q_hist, newest, len, q_cur, q_pred, hist, st));
+  ASP_TRY_HIP(asp::launch_score(s, q_pred, k, seq_lens, scores, hist, st));
+  ASP_TRY_HIP(asp::launch_select(s, scores, hist, seq_lens, idx, n_sel, newest, len, st));
   return ASP_OK;
 }
 
@@ -133,7 +138,8 @@ asp_status asp_predict_query(const asp_dims* dims, const asp_cfg* cfg, const flo
   asp_status st = check_all(dims, cfg, &s);
   if (st != ASP_OK) return st;
   if (!q_hist || !hist_newest || !hist_len || !q_pred) return ASP_ERR_INVALID_ARG;
-  return hip_status(asp::launch_predict(s, q_hist, hist_newest, hist_len, q_pred, stream));
+  return hip_status(asp::launch_predict(s, const_cast<float*>(q_hist), hist_newest, hist_len, nullptr, q_pred, nullptr,
+                                        stream));
 }
 
 asp_status asp_score_keys(const asp_dims* dims, const float* q_pred, const void* k, const int32_t* seq_lens,
@@ -142,7 +148,7 @@ asp_status asp_score_keys(const asp_dims* dims, const float* q_pred, const void*
   asp_status st = check_dims(dims, &s);
   if (st != ASP_OK) return st;
   if (!q_pred || !k || !seq_lens || !scores) return ASP_ERR_INVALID_ARG;
-  return hip_status(asp::launch_score(s, q_pred, k, seq_lens, scores, stream));
+  return hip_status(asp::launch_score(s, q_pred, k, seq_lens, scores, nullptr, stream));
 }
 
 asp_status asp_select_topc(const asp_dims* dims, const asp_cfg* cfg, const float* scores, const int32_t* seq_lens,
@@ -153,7 +159,7 @@ asp_status asp_select_topc(const asp_dims* dims, const asp_cfg* cfg, const float
   if (!scores || !seq_lens || !idx || !n_sel) return ASP_ERR_INVALID_ARG;
   const size_t need = ws_bytes_for(s, ASP_OP_SELECT);
   if (need > 0 && (ws == nullptr || ws_bytes < need)) return ASP_ERR_WORKSPACE;
-  return hip_status(asp::launch_select(s, scores, seq_lens, idx, n_sel, stream));
+  return hip_status(asp::launch_select(s, scores, nullptr, seq_lens, idx, n_sel, nullptr, nullptr, stream));
 }
 
 asp_status asp_sparse_decode(const asp_dims* dims, const asp_cfg* cfg, const float* q, const void* k, const void* v,
@@ -188,11 +194,12 @@ asp_status asp_step(const asp_dims* dims, const asp_cfg* cfg, const float* q_cur
   unsigned char* base = static_cast<unsigned char*>(ws);
   float* q_pred = reinterpret_cast<float*>(base + lay.q_pred);
   float* scores = reinterpret_cast<float*>(base + lay.scores);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(base + lay.hist);
   void* partials = base + lay.partials;
 
   if (!pipelined) {
     st = run_selection(s, q_cur, q_hist, hist_newest, hist_len, k, seq_lens, idx_next, n_sel_next, q_pred, scores,
-                       attn_stream);
+                       hist, attn_stream);
     if (st != ASP_OK) return st;
     ASP_TRY_HIP(asp::launch_attend(s, q_cur, k, v, idx_next, n_sel_next, out, partials, attn_stream));
     if (idx_next_ready) ASP_TRY_HIP(hipEventRecord(idx_next_ready, attn_stream));
@@ -201,7 +208,7 @@ asp_status asp_step(const asp_dims* dims, const asp_cfg* cfg, const float* q_cur
   if (!two_streams) {
     ASP_TRY_HIP(asp::launch_attend(s, q_cur, k, v, idx_cur, n_sel_cur, out, partials, attn_stream));
     st = run_selection(s, q_cur, q_hist, hist_newest, hist_len, k, seq_lens, idx_next, n_sel_next, q_pred, scores,
-                       attn_stream);
+                       hist, attn_stream);
     if (st != ASP_OK) return st;
     if (idx_next_ready) ASP_TRY_HIP(hipEventRecord(idx_next_ready, attn_stream));
     return ASP_OK;
@@ -213,7 +220,7 @@ asp_status asp_step(const asp_dims* dims, const asp_cfg* cfg, const float* q_cur
   if (idx_cur_ready) ASP_TRY_HIP(hipStreamWaitEvent(attn_stream, idx_cur_ready, 0));
   ASP_TRY_HIP(asp::launch_attend(s, q_cur, k, v, idx_cur, n_sel_cur, out, partials, attn_stream));
   st = run_selection(s, q_cur, q_hist, hist_newest, hist_len, k, seq_lens, idx_next, n_sel_next, q_pred, scores,
-                     sel_stream);
+                     hist, sel_stream);
   if (st != ASP_OK) return st;
   if (idx_next_ready) ASP_TRY_HIP(hipEventRecord(idx_next_ready, sel_stream));
   return ASP_OK;

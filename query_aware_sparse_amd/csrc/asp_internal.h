@@ -23,12 +23,22 @@ size_t attend_partials_bytes(const Shape& s);
 
 hipError_t launch_push(const Shape& s, const float* q_cur, float* q_hist, int32_t* newest, int32_t* len,
                        hipStream_t st);
-hipError_t launch_predict(const Shape& s, const float* q_hist, const int32_t* newest, const int32_t* len,
-                          float* q_pred, hipStream_t st);
+// Predictor.  With q_cur == nullptr it predicts from the ring as it stands.
+// With q_cur != nullptr it predicts from the ring after pushing q_cur (lag 0 is
+// q_cur, the ring supplies the older lags) and writes q_cur into each head's
+// next ring slot, but leaves newest/len unchanged: the select launch of the
+// same step advances them (it runs after every predictor workgroup has read
+// them).  hist_zero, when not null, is cleared ([B*Hkv][HIST_BINS]).
+hipError_t launch_predict(const Shape& s, float* q_hist, const int32_t* newest, const int32_t* len,
+                          const float* q_cur, float* q_pred, uint32_t* hist_zero, hipStream_t st);
+// Scores; hist (nullable) accumulates the coarse histogram of every unit and
+// must be zero on entry.
 hipError_t launch_score(const Shape& s, const float* q_pred, const void* k, const int32_t* seq_lens,
-                        float* scores, hipStream_t st);
-hipError_t launch_select(const Shape& s, const float* scores, const int32_t* seq_lens, int32_t* idx,
-                         int32_t* n_sel, hipStream_t st);
+                        float* scores, uint32_t* hist, hipStream_t st);
+// Top-C selection; hist (nullable) is the coarse histogram built by the score
+// launch.  adv_newest/adv_len (nullable) advance the query ring by one slot.
+hipError_t launch_select(const Shape& s, const float* scores, const uint32_t* hist, const int32_t* seq_lens,
+                         int32_t* idx, int32_t* n_sel, int32_t* adv_newest, int32_t* adv_len, hipStream_t st);
 hipError_t launch_attend(const Shape& s, const float* q, const void* k, const void* v, const int32_t* idx,
                          const int32_t* n_sel, float* out, void* partials, hipStream_t st);
 
@@ -71,6 +81,31 @@ __device__ __forceinline__ float group_max(float x) {
   if constexpr (N >= 32) x = fmaxf(x, __shfl_xor(x, 16));
   if constexpr (N >= 64) x = fmaxf(x, __shfl_xor(x, 32));
   return x;
+}
+
+}  // namespace asp
+
+namespace asp {
+
+// Monotone map from float to uint32: a > b (as numbers) iff key(a) > key(b);
+// NaN maps to the key of -inf and -0 to the key of +0.  Shared by the score
+// kernel's coarse histogram and the select kernel, which must agree bit for bit.
+__device__ __forceinline__ uint32_t order_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if ((u & 0x7fffffffu) > 0x7f800000u) u = 0xff800000u;
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Coarse histogram over the top 11 bits of order_key, per unit.
+constexpr int HIST_BINS = 2048;
+constexpr int HIST_SHIFT = 21;
+
+__device__ __forceinline__ double readlane_f64(double x, int lane) {
+  const long long v = __double_as_longlong(x);
+  const int lo = __builtin_amdgcn_readlane((int)(v & 0xffffffffll), lane);
+  const int hi = __builtin_amdgcn_readlane((int)(v >> 32), lane);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
 }
 
 }  // namespace asp

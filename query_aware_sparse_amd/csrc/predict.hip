@@ -10,14 +10,22 @@
 // window of 16 queries).  The pages print no equations; the reading
 // implemented is the one documented on asp_predict_query in include/asp.h.
 //
-// Work per (sequence, query head) is tiny (a 16x16 Gram matrix at W = 16), so
-// one 64-lane wavefront handles one head: the Gram matrix is accumulated in
-// fp64 (products of fp32 values are exact in fp64), factorised once by
-// Cholesky and reused by every window, because the system of a smaller window
-// is the leading block of the largest one.
+// One 64-lane wavefront per (sequence, query head):
+//  1. the lags q_t .. q_{t-P} (P = largest window - 1) are staged in LDS;
+//  2. their Gram matrix is accumulated in fp64 with v_mfma_f64_16x16x4 (fp32
+//     inputs widen exactly, so the products are exact);
+//  3. the ridge system of the largest window is factorised by a register
+//     Cholesky (lane i holds row i, columns are broadcast with readlane); every
+//     smaller window's system is a leading block, so the same factor and the
+//     same forward substitution serve all windows;
+//  4. the back substitutions of all windows run side by side, then each
+//     window's softmax runs across lanes, and the window predictions are
+//     pooled as one weighted sum of the lags.
 #include "asp_internal.h"
 
 namespace asp {
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 // One workgroup per sequence: copy its Hq queries into the next ring slot, then
 // advance the slot and the length (after every thread has read the old slot).
@@ -50,161 +58,229 @@ hipError_t launch_push(const Shape& s, const float* q_cur, float* q_hist, int32_
   return hipGetLastError();
 }
 
-// LDS layout of the predictor (dynamic shared memory, sized per launch):
-//   X     [W][D + 1] float   lag rows, X[j] = q_{t-j}; +1 pad breaks bank conflicts
-//   M     [W][W]     double  Gram of lags 0..P (only the upper triangle filled)
-//   A     [W][W]     double  ridge system, factorised in place (lower triangle)
-//   y     [W]        double  forward-substitution result, shared by all windows
-//   z     [W]        double  back-substitution scratch
-//   coef  [W]        double  beta, then alpha of the current window
-constexpr int PRED_THREADS = 64;
-
-size_t predict_lds_bytes(int W, int D) {
-  size_t x = (size_t)W * (D + 1) * sizeof(float);
-  x = (x + 7) & ~(size_t)7;
-  return x + sizeof(double) * ((size_t)W * W * 2 + 3 * (size_t)W);
+__device__ __forceinline__ double wave_max_f64(double x) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) x = fmax(x, __shfl_xor(x, off));
+  return x;
+}
+__device__ __forceinline__ double wave_sum_f64(double x) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off);
+  return x;
 }
 
-__global__ void __launch_bounds__(PRED_THREADS) predict_kernel(const float* __restrict__ q_hist,
+constexpr int PRED_THREADS = 64;
+constexpr int XS = 128 + 1;  // LDS row stride of the staged lags (floats); +1 avoids bank conflicts
+
+// PB: a bound on P = (largest window) - 1; PB + 1 is a multiple of 4 and at most 64.
+template <int PB>
+__global__ void __launch_bounds__(PRED_THREADS) predict_kernel(float* __restrict__ q_hist,
                                                                const int32_t* __restrict__ newest,
                                                                const int32_t* __restrict__ len,
-                                                               float* __restrict__ q_pred, int Hq, int W, int D,
-                                                               double lambda) {
-  extern __shared__ __align__(16) unsigned char smem[];
+                                                               const float* __restrict__ q_cur,
+                                                               float* __restrict__ q_pred,
+                                                               uint32_t* __restrict__ hist_zero, int Hq, int Hkv,
+                                                               int W, int D, double lambda) {
+  constexpr int NR = ((PB + 1 + 15) / 16) * 16;  // lag rows staged (whole 16-row MFMA tiles)
+  __shared__ float X[NR * XS];
+  __shared__ double M[NR * NR];  // Gram of lags 0..P; later reused for L
+  __shared__ double cw[NR];      // pooled weight of each lag
+
+  const int t = threadIdx.x;
   const int bh = blockIdx.x;
   const int b = bh / Hq;
-  const int t = threadIdx.x;
-  const int xs = D + 1;
-  float* X = reinterpret_cast<float*>(smem);
-  size_t xbytes = ((size_t)W * xs * sizeof(float) + 7) & ~(size_t)7;
-  double* M = reinterpret_cast<double*>(smem + xbytes);
-  double* A = M + W * W;
-  double* y = A + W * W;
-  double* z = y + W;
-  double* coef = z + W;
-
-  const int n = clampi(len[b], 0, W);
-  int nw_slot = newest[b] % W;
-  if (nw_slot < 0) nw_slot += W;
+  float* ring = q_hist + (size_t)bh * W * D;
   float* out = q_pred + (size_t)bh * D;
-  const float* ring = q_hist + (size_t)bh * W * D;
 
-  if (n == 0) {  // no history: predict zero
+  if (hist_zero != nullptr) {  // the G heads of a KV head clear its histogram row together
+    const int G = Hq / Hkv, h = bh % Hq;
+    uint32_t* row = hist_zero + ((size_t)b * Hkv + h / G) * HIST_BINS;
+    const int per = HIST_BINS / G, j0 = (h % G) * per;
+    for (int j = j0 + t; j < j0 + per; j += PRED_THREADS) row[j] = 0u;
+  }
+
+  int on = newest[b] % W;
+  if (on < 0) on += W;
+  const int old_n = clampi(len[b], 0, W);
+  const bool push = q_cur != nullptr;
+  const float* qc = push ? q_cur + (size_t)bh * D : nullptr;
+  const int n = push ? min(old_n + 1, W) : old_n;
+  // Lag j lives in ring slot (on - j) without a push, (on - j + 1) with one
+  // (lag 0 then being q_cur itself).
+  const int shift = push ? 1 : 0;
+  if (push) {
+    // The next slot held lag W-1 of the ring before the push, which no window
+    // reads (the largest window uses lags 0..W-1 counted after the push).
+    const int slot = on + 1 == W ? 0 : on + 1;
+    for (int d = t; d < D; d += PRED_THREADS) ring[(size_t)slot * D + d] = qc[d];
+  }
+
+  if (n == 0) {
     for (int d = t; d < D; d += PRED_THREADS) out[d] = 0.0f;
     return;
   }
-  // Window set {W, W/2, W/4} restricted to 2 <= w <= n, largest first.
-  int wset[3];
+  int wset[3] = {0, 0, 0};
   int nw = 0;
   {
     const int cand[3] = {W, W / 2, W / 4};
+#pragma unroll
     for (int c = 0; c < 3; ++c)
       if (cand[c] >= 2 && cand[c] <= n) wset[nw++] = cand[c];
   }
   if (nw == 0) {  // a single query held: predict it unchanged
-    const float* q0 = ring + (size_t)nw_slot * D;
-    for (int d = t; d < D; d += PRED_THREADS) out[d] = q0[d];
+    for (int d = t; d < D; d += PRED_THREADS) {
+      int slot = on;
+      out[d] = push ? qc[d] : ring[(size_t)slot * D + d];
+    }
     return;
   }
-  const int P = wset[0] - 1;  // lags used by the largest window
+  const int P = wset[0] - 1;
+  const int NT = (P + 1 + 15) / 16;
 
-  // Stage lags 0..P (newest first) in LDS.
-  for (int e = t; e < (P + 1) * D; e += PRED_THREADS) {
+  // 1. Stage lags 0..P (rows up to the tile boundary are zero).
+  for (int e = t; e < NT * 16 * D; e += PRED_THREADS) {
     const int j = e / D, d = e % D;
-    int slot = nw_slot - j;
-    if (slot < 0) slot += W;
-    X[j * xs + d] = ring[(size_t)slot * D + d];
-  }
-  __syncthreads();
-
-  // Gram entries M[a][c] = <q_{t-a}, q_{t-c}> for 0 <= a <= c <= P, fp64.
-  for (int a = 0; a <= P; ++a) {
-    for (int c = a + t; c <= P; c += PRED_THREADS) {
-      const float* xa = X + a * xs;
-      const float* xc = X + c * xs;
-      double acc = 0.0;
-      for (int d = 0; d < D; ++d) acc = fma((double)xa[d], (double)xc[d], acc);
-      M[a * W + c] = acc;
-    }
-  }
-  __syncthreads();
-
-  // Ridge system of the largest window: A = G_P + lambda I (lags 1..P), r = M[0][1..P].
-  for (int e = t; e < P * P; e += PRED_THREADS) {
-    const int i = e / P, j = e % P;
-    if (j <= i) A[i * W + j] = M[(j + 1) * W + (i + 1)] + (i == j ? lambda : 0.0);
-  }
-  for (int i = t; i < P; i += PRED_THREADS) y[i] = M[0 * W + (i + 1)];
-  __syncthreads();
-
-  // Cholesky A = L L^T in place (lower triangle), right-looking, one row per lane.
-  for (int k = 0; k < P; ++k) {
-    if (t == 0) A[k * W + k] = sqrt(A[k * W + k]);
-    __syncthreads();
-    const double dkk = A[k * W + k];
-    for (int i = k + 1 + t; i < P; i += PRED_THREADS) A[i * W + k] /= dkk;
-    __syncthreads();
-    for (int i = k + 1 + t; i < P; i += PRED_THREADS) {
-      const double lik = A[i * W + k];
-      for (int j = k + 1; j <= i; ++j) A[i * W + j] = fma(-lik, A[j * W + k], A[i * W + j]);
-    }
-    __syncthreads();
-  }
-  // Forward substitution L y = r (column oriented); y's leading entries serve
-  // every smaller window unchanged.
-  for (int i = 0; i < P; ++i) {
-    if (t == 0) y[i] = y[i] / A[i * W + i];
-    __syncthreads();
-    const double yi = y[i];
-    for (int k = i + 1 + t; k < P; k += PRED_THREADS) y[k] = fma(-A[k * W + i], yi, y[k]);
-    __syncthreads();
-  }
-
-  double acc[128 / PRED_THREADS] = {0.0, 0.0};
-  for (int wi = 0; wi < nw; ++wi) {
-    const int p = wset[wi] - 1;
-    // Back substitution L_p^T beta = y_p on the leading p x p block.
-    for (int i = t; i < p; i += PRED_THREADS) z[i] = y[i];
-    __syncthreads();
-    for (int i = p - 1; i >= 0; --i) {
-      if (t == 0) coef[i] = z[i] / A[i * W + i];
-      __syncthreads();
-      const double bi = coef[i];
-      for (int k = t; k < i; k += PRED_THREADS) z[k] = fma(-A[i * W + k], bi, z[k]);
-      __syncthreads();
-    }
-    // Softmax over the p lag weights (max subtracted first).
-    if (t == 0) {
-      double m = coef[0];
-      for (int j = 1; j < p; ++j) m = fmax(m, coef[j]);
-      double sum = 0.0;
-      for (int j = 0; j < p; ++j) {
-        const double e = exp(coef[j] - m);
-        coef[j] = e;
-        sum += e;
+    float v = 0.0f;
+    if (j <= P) {
+      if (push && j == 0) {
+        v = qc[d];
+      } else {
+        int slot = (on - j + shift) % W;
+        if (slot < 0) slot += W;
+        v = ring[(size_t)slot * D + d];
       }
-      const double inv = 1.0 / sum;
-      for (int j = 0; j < p; ++j) coef[j] *= inv;
     }
-    __syncthreads();
-    // One step ahead: weight j (j = 1..p) multiplies q_{t+1-j} = X[j-1].
-    for (int r = 0, d = t; d < D; ++r, d += PRED_THREADS) {
-      double s = 0.0;
-      for (int j = 0; j < p; ++j) s = fma(coef[j], (double)X[j * xs + d], s);
-      acc[r] += s;
-    }
-    __syncthreads();
+    X[j * XS + d] = v;
   }
-  const double inv_nw = 1.0 / nw;
-  for (int r = 0, d = t; d < D; ++r, d += PRED_THREADS) out[d] = (float)(acc[r] * inv_nw);
+  __syncthreads();
+
+  // 2. Gram matrix M[a][c] = <lag a, lag c>, fp64 MFMA over 16x16 tiles.  The
+  // contraction index k = 4s + lane/16 walks all D coordinates.
+  const int lr = t & 15, lk = t >> 4;
+  for (int ti = 0; ti < NT; ++ti) {
+    for (int tj = ti; tj < NT; ++tj) {
+      f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+      const float* xa = X + (ti * 16 + lr) * XS + lk;
+      const float* xb = X + (tj * 16 + lr) * XS + lk;
+      for (int s = 0; s < D / 4; ++s)
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xa[4 * s], (double)xb[4 * s], acc, 0, 0, 0);
+      // lane t, register r holds tile element (t/16 + 4r, t%16)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = ti * 16 + lk + 4 * r, j = tj * 16 + lr;
+        M[i * NR + j] = acc[r];
+        M[j * NR + i] = acc[r];
+      }
+    }
+  }
+  __syncthreads();
+
+  // 3. Ridge system of the largest window over lags 1..P:
+  //    A[i][j] = M[i+1][j+1] + lambda [i == j],  r_i = M[0][i+1]; lane i owns row i.
+  double a[PB];
+#pragma unroll
+  for (int j = 0; j < PB; ++j)
+    a[j] = (t < P && j < P) ? M[(t + 1) * NR + (j + 1)] + (j == t ? lambda : 0.0) : 0.0;
+  double y = t < P ? M[t + 1] : 0.0;
+  double invd = 0.0;
+  // Cholesky A = L L^T (right-looking; column k is broadcast lane by lane).
+#pragma unroll
+  for (int k = 0; k < PB; ++k) {
+    if (k < P) {
+      const double dk = sqrt(readlane_f64(a[k], k));
+      const double ik = 1.0 / dk;
+      if (t == k) {
+        a[k] = dk;
+        invd = ik;
+      } else if (t > k) {
+        a[k] *= ik;
+      }
+#pragma unroll
+      for (int j = k + 1; j < PB; ++j) {
+        if (j < P) {
+          const double ljk = readlane_f64(a[k], j);
+          if (t >= j) a[j] = fma(-a[k], ljk, a[j]);
+        }
+      }
+    }
+  }
+  // Forward substitution L y = r (shared by every window).
+#pragma unroll
+  for (int k = 0; k < PB; ++k) {
+    if (k < P) {
+      if (t == k) y *= invd;
+      const double yk = readlane_f64(y, k);
+      if (t > k) y = fma(-a[k], yk, y);
+    }
+  }
+  // Transpose L through LDS so that lane k holds column k: lt[i] = L[i][k].
+  __syncthreads();
+  if (t < P) {
+#pragma unroll
+    for (int j = 0; j < PB; ++j)
+      if (j <= t) M[t * NR + j] = a[j];
+  }
+  __syncthreads();
+  double lt[PB];
+#pragma unroll
+  for (int i = 0; i < PB; ++i) lt[i] = (i < P && i > t) ? M[i * NR + t] : 0.0;
+
+  // 4. Back substitutions L_p^T beta = y_p of every window, side by side.
+  int pw[3];
+  double z[3], beta[3];
+#pragma unroll
+  for (int w = 0; w < 3; ++w) {
+    pw[w] = w < nw ? wset[w] - 1 : 0;
+    z[w] = t < pw[w] ? y : 0.0;
+    beta[w] = 0.0;
+  }
+#pragma unroll
+  for (int i = PB - 1; i >= 0; --i) {
+#pragma unroll
+    for (int w = 0; w < 3; ++w) {
+      if (i < pw[w]) {
+        if (t == i) beta[w] = z[w] * invd;
+        const double bi = readlane_f64(beta[w], i);
+        if (t < i) z[w] = fma(-lt[i], bi, z[w]);
+      }
+    }
+  }
+  // Softmax over each window's lag weights; lane t carries lag t+1, whose
+  // one-step-ahead partner is lag t.  Pool: weight / number of windows.
+  double c = 0.0;
+#pragma unroll
+  for (int w = 0; w < 3; ++w) {
+    if (w < nw) {
+      const bool in = t < pw[w];
+      const double m = wave_max_f64(in ? beta[w] : -INFINITY);
+      const double e = in ? exp(beta[w] - m) : 0.0;
+      const double sum = wave_sum_f64(e);
+      c += e / sum;
+    }
+  }
+  if (t < NR) cw[t] = t < P ? c / nw : 0.0;
+  __syncthreads();
+  for (int d = t; d < D; d += PRED_THREADS) {
+    double acc = 0.0;
+    for (int j = 0; j < P; ++j) acc = fma(cw[j], (double)X[j * XS + d], acc);
+    out[d] = (float)acc;
+  }
 }
 
-hipError_t launch_predict(const Shape& s, const float* q_hist, const int32_t* newest, const int32_t* len,
-                          float* q_pred, hipStream_t st) {
+hipError_t launch_predict(const Shape& s, float* q_hist, const int32_t* newest, const int32_t* len,
+                          const float* q_cur, float* q_pred, uint32_t* hist_zero, hipStream_t st) {
   if (s.B == 0) return hipSuccess;
-  const size_t lds = predict_lds_bytes(s.W, s.D);
-  hipLaunchKernelGGL(predict_kernel, dim3(s.B * s.Hq), dim3(PRED_THREADS), lds, st, q_hist, newest, len, q_pred,
-                     s.Hq, s.W, s.D, s.lambda);
+  const dim3 grid(s.B * s.Hq), block(PRED_THREADS);
+  const int P = s.W - 1;
+#define ASP_PRED_LAUNCH(PB)                                                                                      \
+  hipLaunchKernelGGL(predict_kernel<PB>, grid, block, 0, st, q_hist, newest, len, q_cur, q_pred, hist_zero, s.Hq, \
+                     s.Hkv, s.W, s.D, s.lambda)
+  if (P <= 3) ASP_PRED_LAUNCH(3);
+  else if (P <= 7) ASP_PRED_LAUNCH(7);
+  else if (P <= 15) ASP_PRED_LAUNCH(15);
+  else if (P <= 31) ASP_PRED_LAUNCH(31);
+  else ASP_PRED_LAUNCH(63);
+#undef ASP_PRED_LAUNCH
   return hipGetLastError();
 }
 

@@ -10,40 +10,140 @@
 //
 // This pass streams the whole K cache once and is bound by HBM bandwidth.  The
 // KV layout is head-major ([B][Hkv][T_cap][D]), so a unit's keys are one
-// contiguous stream.  A wavefront issues 16-byte loads: one key row is LPK
-// consecutive lanes, KPW keys per wave-wide load, U loads in flight per lane
-// before any arithmetic.  The group's query slice stays in registers.
+// contiguous stream.
+//
+// bf16 keys: the G x D query block times a 16-key tile is one
+// v_mfma_f32_16x16x32_bf16 per 32 coordinates, with the keys as the B operand
+// straight from the 16-byte loads (lane l: key l%16, coordinates 8*(l/16)..+7
+// of each 32-wide step) and the query heads as rows of the A operand.  The
+// predicted query is fp32; it enters as two bf16 terms, hi = rne(q) and
+// lo = rne(q - hi), so the product keeps ~17 significant bits of q (relative
+// error <= 2^-18 per term) and accumulates in fp32.
+// fp32 keys: a VALU dot product (LPK lanes per key, DPP reduction).
+//
+// Optionally each workgroup also bins its scores by the top 11 bits of the
+// order-preserving key (LDS histogram, then one global atomic per non-empty
+// bin): the first radix pass of the top-C select, done while the keys stream.
 #include "asp_internal.h"
 
 namespace asp {
 
 constexpr int SCORE_THREADS = 256;
+constexpr int SCORE_WAVES = SCORE_THREADS / 64;
 constexpr int SCORE_KEYS_PER_BLOCK = 2048;
 
-template <typename KV>
-__device__ __forceinline__ void unpack16(const uint4& r, float* x) {
-  if constexpr (sizeof(KV) == 2) {
-    x[0] = bf16_lo(r.x); x[1] = bf16_hi(r.x);
-    x[2] = bf16_lo(r.y); x[3] = bf16_hi(r.y);
-    x[4] = bf16_lo(r.z); x[5] = bf16_hi(r.z);
-    x[6] = bf16_lo(r.w); x[7] = bf16_hi(r.w);
-  } else {
-    x[0] = __uint_as_float(r.x); x[1] = __uint_as_float(r.y);
-    x[2] = __uint_as_float(r.z); x[3] = __uint_as_float(r.w);
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <int D, int G, bool HIST>
+__global__ void __launch_bounds__(SCORE_THREADS) score_mfma_kernel(const float* __restrict__ q_pred,
+                                                                   const uint16_t* __restrict__ k,
+                                                                   const int32_t* __restrict__ seq_lens,
+                                                                   float* __restrict__ scores,
+                                                                   uint32_t* __restrict__ hist, int Hq, int Hkv,
+                                                                   int T_cap) {
+  constexpr int S = D / 32;  // MFMA steps over the coordinates
+  constexpr int U = 4;       // 16-key tiles in flight per wave
+  __shared__ uint32_t lhist[HIST ? HIST_BINS : 1];
+
+  const int unit = blockIdx.y;
+  const int b = unit / Hkv, g = unit % Hkv;
+  const int T = clampi(seq_lens[b], 0, T_cap);
+  const int k0 = blockIdx.x * SCORE_KEYS_PER_BLOCK;
+  if (k0 >= T) return;
+  const int k1 = min(k0 + SCORE_KEYS_PER_BLOCK, T);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = lane & 15, c = lane >> 4;
+
+  if constexpr (HIST) {
+    for (int i = threadIdx.x; i < HIST_BINS; i += SCORE_THREADS) lhist[i] = 0u;
+    __syncthreads();
+  }
+
+  // A operand: row j = query head j of the group (zero rows past G), step s
+  // covers coordinates 32s + 8c .. 32s + 8c + 7.
+  bf16x8 ahi[S], alo[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    u32x4 hi = {0u, 0u, 0u, 0u}, lo = {0u, 0u, 0u, 0u};
+    if (j < G) {
+      const float* qh = q_pred + ((size_t)b * Hq + (size_t)g * G + j) * D + 32 * s + 8 * c;
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float x0 = qh[e], x1 = qh[e + 1];
+        const uint32_t h0 = bf16_rne_bits(x0), h1 = bf16_rne_bits(x1);
+        const uint32_t l0 = bf16_rne_bits(x0 - __uint_as_float(h0 << 16));
+        const uint32_t l1 = bf16_rne_bits(x1 - __uint_as_float(h1 << 16));
+        hi[e / 2] = h0 | (h1 << 16);
+        lo[e / 2] = l0 | (l1 << 16);
+      }
+    }
+    ahi[s] = __builtin_bit_cast(bf16x8, hi);
+    alo[s] = __builtin_bit_cast(bf16x8, lo);
+  }
+
+  const uint16_t* kb = k + (size_t)unit * T_cap * D + 8 * c;
+  float* sb = scores + (size_t)unit * T_cap;
+
+  for (int base = k0 + wave * 16 * U; base < k1; base += SCORE_WAVES * 16 * U) {
+    u32x4 kr[U][S];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int key = base + u * 16 + j;
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+        kr[u][s] = key < k1 ? *reinterpret_cast<const u32x4*>(kb + (size_t)key * D + 32 * s)
+                            : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const bf16x8 bk = __builtin_bit_cast(bf16x8, kr[u][s]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[s], bk, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[s], bk, acc, 0, 0, 0);
+      }
+      // lane (c, j) holds heads 4c .. 4c+3 of key base + 16u + j
+      float m = acc[0];
+      if constexpr (G >= 2) m = fmaxf(m, acc[1]);
+      if constexpr (G >= 4) m = fmaxf(fmaxf(m, acc[2]), acc[3]);
+      if constexpr (G == 8) m = fmaxf(m, __shfl_xor(m, 16));
+      const int key = base + u * 16 + j;
+      if (c == 0 && key < k1) {
+        sb[key] = m;
+        if constexpr (HIST) atomicAdd(&lhist[order_key(m) >> HIST_SHIFT], 1u);
+      }
+    }
+  }
+  if constexpr (HIST) {
+    __syncthreads();
+    uint32_t* gh = hist + (size_t)unit * HIST_BINS;
+    for (int i = threadIdx.x; i < HIST_BINS; i += SCORE_THREADS) {
+      const uint32_t v = lhist[i];
+      if (v) atomicAdd(&gh[i], v);
+    }
   }
 }
 
-template <typename KV, int D, int G>
+template <int D, int G, bool HIST>
 __global__ void __launch_bounds__(SCORE_THREADS) score_valu_kernel(const float* __restrict__ q_pred,
-                                                                   const KV* __restrict__ k,
+                                                                   const float* __restrict__ k,
                                                                    const int32_t* __restrict__ seq_lens,
-                                                                   float* __restrict__ scores, int Hq, int Hkv,
+                                                                   float* __restrict__ scores,
+                                                                   uint32_t* __restrict__ hist, int Hq, int Hkv,
                                                                    int T_cap) {
-  constexpr int EPL = 16 / (int)sizeof(KV);  // elements per 16-byte load
-  constexpr int LPK = D / EPL;               // lanes per key row
-  constexpr int KPW = 64 / LPK;              // keys per wave-wide load
-  constexpr int U = 4;                       // loads in flight per lane
-  constexpr int WAVES = SCORE_THREADS / 64;
+  constexpr int EPL = 4;           // fp32 elements per 16-byte load
+  constexpr int LPK = D / EPL;     // lanes per key row
+  constexpr int KPW = 64 / LPK;    // keys per wave-wide load
+  constexpr int U = 4;             // loads in flight per lane
+  __shared__ uint32_t lhist[HIST ? HIST_BINS : 1];
 
   const int unit = blockIdx.y;
   const int b = unit / Hkv, g = unit % Hkv;
@@ -53,6 +153,10 @@ __global__ void __launch_bounds__(SCORE_THREADS) score_valu_kernel(const float* 
   const int k1 = min(k0 + SCORE_KEYS_PER_BLOCK, T);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane % LPK, kl = lane / LPK;
+  if constexpr (HIST) {
+    for (int i = threadIdx.x; i < HIST_BINS; i += SCORE_THREADS) lhist[i] = 0u;
+    __syncthreads();
+  }
 
   float q[G][EPL];
 #pragma unroll
@@ -61,20 +165,19 @@ __global__ void __launch_bounds__(SCORE_THREADS) score_valu_kernel(const float* 
 #pragma unroll
     for (int e = 0; e < EPL; ++e) q[h][e] = qh[e];
   }
-  const KV* kb = k + (size_t)unit * T_cap * D + sub * EPL;
+  const float* kb = k + (size_t)unit * T_cap * D + sub * EPL;
   float* sb = scores + (size_t)unit * T_cap;
 
-  for (int base = k0 + wave * KPW * U; base < k1; base += WAVES * KPW * U) {
-    uint4 raw[U];
+  for (int base = k0 + wave * KPW * U; base < k1; base += SCORE_WAVES * KPW * U) {
+    float4 raw[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int key = base + u * KPW + kl;
-      raw[u] = key < k1 ? *reinterpret_cast<const uint4*>(kb + (size_t)key * D) : make_uint4(0, 0, 0, 0);
+      raw[u] = key < k1 ? *reinterpret_cast<const float4*>(kb + (size_t)key * D) : make_float4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float x[EPL];
-      unpack16<KV>(raw[u], x);
+      const float x[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
       float best = 0.0f;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
@@ -85,35 +188,55 @@ __global__ void __launch_bounds__(SCORE_THREADS) score_valu_kernel(const float* 
         best = h == 0 ? acc : fmaxf(best, acc);
       }
       const int key = base + u * KPW + kl;
-      if (sub == 0 && key < k1) sb[key] = best;
+      if (sub == 0 && key < k1) {
+        sb[key] = best;
+        if constexpr (HIST) atomicAdd(&lhist[order_key(best) >> HIST_SHIFT], 1u);
+      }
+    }
+  }
+  if constexpr (HIST) {
+    __syncthreads();
+    uint32_t* gh = hist + (size_t)unit * HIST_BINS;
+    for (int i = threadIdx.x; i < HIST_BINS; i += SCORE_THREADS) {
+      const uint32_t v = lhist[i];
+      if (v) atomicAdd(&gh[i], v);
     }
   }
 }
 
-template <typename KV, int D>
-static hipError_t launch_score_d(const Shape& s, const float* q_pred, const void* k, const int32_t* seq_lens,
-                                 float* scores, hipStream_t st) {
+template <int D, bool HIST>
+static hipError_t launch_score_dh(const Shape& s, const float* q_pred, const void* k, const int32_t* seq_lens,
+                                  float* scores, uint32_t* hist, hipStream_t st) {
   const dim3 grid((s.T_cap + SCORE_KEYS_PER_BLOCK - 1) / SCORE_KEYS_PER_BLOCK, s.B * s.Hkv);
-  const KV* kk = static_cast<const KV*>(k);
+  const dim3 block(SCORE_THREADS);
+#define ASP_SCORE_LAUNCH(GG)                                                                                   \
+  do {                                                                                                         \
+    if (s.kv == 0)                                                                                             \
+      hipLaunchKernelGGL((score_mfma_kernel<D, GG, HIST>), grid, block, 0, st, q_pred,                        \
+                         static_cast<const uint16_t*>(k), seq_lens, scores, hist, s.Hq, s.Hkv, s.T_cap);      \
+    else                                                                                                       \
+      hipLaunchKernelGGL((score_valu_kernel<D, GG, HIST>), grid, block, 0, st, q_pred,                        \
+                         static_cast<const float*>(k), seq_lens, scores, hist, s.Hq, s.Hkv, s.T_cap);         \
+  } while (0)
   switch (s.G) {
-    case 1: hipLaunchKernelGGL((score_valu_kernel<KV, D, 1>), grid, dim3(SCORE_THREADS), 0, st, q_pred, kk, seq_lens, scores, s.Hq, s.Hkv, s.T_cap); break;
-    case 2: hipLaunchKernelGGL((score_valu_kernel<KV, D, 2>), grid, dim3(SCORE_THREADS), 0, st, q_pred, kk, seq_lens, scores, s.Hq, s.Hkv, s.T_cap); break;
-    case 4: hipLaunchKernelGGL((score_valu_kernel<KV, D, 4>), grid, dim3(SCORE_THREADS), 0, st, q_pred, kk, seq_lens, scores, s.Hq, s.Hkv, s.T_cap); break;
-    case 8: hipLaunchKernelGGL((score_valu_kernel<KV, D, 8>), grid, dim3(SCORE_THREADS), 0, st, q_pred, kk, seq_lens, scores, s.Hq, s.Hkv, s.T_cap); break;
+    case 1: ASP_SCORE_LAUNCH(1); break;
+    case 2: ASP_SCORE_LAUNCH(2); break;
+    case 4: ASP_SCORE_LAUNCH(4); break;
+    case 8: ASP_SCORE_LAUNCH(8); break;
     default: return hipErrorInvalidValue;
   }
+#undef ASP_SCORE_LAUNCH
   return hipGetLastError();
 }
 
 hipError_t launch_score(const Shape& s, const float* q_pred, const void* k, const int32_t* seq_lens, float* scores,
-                        hipStream_t st) {
+                        uint32_t* hist, hipStream_t st) {
   if (s.B == 0) return hipSuccess;
-  if (s.kv == 0) {
-    return s.D == 64 ? launch_score_d<uint16_t, 64>(s, q_pred, k, seq_lens, scores, st)
-                     : launch_score_d<uint16_t, 128>(s, q_pred, k, seq_lens, scores, st);
-  }
-  return s.D == 64 ? launch_score_d<float, 64>(s, q_pred, k, seq_lens, scores, st)
-                   : launch_score_d<float, 128>(s, q_pred, k, seq_lens, scores, st);
+  if (hist != nullptr)
+    return s.D == 64 ? launch_score_dh<64, true>(s, q_pred, k, seq_lens, scores, hist, st)
+                     : launch_score_dh<128, true>(s, q_pred, k, seq_lens, scores, hist, st);
+  return s.D == 64 ? launch_score_dh<64, false>(s, q_pred, k, seq_lens, scores, nullptr, st)
+                   : launch_score_dh<128, false>(s, q_pred, k, seq_lens, scores, nullptr, st);
 }
 
 }  // namespace asp

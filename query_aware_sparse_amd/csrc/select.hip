@@ -22,16 +22,7 @@ constexpr int SEL_THREADS = 1024;
 constexpr int SEL_WAVES = SEL_THREADS / 64;
 constexpr int KEYBUF = 32768;
 constexpr int KEYBUF_PADDED = KEYBUF + KEYBUF / 32;
-constexpr int NBINS = 2048;
-
-// Monotone map from float to uint32: a > b (as numbers) iff key(a) > key(b);
-// NaN maps to the key of -inf and -0 to the key of +0.
-__device__ __forceinline__ uint32_t order_key(float s) {
-  uint32_t u = __float_as_uint(s);
-  if ((u & 0x7fffffffu) > 0x7f800000u) u = 0xff800000u;
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
+constexpr int NBINS = HIST_BINS;
 
 // One padding word every 32 keys keeps a thread's contiguous segment on
 // distinct LDS banks from its neighbours' segments.
@@ -60,9 +51,12 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* scratch, ui
 }
 
 __global__ void __launch_bounds__(SEL_THREADS) select_kernel(const float* __restrict__ scores,
+                                                             const uint32_t* __restrict__ coarse,
                                                              const int32_t* __restrict__ seq_lens,
                                                              int32_t* __restrict__ idx, int32_t* __restrict__ n_sel,
-                                                             int Hkv, int T_cap, int C) {
+                                                             int32_t* __restrict__ adv_newest,
+                                                             int32_t* __restrict__ adv_len, int Hkv, int T_cap,
+                                                             int C, int W) {
   __shared__ uint32_t keys[KEYBUF_PADDED];
   __shared__ uint32_t hist[NBINS];
   __shared__ uint32_t scratch[SEL_WAVES];
@@ -76,6 +70,14 @@ __global__ void __launch_bounds__(SEL_THREADS) select_kernel(const float* __rest
   int32_t* out = idx + (size_t)unit * C;
   const float* row = scores + (size_t)unit * T_cap;
 
+  // Ring advance of a fused step: the predictor launch of the same step has
+  // read newest/len for every head and written the new query one slot ahead.
+  if (adv_newest != nullptr && unit % Hkv == 0 && tid == 0) {
+    int o = adv_newest[b] % W;
+    if (o < 0) o += W;
+    adv_newest[b] = o + 1 == W ? 0 : o + 1;
+    adv_len[b] = min(clampi(adv_len[b], 0, W) + 1, W);
+  }
   for (int j = c_eff + tid; j < C; j += SEL_THREADS) out[j] = -1;
   if (tid == 0) n_sel[unit] = c_eff;
   if (c_eff == T) {  // everything is selected (includes the empty row)
@@ -95,15 +97,21 @@ __global__ void __launch_bounds__(SEL_THREADS) select_kernel(const float* __rest
   const int shifts[3] = {21, 10, 0};
   const uint32_t dmask[3] = {0x7ffu, 0x7ffu, 0x3ffu};
   for (int pass = 0; pass < 3; ++pass) {
-    for (int j = tid; j < NBINS; j += SEL_THREADS) hist[j] = 0;
-    __syncthreads();
     const int sh = shifts[pass];
     const uint32_t dm = dmask[pass];
-    for (int i = tid; i < T; i += SEL_THREADS) {
-      const uint32_t key = resident ? keys[padded(i)] : order_key(row[i]);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & dm], 1u);
+    if (pass == 0 && coarse != nullptr) {  // first digit already binned by the score launch
+      const uint32_t* ch = coarse + (size_t)unit * NBINS;
+      for (int j = tid; j < NBINS; j += SEL_THREADS) hist[j] = ch[j];
+      __syncthreads();
+    } else {
+      for (int j = tid; j < NBINS; j += SEL_THREADS) hist[j] = 0;
+      __syncthreads();
+      for (int i = tid; i < T; i += SEL_THREADS) {
+        const uint32_t key = resident ? keys[padded(i)] : order_key(row[i]);
+        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & dm], 1u);
+      }
+      __syncthreads();
     }
-    __syncthreads();
     // Find digit d with (#keys with digit > d) < need <= (#keys with digit >= d).
     // Thread t owns bins 2047-2t and 2046-2t, so a prefix scan over threads is
     // a suffix scan over bins.
@@ -175,11 +183,11 @@ __global__ void __launch_bounds__(SEL_THREADS) select_kernel(const float* __rest
   }
 }
 
-hipError_t launch_select(const Shape& s, const float* scores, const int32_t* seq_lens, int32_t* idx,
-                         int32_t* n_sel, hipStream_t st) {
+hipError_t launch_select(const Shape& s, const float* scores, const uint32_t* hist, const int32_t* seq_lens,
+                         int32_t* idx, int32_t* n_sel, int32_t* adv_newest, int32_t* adv_len, hipStream_t st) {
   if (s.B == 0) return hipSuccess;
-  hipLaunchKernelGGL(select_kernel, dim3(s.B * s.Hkv), dim3(SEL_THREADS), 0, st, scores, seq_lens, idx, n_sel,
-                     s.Hkv, s.T_cap, s.C);
+  hipLaunchKernelGGL(select_kernel, dim3(s.B * s.Hkv), dim3(SEL_THREADS), 0, st, scores, hist, seq_lens, idx, n_sel,
+                     adv_newest, adv_len, s.Hkv, s.T_cap, s.C, s.W > 0 ? s.W : 1);
   return hipGetLastError();
 }
 

@@ -152,7 +152,8 @@ def _step_run(p: Problem, mode: str, n_steps: int):
                            idx[nxt], nsel[nxt], p.out, ws, attn_stream=attn, sel_stream=sel, q_ready=q_ready,
                            idx_cur_ready=ev[cur], idx_next_ready=ev[nxt])
         torch.cuda.synchronize()
-        results.append((np_(p.out).copy(), np_(idx[nxt]).copy(), np_(nsel[nxt]).copy(), np_(p.q_hist).copy()))
+        results.append((np_(p.out).copy(), np_(idx[nxt]).copy(), np_(nsel[nxt]).copy(), np_(p.q_hist).copy(),
+                        np_(p.newest).copy(), np_(p.length).copy()))
     return results
 
 
@@ -174,14 +175,28 @@ def _manual_run(p: Problem, n_steps: int):
         if s == 0:
             A.asp_sparse_decode(d, c, q, p.k, p.v, idx, n_sel, p.out, p.ws_dec)
         torch.cuda.synchronize()
-        results.append((np_(p.out).copy(), np_(idx).copy(), np_(n_sel).copy(), np_(p.q_hist).copy()))
+        results.append((np_(p.out).copy(), np_(idx).copy(), np_(n_sel).copy(), np_(p.q_hist).copy(),
+                        np_(p.newest).copy(), np_(p.length).copy()))
         idx_prev, n_prev = idx, n_sel
     return results
 
 
-@pytest.mark.parametrize("wl_name", ["tiny", "qwen3-8b-layer"])
+SMALL_STEP_CASES = {
+    # ragged bf16, GQA group 8, head_dim 64, the largest window
+    "g8-d64-w64": wk.RAGGED.replace(name="g8-d64-w64", batch=3, n_q_heads=16, n_kv_heads=2, head_dim=64,
+                                    t_cap=5000, seq_len_range=(100, 5000), window=64, top_c=300, history_steps=70),
+    # fp32 KV, group 2, head_dim 128, window 32 (ring not yet full when the steps start)
+    "g2-d128-w32-f32": wk.TINY.replace(name="g2-d128-w32-f32", batch=2, n_q_heads=4, n_kv_heads=2, head_dim=128,
+                                       t_cap=3000, window=32, top_c=500, history_steps=20),
+    # window 4, group 1
+    "g1-d128-w4": wk.TINY.replace(name="g1-d128-w4", batch=2, n_q_heads=2, n_kv_heads=2, head_dim=128,
+                                  t_cap=1000, kv_dtype="bf16", window=4, top_c=1000, history_steps=6),
+}
+
+
+@pytest.mark.parametrize("wl_name", ["tiny", "qwen3-8b-layer"] + list(SMALL_STEP_CASES))
 def test_step_modes_bit_identical_to_entry_points(wl_name):
-    wl = wk.CONFIGS[wl_name]
+    wl = wk.CONFIGS.get(wl_name) or SMALL_STEP_CASES[wl_name]
     n = 5
     runs = {}
     for mode in ("manual", "one_stream", "two_streams"):
