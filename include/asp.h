@@ -15,8 +15,9 @@
  *
  * Conventions shared by every entry point
  *  - All tensor pointers are DEVICE pointers owned by the caller, dense and
- *    row-major in the layout given.  K and V base pointers must be 16-byte
- *    aligned; float arrays 4-byte aligned.
+ *    row-major in the layout given.  K, V, q_cur and q_hist must be 16-byte
+ *    aligned (16-byte vector loads), every other array 4-byte aligned; a
+ *    misaligned pointer is rejected with ASP_ERR_INVALID_ARG.
  *  - A "unit" is one (sequence b, KV head g); G = n_q_heads / n_kv_heads query
  *    heads h = g*G .. g*G+G-1 share KV head g.
  *  - The library allocates nothing, frees nothing, keeps no state between calls
@@ -67,8 +68,9 @@ typedef struct {
 } asp_dims;
 
 /* Method configuration.  window W: ring length, a multiple of 4 in [4, 64];
- * top_c C: tokens kept per unit, 1 <= C <= t_cap; lambda: ridge penalty,
- * finite and > 0. */
+ * top_c C: tokens kept per unit, 1 <= C <= t_cap (and C <= 256 attention
+ * blocks: 32768 for bf16 and head_dim 128, else ASP_ERR_UNSUPPORTED);
+ * lambda: ridge penalty, finite and > 0. */
 typedef struct {
   int32_t window;
   int32_t top_c;
@@ -111,8 +113,9 @@ asp_status asp_push_query(const asp_dims* dims, const asp_cfg* cfg, const float*
  *   alpha = softmax(beta); q_hat_w = sum_j alpha_j q_{t+1-j};
  *   q_pred = mean over the windows of q_hat_w;
  *   no window (n = 1): q_pred = q_t; n = 0: q_pred = 0.
- * The Gram matrix and the solve are computed in fp64 (one Cholesky factor
- * serves all windows: a smaller window's system is a leading block).
+ * The Gram matrix and the solve are computed in fp64 (one L D L^T
+ * factorisation serves all windows: a smaller window's system is a leading
+ * block).
  * Output q_pred[B][Hq][D] fp32. */
 asp_status asp_predict_query(const asp_dims* dims, const asp_cfg* cfg, const float* q_hist,
                              const int32_t* hist_newest, const int32_t* hist_len, float* q_pred,

@@ -132,7 +132,13 @@ def _ws(ws: Optional[torch.Tensor]):
 
 
 class HipEvent:
-    """A HIP event (timing disabled), for asp_step's stream ordering."""
+    """A HIP event for asp_step's ordering of two streams on one device.
+
+    Created with timing disabled and without the system-scope fence: the event
+    only orders work between streams of the same GPU (each kernel already
+    publishes its writes device-wide when it ends), so the cache writeback a
+    system-scope release would add to every record is not needed.
+    """
 
     _hip = None
 
@@ -145,14 +151,16 @@ class HipEvent:
             hip.hipEventDestroy.restype = ctypes.c_int
             HipEvent._hip = hip
         h = ctypes.c_void_p()
-        rc = HipEvent._hip.hipEventCreateWithFlags(ctypes.byref(h), 0x2)  # hipEventDisableTiming
+        # hipEventDisableTiming | hipEventDisableSystemFence
+        rc = HipEvent._hip.hipEventCreateWithFlags(ctypes.byref(h), 0x2 | 0x20000000)
         if rc != 0:
             raise AspError("hipEventCreateWithFlags failed (%d)" % rc)
         self.handle = h
 
     def __del__(self):
-        if getattr(self, "handle", None) and HipEvent._hip is not None:
-            HipEvent._hip.hipEventDestroy(self.handle)
+        hip = getattr(HipEvent, "_hip", None)
+        if getattr(self, "handle", None) and hip is not None:
+            hip.hipEventDestroy(self.handle)
             self.handle = None
 
 

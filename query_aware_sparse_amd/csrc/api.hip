@@ -46,6 +46,8 @@ asp_status check_cfg(const asp_cfg* c, Shape* s) {
   if (c->window < 4 || c->window > 64 || c->window % 4 != 0) return ASP_ERR_INVALID_ARG;
   if (c->top_c < 1 || c->top_c > s->T_cap) return ASP_ERR_INVALID_ARG;
   if (!(c->lambda > 0.0) || !isfinite(c->lambda)) return ASP_ERR_INVALID_ARG;
+  if ((c->top_c + asp::attend_tokens_per_block(s->D, s->kv) - 1) / asp::attend_tokens_per_block(s->D, s->kv) > 256)
+    return ASP_ERR_UNSUPPORTED;  // more attention splits than the merge handles
   s->W = c->window;
   s->C = c->top_c;
   s->lambda = c->lambda;
@@ -83,6 +85,10 @@ size_t ws_bytes_for(const Shape& s, asp_op op) {
 }
 
 asp_status hip_status(hipError_t e) { return e == hipSuccess ? ASP_OK : ASP_ERR_HIP; }
+
+// The kernels use 16-byte vector loads on K, V, queries and the ring.
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 #define ASP_TRY_HIP(expr)                          \
   do {                                             \
@@ -128,6 +134,7 @@ asp_status asp_push_query(const asp_dims* dims, const asp_cfg* cfg, const float*
   asp_status st = check_all(dims, cfg, &s);
   if (st != ASP_OK) return st;
   if (!q_cur || !q_hist || !hist_newest || !hist_len) return ASP_ERR_INVALID_ARG;
+  if (!aligned16(q_cur) || !aligned16(q_hist)) return ASP_ERR_INVALID_ARG;
   return hip_status(asp::launch_push(s, q_cur, q_hist, hist_newest, hist_len, stream));
 }
 
@@ -138,6 +145,7 @@ asp_status asp_predict_query(const asp_dims* dims, const asp_cfg* cfg, const flo
   asp_status st = check_all(dims, cfg, &s);
   if (st != ASP_OK) return st;
   if (!q_hist || !hist_newest || !hist_len || !q_pred) return ASP_ERR_INVALID_ARG;
+  if (!aligned16(q_hist) || !aligned4(q_pred)) return ASP_ERR_INVALID_ARG;
   return hip_status(asp::launch_predict(s, const_cast<float*>(q_hist), hist_newest, hist_len, nullptr, q_pred, nullptr,
                                         stream));
 }
@@ -148,6 +156,7 @@ asp_status asp_score_keys(const asp_dims* dims, const float* q_pred, const void*
   asp_status st = check_dims(dims, &s);
   if (st != ASP_OK) return st;
   if (!q_pred || !k || !seq_lens || !scores) return ASP_ERR_INVALID_ARG;
+  if (!aligned16(k) || !aligned4(q_pred) || !aligned4(scores)) return ASP_ERR_INVALID_ARG;
   return hip_status(asp::launch_score(s, q_pred, k, seq_lens, scores, nullptr, stream));
 }
 
@@ -157,6 +166,7 @@ asp_status asp_select_topc(const asp_dims* dims, const asp_cfg* cfg, const float
   asp_status st = check_all(dims, cfg, &s);
   if (st != ASP_OK) return st;
   if (!scores || !seq_lens || !idx || !n_sel) return ASP_ERR_INVALID_ARG;
+  if (!aligned4(scores)) return ASP_ERR_INVALID_ARG;
   const size_t need = ws_bytes_for(s, ASP_OP_SELECT);
   if (need > 0 && (ws == nullptr || ws_bytes < need)) return ASP_ERR_WORKSPACE;
   return hip_status(asp::launch_select(s, scores, nullptr, seq_lens, idx, n_sel, nullptr, nullptr, stream));
@@ -169,6 +179,7 @@ asp_status asp_sparse_decode(const asp_dims* dims, const asp_cfg* cfg, const flo
   asp_status st = check_all(dims, cfg, &s);
   if (st != ASP_OK) return st;
   if (!q || !k || !v || !idx || !n_sel || !out) return ASP_ERR_INVALID_ARG;
+  if (!aligned16(k) || !aligned16(v) || !aligned4(q) || !aligned4(out)) return ASP_ERR_INVALID_ARG;
   const size_t need = ws_bytes_for(s, ASP_OP_DECODE);
   if (ws == nullptr || ws_bytes < need) return ASP_ERR_WORKSPACE;
   return hip_status(asp::launch_attend(s, q, k, v, idx, n_sel, out, ws, stream));
@@ -186,6 +197,9 @@ asp_status asp_step(const asp_dims* dims, const asp_cfg* cfg, const float* q_cur
   if (!q_cur || !q_hist || !hist_newest || !hist_len || !k || !v || !seq_lens || !idx_next || !n_sel_next || !out)
     return ASP_ERR_INVALID_ARG;
   if ((idx_cur == nullptr) != (n_sel_cur == nullptr)) return ASP_ERR_INVALID_ARG;
+  if (!aligned16(q_cur) || !aligned16(q_hist) || !aligned16(k) || !aligned16(v) || !aligned4(out))
+    return ASP_ERR_INVALID_ARG;
+  if (!aligned4(ws)) return ASP_ERR_WORKSPACE;
   const bool pipelined = idx_cur != nullptr;
   const bool two_streams = pipelined && sel_stream != nullptr && sel_stream != attn_stream;
   if (two_streams && q_ready == nullptr) return ASP_ERR_INVALID_ARG;

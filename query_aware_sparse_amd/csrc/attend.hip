@@ -198,31 +198,62 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_kernel(const float* __rest
 }
 
 // One workgroup per (sequence, query head): log-sum-exp merge of the partials.
+// The first wavefront reads the m/l pairs of all splits (independent loads,
+// splits strided over its lanes) and forms the maximum, the split weights and
+// the normaliser with cross-lane reductions; each output coordinate then reads
+// its partial sums with independent loads.
+constexpr int MERGE_MAX_SPLITS = 256;
+
 __global__ void __launch_bounds__(128) merge_kernel(const float* __restrict__ part_acc,
                                                     const float* __restrict__ part_ml,
                                                     const int32_t* __restrict__ n_sel, float* __restrict__ out,
                                                     int Hq, int Hkv, int G, int D, int C, int nsplit, int tpb) {
+  constexpr int PER = MERGE_MAX_SPLITS / 64;
+  __shared__ float sw[MERGE_MAX_SPLITS];
+  __shared__ float s_inv_l;
   const int bh = blockIdx.x;
   const int b = bh / Hq, h = bh % Hq;
   const int g = h / G, hh = h % G;
   const int unit = b * Hkv + g;
   const int n = clampi(n_sel[unit], 0, C);
-  const int ns = (n + tpb - 1) / tpb;
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, part_ml[(((size_t)unit * nsplit + s) * G + hh) * 2]);
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float L = 0.0f, o = 0.0f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < ns; ++s) {
-        const size_t p = ((size_t)unit * nsplit + s) * G + hh;
-        const float ms = part_ml[p * 2];
-        if (ms == -INFINITY) continue;
-        const float w = exp2f(ms - M);
-        L = fmaf(part_ml[p * 2 + 1], w, L);
-        o = fmaf(part_acc[p * D + d], w, o);
+  const int ns = min((n + tpb - 1) / tpb, MERGE_MAX_SPLITS);
+  const int t = threadIdx.x;
+  if (t < 64) {
+    float m[PER], l[PER];
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int sp = t + 64 * r;
+      m[r] = -INFINITY;
+      l[r] = 0.0f;
+      if (sp < ns) {
+        const size_t p = ((size_t)unit * nsplit + sp) * G + hh;
+        m[r] = part_ml[p * 2];
+        l[r] = part_ml[p * 2 + 1];
       }
     }
-    out[(size_t)bh * D + d] = L > 0.0f ? o / L : 0.0f;
+    float mx = m[0];
+#pragma unroll
+    for (int r = 1; r < PER; ++r) mx = fmaxf(mx, m[r]);
+    const float M = group_max<64>(mx);
+    float lw = 0.0f;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int sp = t + 64 * r;
+      // splits whose tokens were all skipped carry m = -inf and l = 0
+      const float w = (sp < ns && m[r] != -INFINITY) ? exp2f(m[r] - M) : 0.0f;
+      if (sp < ns) sw[sp] = w;
+      lw = fmaf(l[r], w, lw);
+    }
+    const float L = group_sum<64>(lw);
+    if (t == 0) s_inv_l = L > 0.0f ? 1.0f / L : 0.0f;
+  }
+  __syncthreads();
+  const float inv_l = s_inv_l;
+  for (int d = t; d < D; d += blockDim.x) {
+    float o = 0.0f;
+    const float* pa = part_acc + (((size_t)unit * nsplit) * G + hh) * D + d;
+    for (int s = 0; s < ns; ++s) o = fmaf(pa[(size_t)s * G * D], sw[s], o);
+    out[(size_t)bh * D + d] = o * inv_l;
   }
 }
 

@@ -14,8 +14,12 @@
 //
 // bf16 keys: the G x D query block times a 16-key tile is one
 // v_mfma_f32_16x16x32_bf16 per 32 coordinates, with the keys as the B operand
-// straight from the 16-byte loads (lane l: key l%16, coordinates 8*(l/16)..+7
-// of each 32-wide step) and the query heads as rows of the A operand.  The
+// (lane l: key l%16, coordinates 8*(l/16)..+7 of each 32-wide step) and the
+// query heads as rows of the A operand.  Keys arrive with fully coalesced
+// non-temporal 16-byte loads (each wave-wide load covers whole key rows) and
+// are transposed into the MFMA layout through a per-wave, XOR-swizzled LDS
+// tile: loading 64-byte column slices of 16 rows straight into the operand
+// layout costs ~15% of the bandwidth on this part.  The
 // predicted query is fp32; it enters as two bf16 terms, hi = rne(q) and
 // lo = rne(q - hi), so the product keeps ~17 significant bits of q (relative
 // error <= 2^-18 per term) and accumulates in fp32.
@@ -48,8 +52,12 @@ __global__ void __launch_bounds__(SCORE_THREADS) score_mfma_kernel(const float* 
                                                                    float* __restrict__ scores,
                                                                    uint32_t* __restrict__ hist, int Hq, int Hkv,
                                                                    int T_cap) {
-  constexpr int S = D / 32;  // MFMA steps over the coordinates
-  constexpr int U = 4;       // 16-key tiles in flight per wave
+  constexpr int S = D / 32;          // MFMA steps over the coordinates
+  constexpr int CH = D * 2 / 16;     // 16-byte chunks per key row
+  constexpr int RPI = 64 / CH;       // key rows per wave-wide load
+  constexpr int NI = 16 / RPI;       // loads per 16-key tile
+  constexpr int U = 4;               // 16-key tiles per wave and iteration
+  __shared__ u32x4 tile[SCORE_WAVES][U][16][CH];
   __shared__ uint32_t lhist[HIST ? HIST_BINS : 1];
 
   const int unit = blockIdx.y;
@@ -59,7 +67,8 @@ __global__ void __launch_bounds__(SCORE_THREADS) score_mfma_kernel(const float* 
   if (k0 >= T) return;
   const int k1 = min(k0 + SCORE_KEYS_PER_BLOCK, T);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int j = lane & 15, c = lane >> 4;
+  const int j = lane & 15, c = lane >> 4;          // MFMA roles: key column j, coordinate group c
+  const int lrow = lane / CH, lchunk = lane % CH;  // load roles: row in the load, 16-byte chunk
 
   if constexpr (HIST) {
     for (int i = threadIdx.x; i < HIST_BINS; i += SCORE_THREADS) lhist[i] = 0u;
@@ -88,25 +97,40 @@ __global__ void __launch_bounds__(SCORE_THREADS) score_mfma_kernel(const float* 
     alo[s] = __builtin_bit_cast(bf16x8, lo);
   }
 
-  const uint16_t* kb = k + (size_t)unit * T_cap * D + 8 * c;
+  const u32x4* kb = reinterpret_cast<const u32x4*>(k + (size_t)unit * T_cap * D);
   float* sb = scores + (size_t)unit * T_cap;
 
   for (int base = k0 + wave * 16 * U; base < k1; base += SCORE_WAVES * 16 * U) {
-    u32x4 kr[U][S];
+    // Coalesced non-temporal loads: each wave-wide load is RPI whole key rows.
+    u32x4 gld[U][NI];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int key = base + u * 16 + j;
 #pragma unroll
-      for (int s = 0; s < S; ++s)
-        kr[u][s] = key < k1 ? *reinterpret_cast<const u32x4*>(kb + (size_t)key * D + 32 * s)
-                            : u32x4{0u, 0u, 0u, 0u};
+      for (int i = 0; i < NI; ++i) {
+        const int key = base + u * 16 + RPI * i + lrow;
+        gld[u][i] = key < k1 ? __builtin_nontemporal_load(kb + (size_t)key * CH + lchunk) : u32x4{0u, 0u, 0u, 0u};
+      }
     }
+    // Transpose through LDS: chunk q of tile row r is stored at q ^ (r % CH),
+    // which keeps both the row-wise writes and the column-wise reads spread
+    // over all banks.
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int r = RPI * i + lrow;
+        tile[wave][u][r][lchunk ^ (r % CH)] = gld[u][i];
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        const bf16x8 bk = __builtin_bit_cast(bf16x8, kr[u][s]);
+        const bf16x8 bk = __builtin_bit_cast(bf16x8, tile[wave][u][j][(4 * s + c) ^ (j % CH)]);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[s], bk, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[s], bk, acc, 0, 0, 0);
       }
@@ -121,6 +145,10 @@ __global__ void __launch_bounds__(SCORE_THREADS) score_mfma_kernel(const float* 
         if constexpr (HIST) atomicAdd(&lhist[order_key(m) >> HIST_SHIFT], 1u);
       }
     }
+    // The next iteration overwrites this wave's tile.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
   if constexpr (HIST) {
     __syncthreads();

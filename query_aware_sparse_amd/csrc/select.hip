@@ -7,26 +7,54 @@
 // with +0, and the lower index wins a tie.
 //
 // One 1024-thread workgroup per unit.  Scores become order-preserving 32-bit
-// keys; an MSD radix select (digits of 11, 11 and 10 bits, histograms in LDS)
-// narrows down the exact C_eff-th key tau and how many of the keys equal to
-// tau are still needed; a final ordered compaction (per-thread contiguous
-// segments plus one block-wide scan per chunk) writes every key above tau and
-// the first needed keys equal to tau, in index order.  Up to 32768 keys are
-// kept in LDS for every pass; longer rows are read from L2 on each pass and
-// staged through LDS in 32768-key chunks for the compaction.
+// keys; an MSD radix select (digits of 11, 11 and 10 bits) finds the exact
+// C_eff-th key tau and how many keys equal to tau are still needed; an ordered
+// compaction then writes every key above tau and the first needed keys equal
+// to tau, in index order.
+//  * The first digit's histogram comes from the score launch when given (it
+//    was binned while the keys streamed), so the boundary bin is known before
+//    the row is read; while the row is staged in LDS, the keys of that bin
+//    (their number is the bin count) are copied to a short candidate list and
+//    the remaining digits are resolved on that list alone.
+//  * Rows up to 32768 keys stay in LDS for every pass; longer rows are read
+//    from L2 on each pass and staged through LDS in 32768-key chunks for the
+//    compaction.
+//  * Compaction: each thread owns a contiguous segment (at most 32 keys, kept
+//    in registers), one block-wide scan per chunk gives every thread its
+//    output offset.
 #include "asp_internal.h"
 
 namespace asp {
 
 constexpr int SEL_THREADS = 1024;
 constexpr int SEL_WAVES = SEL_THREADS / 64;
-constexpr int KEYBUF = 32768;
+constexpr int KEYBUF = 32768;                   // keys staged in LDS
 constexpr int KEYBUF_PADDED = KEYBUF + KEYBUF / 32;
+constexpr int SEG_MAX = KEYBUF / SEL_THREADS;   // keys per thread in a compaction chunk
+constexpr int CAND_MAX = 3072;                  // boundary-bin candidates kept in LDS
 constexpr int NBINS = HIST_BINS;
+constexpr int LOAD_BATCH = 8;                   // global loads in flight per thread
 
 // One padding word every 32 keys keeps a thread's contiguous segment on
 // distinct LDS banks from its neighbours' segments.
 __device__ __forceinline__ int padded(int i) { return i + (i >> 5); }
+
+// Wave-aggregated append to the candidate list: one LDS atomic per wave.  A
+// count beyond CAND_MAX (only possible with an inconsistent coarse histogram)
+// is detected after the sweep.  Must be reached by every lane of the wave.
+__device__ __forceinline__ void push_cand(uint32_t* cand, uint32_t* n_cand, bool pred, uint32_t key) {
+  const unsigned long long mask = __ballot(pred);
+  if (mask == 0ull) return;
+  const int lane = threadIdx.x & 63;
+  const int leader = __ffsll((long long)mask) - 1;
+  uint32_t base = 0;
+  if (lane == leader) base = atomicAdd(n_cand, (uint32_t)__popcll(mask));
+  base = (uint32_t)__builtin_amdgcn_readlane((int)base, leader);
+  if (pred) {
+    const uint32_t p = base + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
+    if (p < (uint32_t)CAND_MAX) cand[p] = key;
+  }
+}
 
 // Inclusive scan over the 1024 threads of the block; *total receives the sum.
 __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* scratch, uint32_t* total) {
@@ -50,6 +78,36 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* scratch, ui
   return v + before;
 }
 
+// Given hist[] filled for the current digit, find the digit d with
+// (#keys with digit > d) < need <= (#keys with digit >= d); narrow
+// prefix/pmask and need.  Returns true when every key of bin d is taken.
+__device__ __forceinline__ bool pick_digit(const uint32_t* hist, uint32_t* scratch, uint32_t* sh, int shift,
+                                           uint32_t dmask, uint32_t& prefix, uint32_t& pmask, uint32_t& need) {
+  const int tid = threadIdx.x;
+  // Thread t owns bins 2047-2t and 2046-2t: a prefix scan over threads is a
+  // suffix scan over bins.
+  const int hi = NBINS - 1 - 2 * tid, lo = hi - 1;
+  const uint32_t chi = hist[hi], clo = hist[lo];
+  uint32_t total;
+  const uint32_t incl = block_scan(chi + clo, scratch, &total);
+  const uint32_t excl = incl - chi - clo;
+  if (excl < need && need <= excl + chi) {
+    sh[0] = (uint32_t)hi;
+    sh[1] = excl;
+  } else if (excl + chi < need && need <= incl) {
+    sh[0] = (uint32_t)lo;
+    sh[1] = excl + chi;
+  }
+  __syncthreads();
+  const uint32_t d = sh[0];
+  need -= sh[1];
+  prefix |= d << shift;
+  pmask |= dmask << shift;
+  const bool whole = hist[d] == need;
+  __syncthreads();
+  return whole;
+}
+
 __global__ void __launch_bounds__(SEL_THREADS) select_kernel(const float* __restrict__ scores,
                                                              const uint32_t* __restrict__ coarse,
                                                              const int32_t* __restrict__ seq_lens,
@@ -59,8 +117,10 @@ __global__ void __launch_bounds__(SEL_THREADS) select_kernel(const float* __rest
                                                              int C, int W) {
   __shared__ uint32_t keys[KEYBUF_PADDED];
   __shared__ uint32_t hist[NBINS];
+  __shared__ uint32_t cand[CAND_MAX];
   __shared__ uint32_t scratch[SEL_WAVES];
-  __shared__ uint32_t sh_digit, sh_above;
+  __shared__ uint32_t sh[2];
+  __shared__ uint32_t n_cand;
 
   const int unit = blockIdx.x;
   const int b = unit / Hkv;
@@ -84,57 +144,131 @@ __global__ void __launch_bounds__(SEL_THREADS) select_kernel(const float* __rest
     for (int j = tid; j < T; j += SEL_THREADS) out[j] = j;
     return;
   }
-
   const bool resident = T <= KEYBUF;
-  if (resident) {
-    for (int i = tid; i < T; i += SEL_THREADS) keys[padded(i)] = order_key(row[i]);
-  }
 
-  // Radix select of the C_eff-th largest key: after each pass, `prefix` holds
-  // the key bits fixed so far (under `pmask`) and `need` how many keys equal
-  // to the prefix must still be taken.
+  // After each digit: `prefix` holds the key bits fixed so far (under
+  // `pmask`), `need` how many keys equal to the prefix must still be taken.
   uint32_t prefix = 0, pmask = 0, need = (uint32_t)c_eff;
+  bool done = false;       // every key equal to the prefix is taken
+  bool have_d0 = false;    // first digit resolved
+  if (tid == 0) n_cand = 0;
+  if (coarse != nullptr) {
+    const uint32_t* ch = coarse + (size_t)unit * NBINS;
+    for (int j = tid; j < NBINS; j += SEL_THREADS) hist[j] = ch[j];
+    __syncthreads();
+    done = pick_digit(hist, scratch, sh, 21, 0x7ffu, prefix, pmask, need);
+    have_d0 = true;
+  }
+  // Candidates of the boundary bin are collected while the keys are read,
+  // when the first digit is already known and they fit.
+  bool collect = have_d0 && !done && hist[prefix >> 21] <= (uint32_t)CAND_MAX;
+
+  if (resident) {
+    for (int base = 0; base < T; base += SEL_THREADS * LOAD_BATCH) {
+      float v[LOAD_BATCH];
+#pragma unroll
+      for (int u = 0; u < LOAD_BATCH; ++u) {
+        const int i = base + u * SEL_THREADS + tid;
+        v[u] = i < T ? row[i] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < LOAD_BATCH; ++u) {
+        const int i = base + u * SEL_THREADS + tid;
+        const uint32_t key = order_key(v[u]);
+        if (i < T) keys[padded(i)] = key;
+        if (collect) push_cand(cand, &n_cand, i < T && (key & pmask) == prefix, key);
+      }
+    }
+  } else if (collect) {
+    for (int base = 0; base < T; base += SEL_THREADS * LOAD_BATCH) {
+      float v[LOAD_BATCH];
+#pragma unroll
+      for (int u = 0; u < LOAD_BATCH; ++u) {
+        const int i = base + u * SEL_THREADS + tid;
+        v[u] = i < T ? row[i] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < LOAD_BATCH; ++u) {
+        const int i = base + u * SEL_THREADS + tid;
+        const uint32_t key = order_key(v[u]);
+        push_cand(cand, &n_cand, i < T && (key & pmask) == prefix, key);
+      }
+    }
+  }
+  __syncthreads();
+
+  if (collect && n_cand > (uint32_t)CAND_MAX) collect = false;
+  // Remaining digits: histogram over the candidate list when it holds exactly
+  // the keys matching the prefix, else over the whole row.
   const int shifts[3] = {21, 10, 0};
   const uint32_t dmask[3] = {0x7ffu, 0x7ffu, 0x3ffu};
-  for (int pass = 0; pass < 3; ++pass) {
-    const int sh = shifts[pass];
+  for (int pass = have_d0 ? 1 : 0; pass < 3 && !done; ++pass) {
+    for (int j = tid; j < NBINS; j += SEL_THREADS) hist[j] = 0;
+    __syncthreads();
+    const int s = shifts[pass];
     const uint32_t dm = dmask[pass];
-    if (pass == 0 && coarse != nullptr) {  // first digit already binned by the score launch
-      const uint32_t* ch = coarse + (size_t)unit * NBINS;
-      for (int j = tid; j < NBINS; j += SEL_THREADS) hist[j] = ch[j];
-      __syncthreads();
-    } else {
-      for (int j = tid; j < NBINS; j += SEL_THREADS) hist[j] = 0;
-      __syncthreads();
-      for (int i = tid; i < T; i += SEL_THREADS) {
-        const uint32_t key = resident ? keys[padded(i)] : order_key(row[i]);
-        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & dm], 1u);
+    if (collect) {
+      const int nc = (int)n_cand;
+      for (int i = tid; i < nc; i += SEL_THREADS) {
+        const uint32_t key = cand[i];
+        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> s) & dm], 1u);
       }
-      __syncthreads();
-    }
-    // Find digit d with (#keys with digit > d) < need <= (#keys with digit >= d).
-    // Thread t owns bins 2047-2t and 2046-2t, so a prefix scan over threads is
-    // a suffix scan over bins.
-    const int hi = NBINS - 1 - 2 * tid, lo = hi - 1;
-    const uint32_t chi = hist[hi], clo = hist[lo];
-    uint32_t total;
-    const uint32_t incl = block_scan(chi + clo, scratch, &total);
-    const uint32_t excl = incl - chi - clo;
-    if (excl < need && need <= excl + chi) {
-      sh_digit = (uint32_t)hi;
-      sh_above = excl;
-    } else if (excl + chi < need && need <= incl) {
-      sh_digit = (uint32_t)lo;
-      sh_above = excl + chi;
+    } else if (resident) {
+      for (int base = 0; base < T; base += SEL_THREADS * LOAD_BATCH) {
+        uint32_t kv[LOAD_BATCH];
+#pragma unroll
+        for (int u = 0; u < LOAD_BATCH; ++u) {
+          const int i = base + u * SEL_THREADS + tid;
+          kv[u] = i < T ? keys[padded(i)] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < LOAD_BATCH; ++u) {
+          const int i = base + u * SEL_THREADS + tid;
+          if (i < T && (kv[u] & pmask) == prefix) atomicAdd(&hist[(kv[u] >> s) & dm], 1u);
+        }
+      }
+    } else {
+      for (int base = 0; base < T; base += SEL_THREADS * LOAD_BATCH) {
+        float v[LOAD_BATCH];
+#pragma unroll
+        for (int u = 0; u < LOAD_BATCH; ++u) {
+          const int i = base + u * SEL_THREADS + tid;
+          v[u] = i < T ? row[i] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < LOAD_BATCH; ++u) {
+          const int i = base + u * SEL_THREADS + tid;
+          const uint32_t key = order_key(v[u]);
+          if (i < T && (key & pmask) == prefix) atomicAdd(&hist[(key >> s) & dm], 1u);
+        }
+      }
     }
     __syncthreads();
-    const uint32_t d = sh_digit;
-    need -= sh_above;
-    prefix |= d << sh;
-    pmask |= dm << sh;
-    const bool whole_bin = hist[d] == need;  // every key of this bin is taken: stop refining
-    __syncthreads();
-    if (whole_bin) break;
+    done = pick_digit(hist, scratch, sh, s, dm, prefix, pmask, need);
+    if (pass == 0) {
+      // Standalone call: the first digit was just found; the refinement can
+      // still run on candidates, gathered by one more sweep.
+      collect = !done && hist[prefix >> 21] <= (uint32_t)CAND_MAX;
+      if (collect) {
+        if (tid == 0) n_cand = 0;
+        __syncthreads();
+        for (int base = 0; base < T; base += SEL_THREADS * LOAD_BATCH) {
+          uint32_t kv[LOAD_BATCH];
+#pragma unroll
+          for (int u = 0; u < LOAD_BATCH; ++u) {
+            const int i = base + u * SEL_THREADS + tid;
+            kv[u] = i < T ? (resident ? keys[padded(i)] : order_key(row[i])) : 0u;
+          }
+#pragma unroll
+          for (int u = 0; u < LOAD_BATCH; ++u) {
+            const int i = base + u * SEL_THREADS + tid;
+            push_cand(cand, &n_cand, i < T && (kv[u] & pmask) == prefix, kv[u]);
+          }
+        }
+        __syncthreads();
+        if (n_cand > (uint32_t)CAND_MAX) collect = false;
+      }
+    }
   }
 
   // Ordered compaction, one chunk of up to KEYBUF keys at a time.
@@ -143,40 +277,60 @@ __global__ void __launch_bounds__(SEL_THREADS) select_kernel(const float* __rest
     const int n = min(KEYBUF, T - c0);
     if (!resident) {
       __syncthreads();
-      for (int i = tid; i < n; i += SEL_THREADS) keys[padded(i)] = order_key(row[c0 + i]);
+      for (int base = 0; base < n; base += SEL_THREADS * LOAD_BATCH) {
+        float v[LOAD_BATCH];
+#pragma unroll
+        for (int u = 0; u < LOAD_BATCH; ++u) {
+          const int i = base + u * SEL_THREADS + tid;
+          v[u] = i < n ? row[c0 + i] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < LOAD_BATCH; ++u) {
+          const int i = base + u * SEL_THREADS + tid;
+          if (i < n) keys[padded(i)] = order_key(v[u]);
+        }
+      }
     }
     __syncthreads();
-    const int seg = (n + SEL_THREADS - 1) / SEL_THREADS;
-    const int s0 = min(tid * seg, n), s1 = min(s0 + seg, n);
-    uint32_t gt = 0, eq = 0;
-    for (int i = s0; i < s1; ++i) {
-      const uint32_t key = keys[padded(i)] & pmask;
-      gt += key > prefix;
-      eq += key == prefix;
+    const int seg = (n + SEL_THREADS - 1) / SEL_THREADS;  // <= SEG_MAX
+    const int s0 = min(tid * seg, n), len = min(s0 + seg, n) - s0;
+    // Bit i of gtm / eqm: key s0+i of this thread's segment is above / equal
+    // to the prefix.
+    uint32_t gtm = 0u, eqm = 0u;
+#pragma unroll
+    for (int i = 0; i < SEG_MAX; ++i) {
+      const uint32_t kv = i < len ? keys[padded(s0 + i)] & pmask : 0u;
+      gtm |= (i < len && kv > prefix) ? (1u << i) : 0u;
+      eqm |= (i < len && kv == prefix) ? (1u << i) : 0u;
     }
+    const uint32_t gt = (uint32_t)__popc(gtm), eq = (uint32_t)__popc(eqm);
     // Counts per chunk are at most 32768, so both fit a 16-bit half.
     uint32_t tot;
     const uint32_t incl = block_scan((gt << 16) | eq, scratch, &tot);
     const uint32_t excl = incl - ((gt << 16) | eq);
     const uint32_t gt_before = excl >> 16, eq_before = excl & 0xffffu;
     const uint32_t gt_tot = tot >> 16, eq_tot = tot & 0xffffu;
-    const uint32_t taken_eq_before = min(eq_seen + eq_before, need) - min(eq_seen, need);
-    uint32_t pos = written + gt_before + taken_eq_before;
-    uint32_t eq_rank = eq_seen + eq_before;
-    for (int i = s0; i < s1; ++i) {
-      const uint32_t key = keys[padded(i)] & pmask;
-      // pos < c_eff always holds when the counts are right; the test keeps a
-      // miscount from ever writing past the row.
-      if (key > prefix) {
-        if (pos < (uint32_t)c_eff) out[pos] = c0 + i;
-        ++pos;
-      } else if (key == prefix) {
-        if (eq_rank < need) {
-          if (pos < (uint32_t)c_eff) out[pos] = c0 + i;
-          ++pos;
-        }
-        ++eq_rank;
-      }
+    // Keys equal to the prefix are taken in index order until `need` are taken:
+    // this thread takes the lowest `take` bits of eqm.  Both counts are formed
+    // as differences of clamped prefix sums (no conditional subtraction: a
+    // select around `need - before_eq` was once folded into a wrong pos).
+    const uint32_t before_eq = eq_seen + eq_before;
+    const uint32_t taken_before = min(before_eq, need);
+    uint32_t take = min(before_eq + eq, need) - taken_before;
+    uint32_t selm = gtm;
+    for (uint32_t m = eqm; take > 0u; --take) {
+      const uint32_t low = m & (0u - m);
+      selm |= low;
+      m ^= low;
+    }
+    // pos < c_eff always holds when the counts are right; the test keeps a
+    // miscount from ever writing past the row.
+    uint32_t pos = written + gt_before + (taken_before - min(eq_seen, need));
+    while (selm != 0u) {
+      const int i = __ffs((int)selm) - 1;
+      selm &= selm - 1u;
+      if (pos < (uint32_t)c_eff) out[pos] = c0 + s0 + i;
+      ++pos;
     }
     written += gt_tot + (min(eq_seen + eq_tot, need) - min(eq_seen, need));
     eq_seen += eq_tot;
