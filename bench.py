@@ -66,7 +66,7 @@ def file_hash(path: str) -> str:
 def measured_traffic(kernel_src: str):
     """HBM traffic of the score kernel from the committed rocprofv3 counter
     summary, or None when the kernel source changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", "score_kernel_traffic.json")
+    path = os.path.join(ROOT, "profiles", "score_keys_qwen3-8b-layer_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
