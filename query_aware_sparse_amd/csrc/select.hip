@@ -56,14 +56,24 @@ __device__ __forceinline__ void push_cand(uint32_t* cand, uint32_t* n_cand, bool
   }
 }
 
+// Inclusive scan over the 64 lanes of a wavefront with DPP: Hillis-Steele
+// inside each 16-lane row (row_shr 1, 2, 4, 8; lanes shifted in from outside
+// the row read 0), then the row totals are carried with row_bcast:15 (into
+// rows 1 and 3) and row_bcast:31 (into rows 2 and 3).
+__device__ __forceinline__ uint32_t wave_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false); // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false); // row_bcast:31
+  return x;
+}
+
 // Inclusive scan over the 1024 threads of the block; *total receives the sum.
 __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* scratch, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t o = __shfl_up(v, off);
-    if (lane >= off) v += o;
-  }
+  v = wave_scan(v);
   if (lane == 63) scratch[wave] = v;
   __syncthreads();
   uint32_t before = 0, tot = 0;
@@ -76,6 +86,36 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* scratch, ui
   __syncthreads();
   *total = tot;
   return v + before;
+}
+
+// Exclusive prefix over the block of a value whose two 16-bit halves are each
+// at most 32 per thread (the compaction's per-thread counts): every bit plane
+// is a ballot, so no cross-lane data movement is needed inside a wave.
+__device__ __forceinline__ uint32_t block_excl_small(uint32_t v, uint32_t* scratch, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t ex = 0u, wt = 0u;
+#pragma unroll
+  for (int half = 0; half < 32; half += 16) {
+#pragma unroll
+    for (int b = 0; b < 6; ++b) {
+      const unsigned long long m = __ballot((v >> (half + b)) & 1u);
+      const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      ex += below << (half + b);
+      wt += (uint32_t)__popcll(m) << (half + b);
+    }
+  }
+  if (lane == 0) scratch[wave] = wt;
+  __syncthreads();
+  uint32_t before = 0u, tot = 0u;
+#pragma unroll
+  for (int w = 0; w < SEL_WAVES; ++w) {
+    const uint32_t x = scratch[w];
+    before += w < wave ? x : 0u;
+    tot += x;
+  }
+  __syncthreads();
+  *total = tot;
+  return ex + before;
 }
 
 // Given hist[] filled for the current digit, find the digit d with
@@ -151,19 +191,93 @@ __global__ void __launch_bounds__(SEL_THREADS) select_kernel(const float* __rest
   uint32_t prefix = 0, pmask = 0, need = (uint32_t)c_eff;
   bool done = false;       // every key equal to the prefix is taken
   bool have_d0 = false;    // first digit resolved
+  bool collect = false;    // the candidate list holds every key matching the prefix
   if (tid == 0) n_cand = 0;
-  if (coarse != nullptr) {
-    const uint32_t* ch = coarse + (size_t)unit * NBINS;
-    for (int j = tid; j < NBINS; j += SEL_THREADS) hist[j] = ch[j];
-    __syncthreads();
-    done = pick_digit(hist, scratch, sh, 21, 0x7ffu, prefix, pmask, need);
-    have_d0 = true;
-  }
-  // Candidates of the boundary bin are collected while the keys are read,
-  // when the first digit is already known and they fit.
-  bool collect = have_d0 && !done && hist[prefix >> 21] <= (uint32_t)CAND_MAX;
 
-  if (resident) {
+  // Resident rows: issue every load of the row first (16-byte loads when the
+  // row is 16-byte aligned), so that the coarse pick below runs while they fly.
+  // (T_cap % 4 == 0 keeps the rounded-up float4 count inside every row.)
+  const bool vec4 = resident && (T_cap & 3) == 0 && (reinterpret_cast<uintptr_t>(row) & 15u) == 0u;
+  constexpr int V4 = KEYBUF / 4 / SEL_THREADS;  // float4 per thread for a full row
+  float4 rv[V4];
+  if (vec4) {
+    const float4* row4 = reinterpret_cast<const float4*>(row);
+    const int nf = (T + 3) / 4;  // 4 * nf <= T_cap
+#pragma unroll
+    for (int u = 0; u < V4; ++u) {
+      const int f = u * SEL_THREADS + tid;
+      rv[u] = f < nf ? row4[f] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+  }
+
+  if (coarse != nullptr) {
+    // First digit from the score launch's histogram, resolved by wave 0 alone:
+    // lane l sums bins [2048 - 32(l+1), 2048 - 32l); a wave scan of those sums
+    // (highest bins first) locates the lane whose range crosses `need`, which
+    // then walks its bins from the top.
+    if (tid < 64) {
+      const uint32_t* ch = coarse + (size_t)unit * NBINS + (NBINS - 32 * (tid + 1));
+      uint32_t bins[32];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint4 x = reinterpret_cast<const uint4*>(ch)[q];
+        bins[4 * q] = x.x;
+        bins[4 * q + 1] = x.y;
+        bins[4 * q + 2] = x.z;
+        bins[4 * q + 3] = x.w;
+      }
+      uint32_t lsum = 0u;
+#pragma unroll
+      for (int q = 0; q < 32; ++q) lsum += bins[q];
+      const uint32_t incl = wave_scan(lsum);
+      const uint32_t excl = incl - lsum;
+      if (excl < need && need <= incl) {
+        uint32_t acc = excl;
+        int d = 0;
+        uint32_t above = 0u, cnt = 0u;
+#pragma unroll
+        for (int q = 31; q >= 0; --q) {  // bins from the highest down
+          const uint32_t c = bins[q];
+          if (d == 0 && acc + c >= need) {
+            d = NBINS - 32 * (tid + 1) + q + 1;  // +1: 0 means "not found yet"
+            above = acc;
+            cnt = c;
+          }
+          acc += c;
+        }
+        sh[0] = (uint32_t)(d - 1);
+        sh[1] = above;
+        hist[0] = cnt;  // count of the boundary bin
+      }
+    }
+    __syncthreads();
+    const uint32_t d0 = sh[0];
+    need -= sh[1];
+    prefix = d0 << 21;
+    pmask = 0x7ffu << 21;
+    const uint32_t bin_count = hist[0];
+    done = bin_count == need;
+    have_d0 = true;
+    __syncthreads();
+    // A candidate list pays off only for rows that stay in global memory; a
+    // resident row is refined straight from registers / LDS.
+    collect = !resident && !done && bin_count <= (uint32_t)CAND_MAX;
+  }
+
+  if (vec4) {
+#pragma unroll
+    for (int u = 0; u < V4; ++u) {
+      const int i0 = 4 * (u * SEL_THREADS + tid);
+      const float vals[4] = {rv[u].x, rv[u].y, rv[u].z, rv[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = i0 + e;
+        const uint32_t key = order_key(vals[e]);
+        if (i < T) keys[padded(i)] = key;
+        if (collect) push_cand(cand, &n_cand, i < T && (key & pmask) == prefix, key);
+      }
+    }
+  } else if (resident) {
     for (int base = 0; base < T; base += SEL_THREADS * LOAD_BATCH) {
       float v[LOAD_BATCH];
 #pragma unroll
@@ -213,6 +327,17 @@ __global__ void __launch_bounds__(SEL_THREADS) select_kernel(const float* __rest
         const uint32_t key = cand[i];
         if ((key & pmask) == prefix) atomicAdd(&hist[(key >> s) & dm], 1u);
       }
+    } else if (vec4) {  // the row is still in registers
+#pragma unroll
+      for (int u = 0; u < V4; ++u) {
+        const int i0 = 4 * (u * SEL_THREADS + tid);
+        const float vals[4] = {rv[u].x, rv[u].y, rv[u].z, rv[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t key = order_key(vals[e]);
+          if (i0 + e < T && (key & pmask) == prefix) atomicAdd(&hist[(key >> s) & dm], 1u);
+        }
+      }
     } else if (resident) {
       for (int base = 0; base < T; base += SEL_THREADS * LOAD_BATCH) {
         uint32_t kv[LOAD_BATCH];
@@ -248,7 +373,7 @@ __global__ void __launch_bounds__(SEL_THREADS) select_kernel(const float* __rest
     if (pass == 0) {
       // Standalone call: the first digit was just found; the refinement can
       // still run on candidates, gathered by one more sweep.
-      collect = !done && hist[prefix >> 21] <= (uint32_t)CAND_MAX;
+      collect = !resident && !done && hist[prefix >> 21] <= (uint32_t)CAND_MAX;
       if (collect) {
         if (tid == 0) n_cand = 0;
         __syncthreads();
@@ -306,8 +431,7 @@ __global__ void __launch_bounds__(SEL_THREADS) select_kernel(const float* __rest
     const uint32_t gt = (uint32_t)__popc(gtm), eq = (uint32_t)__popc(eqm);
     // Counts per chunk are at most 32768, so both fit a 16-bit half.
     uint32_t tot;
-    const uint32_t incl = block_scan((gt << 16) | eq, scratch, &tot);
-    const uint32_t excl = incl - ((gt << 16) | eq);
+    const uint32_t excl = block_excl_small((gt << 16) | eq, scratch, &tot);
     const uint32_t gt_before = excl >> 16, eq_before = excl & 0xffffu;
     const uint32_t gt_tot = tot >> 16, eq_tot = tot & 0xffffu;
     // Keys equal to the prefix are taken in index order until `need` are taken:

@@ -173,6 +173,14 @@ def test_select_bit_exact_32k_rows(kind):
     _select_case(len(lens), 2, 32768, lens, 2048, seed=5, kind=kind)
 
 
+@pytest.mark.parametrize("T_cap", [4097, 4098, 4099, 4100])
+def test_select_bit_exact_any_row_stride(T_cap):
+    # Row strides that are not a multiple of 4 floats: only some rows are
+    # 16-byte aligned, and the last row ends at the end of the buffer.
+    lens = [T_cap, T_cap - 1, 3001, T_cap]
+    _select_case(len(lens), 3, T_cap, lens, 700, seed=T_cap, kind="quantized")
+
+
 @pytest.mark.parametrize("kind", ["normal", "quantized"])
 def test_select_bit_exact_rows_longer_than_lds(kind):
     lens = [131072, 70001, 32769, 8192]
