@@ -17,7 +17,8 @@
  *  - All tensor pointers are DEVICE pointers owned by the caller, dense and
  *    row-major in the layout given.  K, V, q_cur and q_hist must be 16-byte
  *    aligned (16-byte vector loads), every other array 4-byte aligned; a
- *    misaligned pointer is rejected with ASP_ERR_INVALID_ARG.
+ *    misaligned pointer is rejected with ASP_ERR_INVALID_ARG.  A workspace
+ *    must be 16-byte aligned, else ASP_ERR_WORKSPACE.
  *  - A "unit" is one (sequence b, KV head g); G = n_q_heads / n_kv_heads query
  *    heads h = g*G .. g*G+G-1 share KV head g.
  *  - The library allocates nothing, frees nothing, keeps no state between calls
@@ -137,7 +138,8 @@ asp_status asp_score_keys(const asp_dims* dims, const float* q_pred, const void*
  * idx[b][g][0..C_eff) in ascending index order, idx[b][g][C_eff..C) = -1, and
  * n_sel[b][g] = C_eff.  scores[B][Hkv][t_cap] fp32, idx[B][Hkv][C] int32,
  * n_sel[B][Hkv] int32.  ws/ws_bytes: asp_workspace_size(ASP_OP_SELECT) bytes
- * (NULL allowed when that is 0). */
+ * of device scratch (about 4.2 bytes per key slot plus 8 KiB per unit; its
+ * contents need no initialisation and are not kept between calls). */
 asp_status asp_select_topc(const asp_dims* dims, const asp_cfg* cfg, const float* scores, const int32_t* seq_lens,
                            int32_t* idx, int32_t* n_sel, void* ws, size_t ws_bytes, hipStream_t stream);
 

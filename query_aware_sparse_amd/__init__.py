@@ -215,6 +215,8 @@ def asp_select_topc(dims: Dims, cfg: Cfg, scores, seq_lens, idx, n_sel, ws=None,
     _check(seq_lens, "seq_lens", (B,), torch.int32)
     _check(idx, "idx", (B, Hkv, C), torch.int32)
     _check(n_sel, "n_sel", (B, Hkv), torch.int32)
+    if ws is None:  # scratch of the selection launches, sized by the library
+        ws = torch.empty(asp_workspace_size(dims, cfg, OP_SELECT), dtype=torch.uint8, device=scores.device)
     wp, wb = _ws(ws)
     _raise("asp_select_topc", load().asp_select_topc(ctypes.byref(dims), ctypes.byref(cfg), _ptr(scores),
                                                      _ptr(seq_lens), _ptr(idx), _ptr(n_sel), wp, wb,

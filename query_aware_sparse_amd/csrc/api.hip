@@ -61,23 +61,26 @@ asp_status check_all(const asp_dims* d, const asp_cfg* c, Shape* s) {
 }
 
 struct StepLayout {
-  size_t q_pred, scores, hist, partials, total;
+  size_t q_pred, scores, hist, select, partials, total;
 };
 
-// Workspace of asp_step: predicted queries, score rows and coarse histograms
-// (selection stream), attention partials (attention stream).
+// Workspace of asp_step: predicted queries, score rows, coarse histograms and
+// the selection's scratch (selection stream), attention partials (attention
+// stream).
 StepLayout step_layout(const Shape& s) {
   StepLayout l;
   l.q_pred = 0;
   l.scores = align_up(l.q_pred + (size_t)s.B * s.Hq * s.D * sizeof(float));
   l.hist = align_up(l.scores + (size_t)s.B * s.Hkv * s.T_cap * sizeof(float));
-  l.partials = align_up(l.hist + (size_t)s.B * s.Hkv * asp::HIST_BINS * sizeof(uint32_t));
+  l.select = align_up(l.hist + (size_t)s.B * s.Hkv * asp::HIST_BINS * sizeof(uint32_t));
+  l.partials = align_up(l.select + asp::select_ws_bytes(s, false));
   l.total = align_up(l.partials + asp::attend_partials_bytes(s));
   return l;
 }
 
 size_t ws_bytes_for(const Shape& s, asp_op op) {
   switch (op) {
+    case ASP_OP_SELECT: return align_up(asp::select_ws_bytes(s, true));
     case ASP_OP_DECODE: return align_up(asp::attend_partials_bytes(s));
     case ASP_OP_STEP: return step_layout(s).total;
     default: return 0;
@@ -95,15 +98,16 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
     if ((expr) != hipSuccess) return ASP_ERR_HIP;  \
   } while (0)
 
-// Selection work of one step: three launches.  The predictor pushes q_cur into
+// Selection work of one step: four launches.  The predictor pushes q_cur into
 // every head's ring slot and clears the coarse histograms; the score launch
-// fills the histograms; the select launch uses them and advances the ring.
+// fills the histograms; the two select launches use them, and the last one
+// advances the ring.
 asp_status run_selection(const Shape& s, const float* q_cur, float* q_hist, int32_t* newest, int32_t* len,
                          const void* k, const int32_t* seq_lens, int32_t* idx, int32_t* n_sel, float* q_pred,
-                         float* scores, uint32_t* hist, hipStream_t st) {
+                         float* scores, uint32_t* hist, void* sel_ws, hipStream_t st) {
   ASP_TRY_HIP(asp::launch_predict(s, q_hist, newest, len, q_cur, q_pred, hist, st));
   ASP_TRY_HIP(asp::launch_score(s, q_pred, k, seq_lens, scores, hist, st));
-  ASP_TRY_HIP(asp::launch_select(s, scores, hist, seq_lens, idx, n_sel, newest, len, st));
+  ASP_TRY_HIP(asp::launch_select(s, scores, hist, seq_lens, idx, n_sel, newest, len, sel_ws, st));
   return ASP_OK;
 }
 
@@ -168,8 +172,8 @@ asp_status asp_select_topc(const asp_dims* dims, const asp_cfg* cfg, const float
   if (!scores || !seq_lens || !idx || !n_sel) return ASP_ERR_INVALID_ARG;
   if (!aligned4(scores)) return ASP_ERR_INVALID_ARG;
   const size_t need = ws_bytes_for(s, ASP_OP_SELECT);
-  if (need > 0 && (ws == nullptr || ws_bytes < need)) return ASP_ERR_WORKSPACE;
-  return hip_status(asp::launch_select(s, scores, nullptr, seq_lens, idx, n_sel, nullptr, nullptr, stream));
+  if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return ASP_ERR_WORKSPACE;
+  return hip_status(asp::launch_select(s, scores, nullptr, seq_lens, idx, n_sel, nullptr, nullptr, ws, stream));
 }
 
 asp_status asp_sparse_decode(const asp_dims* dims, const asp_cfg* cfg, const float* q, const void* k, const void* v,
@@ -199,7 +203,7 @@ asp_status asp_step(const asp_dims* dims, const asp_cfg* cfg, const float* q_cur
   if ((idx_cur == nullptr) != (n_sel_cur == nullptr)) return ASP_ERR_INVALID_ARG;
   if (!aligned16(q_cur) || !aligned16(q_hist) || !aligned16(k) || !aligned16(v) || !aligned4(out))
     return ASP_ERR_INVALID_ARG;
-  if (!aligned4(ws)) return ASP_ERR_WORKSPACE;
+  if (!aligned16(ws)) return ASP_ERR_WORKSPACE;
   const bool pipelined = idx_cur != nullptr;
   const bool two_streams = pipelined && sel_stream != nullptr && sel_stream != attn_stream;
   if (two_streams && q_ready == nullptr) return ASP_ERR_INVALID_ARG;
@@ -209,11 +213,12 @@ asp_status asp_step(const asp_dims* dims, const asp_cfg* cfg, const float* q_cur
   float* q_pred = reinterpret_cast<float*>(base + lay.q_pred);
   float* scores = reinterpret_cast<float*>(base + lay.scores);
   uint32_t* hist = reinterpret_cast<uint32_t*>(base + lay.hist);
+  void* sel_ws = base + lay.select;
   void* partials = base + lay.partials;
 
   if (!pipelined) {
     st = run_selection(s, q_cur, q_hist, hist_newest, hist_len, k, seq_lens, idx_next, n_sel_next, q_pred, scores,
-                       hist, attn_stream);
+                       hist, sel_ws, attn_stream);
     if (st != ASP_OK) return st;
     ASP_TRY_HIP(asp::launch_attend(s, q_cur, k, v, idx_next, n_sel_next, out, partials, attn_stream));
     if (idx_next_ready) ASP_TRY_HIP(hipEventRecord(idx_next_ready, attn_stream));
@@ -222,7 +227,7 @@ asp_status asp_step(const asp_dims* dims, const asp_cfg* cfg, const float* q_cur
   if (!two_streams) {
     ASP_TRY_HIP(asp::launch_attend(s, q_cur, k, v, idx_cur, n_sel_cur, out, partials, attn_stream));
     st = run_selection(s, q_cur, q_hist, hist_newest, hist_len, k, seq_lens, idx_next, n_sel_next, q_pred, scores,
-                       hist, attn_stream);
+                       hist, sel_ws, attn_stream);
     if (st != ASP_OK) return st;
     if (idx_next_ready) ASP_TRY_HIP(hipEventRecord(idx_next_ready, attn_stream));
     return ASP_OK;
@@ -234,7 +239,7 @@ asp_status asp_step(const asp_dims* dims, const asp_cfg* cfg, const float* q_cur
   if (idx_cur_ready) ASP_TRY_HIP(hipStreamWaitEvent(attn_stream, idx_cur_ready, 0));
   ASP_TRY_HIP(asp::launch_attend(s, q_cur, k, v, idx_cur, n_sel_cur, out, partials, attn_stream));
   st = run_selection(s, q_cur, q_hist, hist_newest, hist_len, k, seq_lens, idx_next, n_sel_next, q_pred, scores,
-                     hist, sel_stream);
+                     hist, sel_ws, sel_stream);
   if (st != ASP_OK) return st;
   if (idx_next_ready) ASP_TRY_HIP(hipEventRecord(idx_next_ready, sel_stream));
   return ASP_OK;

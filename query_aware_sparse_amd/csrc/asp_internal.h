@@ -36,9 +36,12 @@ hipError_t launch_predict(const Shape& s, float* q_hist, const int32_t* newest, 
 hipError_t launch_score(const Shape& s, const float* q_pred, const void* k, const int32_t* seq_lens,
                         float* scores, uint32_t* hist, hipStream_t st);
 // Top-C selection; hist (nullable) is the coarse histogram built by the score
-// launch.  adv_newest/adv_len (nullable) advance the query ring by one slot.
+// launch (when null, one is built in ws first).  adv_newest/adv_len (nullable)
+// advance the query ring by one slot.  ws: select_ws_bytes(s, hist == nullptr).
+size_t select_ws_bytes(const Shape& s, bool with_hist);
 hipError_t launch_select(const Shape& s, const float* scores, const uint32_t* hist, const int32_t* seq_lens,
-                         int32_t* idx, int32_t* n_sel, int32_t* adv_newest, int32_t* adv_len, hipStream_t st);
+                         int32_t* idx, int32_t* n_sel, int32_t* adv_newest, int32_t* adv_len, void* ws,
+                         hipStream_t st);
 hipError_t launch_attend(const Shape& s, const float* q, const void* k, const void* v, const int32_t* idx,
                          const int32_t* n_sel, float* out, void* partials, hipStream_t st);
 

@@ -54,6 +54,9 @@ def test_workspace_sizes(lib):
     d, c = _dims(), A.Cfg(16, 2048, 1e-2)
     assert A.asp_workspace_size(d, c, A.OP_PUSH) == 0
     assert A.asp_workspace_size(d, c, A.OP_SCORE) == 0
+    sel = A.asp_workspace_size(d, c, A.OP_SELECT)
+    # coarse histograms, per-region candidate lists, counts and bitmaps
+    assert sel % 256 == 0 and sel >= 8 * 8 * (2048 * 4 + 32768 * 4 + 32768 // 8)
     dec = A.asp_workspace_size(d, c, A.OP_DECODE)
     step = A.asp_workspace_size(d, c, A.OP_STEP)
     assert dec > 0 and dec % 256 == 0
@@ -109,6 +112,9 @@ def test_null_pointers_and_short_workspace_rejected(lib):
     assert _call_decode(lib, d, c, ctypes.c_void_p(256), 1 << 30, null_out=True) == 1
     need = A.asp_workspace_size(d, c, A.OP_DECODE)
     assert _call_decode(lib, d, c, None, 0) == 3
+    need_sel = A.asp_workspace_size(d, c, A.OP_SELECT)
+    assert _call_select(lib, d, c, None, 0) == 3
+    assert _call_select(lib, d, c, ctypes.c_void_p(256), need_sel - 1) == 3
     assert _call_decode(lib, d, c, ctypes.c_void_p(256), need - 1) == 3
     assert lib.asp_score_keys(None, None, None, None, None, None) == 1
     one = ctypes.c_void_p(16)
