@@ -226,22 +226,29 @@ asp_status asp_step(const asp_dims* dims, const asp_cfg* cfg, const float* q_cur
   }
   if (!two_streams) {
     ASP_TRY_HIP(asp::launch_attend(s, q_cur, k, v, idx_cur, n_sel_cur, out, partials, attn_stream));
-    st = run_selection(s, q_cur, q_hist, hist_newest, hist_len, k, seq_lens, idx_next, n_sel_next, q_pred, scores,
-                       hist, sel_ws, attn_stream);
-    if (st != ASP_OK) return st;
-    if (idx_next_ready) ASP_TRY_HIP(hipEventRecord(idx_next_ready, attn_stream));
+    ASP_TRY_HIP(asp::launch_predict(s, q_hist, hist_newest, hist_len, q_cur, q_pred, hist, attn_stream));
+    ASP_TRY_HIP(asp::launch_score(s, q_pred, k, seq_lens, scores, hist, attn_stream));
+    ASP_TRY_HIP(asp::launch_select(s, scores, hist, seq_lens, idx_next, n_sel_next, hist_newest, hist_len, sel_ws,
+                                   attn_stream, idx_next_ready));
     return ASP_OK;
   }
-  // Two streams: the selection stream starts once q_cur exists and the previous
-  // step's attention (which read the buffer idx_next now overwrites) is done.
+  // Two streams.  The selection stream starts once q_cur exists (q_ready, as
+  // recorded on the attention stream) and the previous step's attention, which
+  // read the buffer idx_next now overwrites, is done.  q_ready is then
+  // re-recorded by the predictor launch, and the attention stream waits for it
+  // as well: the attention (which needs none of the predictor's output) thus
+  // shares the GPU with the HBM-bound score pass rather than with the
+  // latency-bound predictor.  idx_next_ready is recorded by the last select
+  // launch.  Events recorded by a launch itself cost no extra queue packet.
   ASP_TRY_HIP(hipEventRecord(q_ready, attn_stream));
   ASP_TRY_HIP(hipStreamWaitEvent(sel_stream, q_ready, 0));
+  ASP_TRY_HIP(asp::launch_predict(s, q_hist, hist_newest, hist_len, q_cur, q_pred, hist, sel_stream, q_ready));
   if (idx_cur_ready) ASP_TRY_HIP(hipStreamWaitEvent(attn_stream, idx_cur_ready, 0));
+  ASP_TRY_HIP(hipStreamWaitEvent(attn_stream, q_ready, 0));
   ASP_TRY_HIP(asp::launch_attend(s, q_cur, k, v, idx_cur, n_sel_cur, out, partials, attn_stream));
-  st = run_selection(s, q_cur, q_hist, hist_newest, hist_len, k, seq_lens, idx_next, n_sel_next, q_pred, scores,
-                     hist, sel_ws, sel_stream);
-  if (st != ASP_OK) return st;
-  if (idx_next_ready) ASP_TRY_HIP(hipEventRecord(idx_next_ready, sel_stream));
+  ASP_TRY_HIP(asp::launch_score(s, q_pred, k, seq_lens, scores, hist, sel_stream));
+  ASP_TRY_HIP(asp::launch_select(s, scores, hist, seq_lens, idx_next, n_sel_next, hist_newest, hist_len, sel_ws,
+                                 sel_stream, idx_next_ready));
   return ASP_OK;
 }
 

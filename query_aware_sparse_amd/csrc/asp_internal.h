@@ -29,8 +29,10 @@ hipError_t launch_push(const Shape& s, const float* q_cur, float* q_hist, int32_
 // next ring slot, but leaves newest/len unchanged: the select launch of the
 // same step advances them (it runs after every predictor workgroup has read
 // them).  hist_zero, when not null, is cleared ([B*Hkv][HIST_BINS]).
+// `done` (nullable) is recorded when the launch completes.
 hipError_t launch_predict(const Shape& s, float* q_hist, const int32_t* newest, const int32_t* len,
-                          const float* q_cur, float* q_pred, uint32_t* hist_zero, hipStream_t st);
+                          const float* q_cur, float* q_pred, uint32_t* hist_zero, hipStream_t st,
+                          hipEvent_t done = nullptr);
 // Scores; hist (nullable) accumulates the coarse histogram of every unit and
 // must be zero on entry.
 hipError_t launch_score(const Shape& s, const float* q_pred, const void* k, const int32_t* seq_lens,
@@ -41,9 +43,12 @@ hipError_t launch_score(const Shape& s, const float* q_pred, const void* k, cons
 size_t select_ws_bytes(const Shape& s, bool with_hist);
 hipError_t launch_select(const Shape& s, const float* scores, const uint32_t* hist, const int32_t* seq_lens,
                          int32_t* idx, int32_t* n_sel, int32_t* adv_newest, int32_t* adv_len, void* ws,
-                         hipStream_t st);
+                         hipStream_t st, hipEvent_t done = nullptr);
+// Sparse attention: split-K partials into `partials`, then the merge into out.
 hipError_t launch_attend(const Shape& s, const float* q, const void* k, const void* v, const int32_t* idx,
                          const int32_t* n_sel, float* out, void* partials, hipStream_t st);
+// The merge alone (partials written by the attention blocks).
+hipError_t launch_merge(const Shape& s, const int32_t* n_sel, float* out, const void* partials, hipStream_t st);
 
 // ---------------------------------------------------------------- device helpers
 

@@ -1,25 +1,8 @@
-// Sparse decode attention over the selected tokens, split-K with an fp32
-// softmax and a log-sum-exp merge.
-//
-// Sources: reproduction card, "Layout" (full versus top-C sparse attention) and
-// "Key finding" (the method attends to the C selected tokens only); research-map
-// summary of AsyncSpade, "Approach" (the selection is consumed by the inference
-// step).  Reading taken: the attention query is the actual current query, the
-// prediction only chooses the tokens.
-//
-// Grid: (split, unit).  A workgroup of 4 wavefronts gathers up to
-// 4 * 8 * KPW selected K and V rows of one unit (each row read once and used by
-// all G query heads of the group), computes the G x tokens logits, the block
-// softmax statistics (max in the log2 domain, sum) and the weighted V sum, and
-// writes one partial (acc[G][D], m[G], l[G]).  The merge kernel combines the
-// partials of each (sequence, query head).
-#include "asp_internal.h"
+// Launches of the sparse attention and its merge; the attention block body is
+// in attend_block.h.
+#include "attend_block.h"
 
 namespace asp {
-
-constexpr int ATT_THREADS = 256;
-constexpr int ATT_WAVES = ATT_THREADS / 64;
-constexpr int ATT_NL = 8;  // row loads in flight per lane for K and for V
 
 int attend_tokens_per_block(int D, int kv) {
   const int row_bytes = D * (kv == 0 ? 2 : 4);
@@ -37,19 +20,6 @@ size_t attend_partials_bytes(const Shape& s) {
   return units * attend_num_splits(s) * s.G * (s.D + 2) * sizeof(float);
 }
 
-template <typename KV>
-__device__ __forceinline__ void unpack_row16(const uint4& r, float* x) {
-  if constexpr (sizeof(KV) == 2) {
-    x[0] = bf16_lo(r.x); x[1] = bf16_hi(r.x);
-    x[2] = bf16_lo(r.y); x[3] = bf16_hi(r.y);
-    x[4] = bf16_lo(r.z); x[5] = bf16_hi(r.z);
-    x[6] = bf16_lo(r.w); x[7] = bf16_hi(r.w);
-  } else {
-    x[0] = __uint_as_float(r.x); x[1] = __uint_as_float(r.y);
-    x[2] = __uint_as_float(r.z); x[3] = __uint_as_float(r.w);
-  }
-}
-
 template <typename KV, int D, int G>
 __global__ void __launch_bounds__(ATT_THREADS) attend_kernel(const float* __restrict__ q, const KV* __restrict__ k,
                                                              const KV* __restrict__ v,
@@ -58,143 +28,9 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_kernel(const float* __rest
                                                              float* __restrict__ part_acc,
                                                              float* __restrict__ part_ml, int Hq, int Hkv, int T_cap,
                                                              int C, int nsplit) {
-  constexpr int EPL = 16 / (int)sizeof(KV);
-  constexpr int LPK = D / EPL;
-  constexpr int KPW = 64 / LPK;
-  constexpr int TPW = ATT_NL * KPW;
-  constexpr int TPB = ATT_WAVES * TPW;
-  __shared__ float sm_m[ATT_WAVES][G];
-  __shared__ float sm_l[ATT_WAVES][G];
-  __shared__ float sm_acc[ATT_WAVES][G][D];
-
-  const int split = blockIdx.x, unit = blockIdx.y;
-  const int b = unit / Hkv, g = unit % Hkv;
-  const int n = clampi(n_sel[unit], 0, C);
-  const int tok0 = split * TPB;
-  if (tok0 >= n) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int sub = lane % LPK, kl = lane / LPK;
-
-  // Query slice, pre-scaled so that exp2 of a logit difference is the softmax
-  // weight: log2(e) / sqrt(D).
-  const float scale = 1.4426950408889634f / sqrtf((float)D);
-  float qr[G][EPL];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float* qh = q + ((size_t)b * Hq + (size_t)g * G + h) * D + sub * EPL;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) qr[h][e] = qh[e] * scale;
-  }
-
-  const int32_t* ib = idx + (size_t)unit * C;
-  int tk[ATT_NL];
-  bool ok[ATT_NL];
-#pragma unroll
-  for (int i = 0; i < ATT_NL; ++i) {
-    const int t = tok0 + wave * TPW + i * KPW + kl;
-    const int id = t < n ? ib[t] : -1;
-    ok[i] = id >= 0 && id < T_cap;
-    tk[i] = ok[i] ? id : 0;
-  }
-  const KV* kb = k + (size_t)unit * T_cap * D + sub * EPL;
-  const KV* vb = v + (size_t)unit * T_cap * D + sub * EPL;
-  uint4 kr[ATT_NL], vr[ATT_NL];
-#pragma unroll
-  for (int i = 0; i < ATT_NL; ++i)
-    kr[i] = ok[i] ? *reinterpret_cast<const uint4*>(kb + (size_t)tk[i] * D) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-  for (int i = 0; i < ATT_NL; ++i)
-    vr[i] = ok[i] ? *reinterpret_cast<const uint4*>(vb + (size_t)tk[i] * D) : make_uint4(0, 0, 0, 0);
-
-  // Logits (log2 domain); every lane of a key's lane group holds the same value.
-  float lg[G][ATT_NL];
-#pragma unroll
-  for (int i = 0; i < ATT_NL; ++i) {
-    float x[EPL];
-    unpack_row16<KV>(kr[i], x);
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float acc = 0.0f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc = fmaf(qr[h][e], x[e], acc);
-      acc = group_sum<LPK>(acc);
-      lg[h][i] = ok[i] ? acc : -INFINITY;
-    }
-  }
-  // Block maximum per head.
-  float m[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float x = lg[h][0];
-#pragma unroll
-    for (int i = 1; i < ATT_NL; ++i) x = fmaxf(x, lg[h][i]);
-    x = group_max<64>(x);
-    if (lane == 0) sm_m[wave][h] = x;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float x = sm_m[0][h];
-#pragma unroll
-    for (int w = 1; w < ATT_WAVES; ++w) x = fmaxf(x, sm_m[w][h]);
-    m[h] = x;
-  }
-  // Weights, their sum and the weighted V rows.
-  float acc[G][EPL];
-  float l[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    l[h] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.0f;
-  }
-#pragma unroll
-  for (int i = 0; i < ATT_NL; ++i) {
-    float x[EPL];
-    unpack_row16<KV>(vr[i], x);
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float p = ok[i] ? exp2f(lg[h][i] - m[h]) : 0.0f;
-      l[h] += p;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, x[e], acc[h][e]);
-    }
-  }
-  // Reduce over the key lane groups of the wave (lanes with the same `sub`).
-#pragma unroll
-  for (int off = LPK; off < 64; off <<= 1) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      l[h] += __shfl_xor(l[h], off);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], off);
-    }
-  }
-  if (kl == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) sm_acc[wave][h][sub * EPL + e] = acc[h][e];
-      if (sub == 0) sm_l[wave][h] = l[h];
-    }
-  }
-  __syncthreads();
-  const size_t pbase = ((size_t)unit * nsplit + split) * G;
-  for (int e = threadIdx.x; e < G * D; e += ATT_THREADS) {
-    const int h = e / D, d = e % D;
-    float s = 0.0f;
-#pragma unroll
-    for (int w = 0; w < ATT_WAVES; ++w) s += sm_acc[w][h][d];
-    part_acc[(pbase + h) * D + d] = s;
-  }
-  if (threadIdx.x < G) {
-    const int h = threadIdx.x;
-    float s = 0.0f;
-#pragma unroll
-    for (int w = 0; w < ATT_WAVES; ++w) s += sm_l[w][h];
-    part_ml[(pbase + h) * 2 + 0] = m[h];
-    part_ml[(pbase + h) * 2 + 1] = s;
-  }
+  __shared__ __align__(16) unsigned char smem[attend_lds_bytes<D, G>()];
+  attend_block<KV, D, G>(q, k, v, idx, n_sel, part_acc, part_ml, Hq, Hkv, T_cap, C, nsplit, blockIdx.x, blockIdx.y,
+                         smem);
 }
 
 // One workgroup per (sequence, query head): log-sum-exp merge of the partials.
@@ -292,6 +128,14 @@ hipError_t launch_attend(const Shape& s, const float* q, const void* k, const vo
     e = s.D == 64 ? launch_attend_d<float, 64>(s, q, k, v, idx, n_sel, part_acc, part_ml, st)
                   : launch_attend_d<float, 128>(s, q, k, v, idx, n_sel, part_acc, part_ml, st);
   if (e != hipSuccess) return e;
+  return launch_merge(s, n_sel, out, partials, st);
+}
+
+hipError_t launch_merge(const Shape& s, const int32_t* n_sel, float* out, const void* partials, hipStream_t st) {
+  if (s.B == 0) return hipSuccess;
+  const int nsplit = attend_num_splits(s);
+  const float* part_acc = static_cast<const float*>(partials);
+  const float* part_ml = part_acc + (size_t)s.B * s.Hkv * nsplit * s.G * s.D;
   hipLaunchKernelGGL(merge_kernel, dim3(s.B * s.Hq), dim3(128), 0, st, part_acc, part_ml, n_sel, out, s.Hq, s.Hkv,
                      s.G, s.D, s.C, nsplit, attend_tokens_per_block(s.D, s.kv));
   return hipGetLastError();

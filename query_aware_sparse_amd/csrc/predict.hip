@@ -22,6 +22,8 @@
 //  4. the back substitutions of all windows run side by side, then each
 //     window's softmax runs across lanes, and the window predictions are
 //     pooled as one weighted sum of the lags.
+#include <hip/hip_ext.h>
+
 #include "asp_internal.h"
 
 namespace asp {
@@ -357,13 +359,14 @@ __global__ void __launch_bounds__(PRED_THREADS) predict_kernel(float* __restrict
 }
 
 hipError_t launch_predict(const Shape& s, float* q_hist, const int32_t* newest, const int32_t* len,
-                          const float* q_cur, float* q_pred, uint32_t* hist_zero, hipStream_t st) {
-  if (s.B == 0) return hipSuccess;
+                          const float* q_cur, float* q_pred, uint32_t* hist_zero, hipStream_t st, hipEvent_t done) {
+  if (s.B == 0) return done ? hipEventRecord(done, st) : hipSuccess;
   const dim3 grid(s.B * s.Hq), block(PRED_THREADS);
   const int P = s.W - 1;
-#define ASP_PRED_LAUNCH(PB)                                                                                      \
-  hipLaunchKernelGGL(predict_kernel<PB>, grid, block, 0, st, q_hist, newest, len, q_cur, q_pred, hist_zero, s.Hq, \
-                     s.Hkv, s.W, s.D, s.lambda)
+  // `done`, when given, is recorded by the launch itself (no separate marker).
+#define ASP_PRED_LAUNCH(PB)                                                                                         \
+  hipExtLaunchKernelGGL(predict_kernel<PB>, grid, block, 0, st, nullptr, done, 0, q_hist, newest, len, q_cur, q_pred, \
+                        hist_zero, s.Hq, s.Hkv, s.W, s.D, s.lambda)
   if (P <= 3) ASP_PRED_LAUNCH(3);
   else if (P <= 7) ASP_PRED_LAUNCH(7);
   else if (P <= 15) ASP_PRED_LAUNCH(15);

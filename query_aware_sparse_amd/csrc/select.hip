@@ -21,6 +21,8 @@
 //    two radix digits over them alone, marks the chosen candidates in the
 //    bitmap and compacts the bitmap in index order: every output position is
 //    a prefix count of set bits.
+#include <hip/hip_ext.h>
+
 #include "asp_internal.h"
 
 namespace asp {
@@ -405,8 +407,8 @@ __global__ void __launch_bounds__(SEL_THREADS) select_finish_kernel(const int32_
 
 hipError_t launch_select(const Shape& s, const float* scores, const uint32_t* hist, const int32_t* seq_lens,
                          int32_t* idx, int32_t* n_sel, int32_t* adv_newest, int32_t* adv_len, void* ws,
-                         hipStream_t st) {
-  if (s.B == 0) return hipSuccess;
+                         hipStream_t st, hipEvent_t done) {
+  if (s.B == 0) return done ? hipEventRecord(done, st) : hipSuccess;
   const int units = s.B * s.Hkv, nr = select_regions(s.T_cap);
   SelectWs w = carve(s, ws, hist == nullptr);
   if (hist == nullptr) {
@@ -417,8 +419,9 @@ hipError_t launch_select(const Shape& s, const float* scores, const uint32_t* hi
   const int segs = (s.T_cap + SEG - 1) / SEG;
   hipLaunchKernelGGL(select_classify_kernel, dim3(segs, units), dim3(SEL_THREADS), 0, st, scores, hist, seq_lens, w,
                      s.Hkv, s.T_cap, s.C, nr);
-  hipLaunchKernelGGL(select_finish_kernel, dim3(units), dim3(SEL_THREADS), 0, st, seq_lens, w, idx, n_sel, adv_newest,
-                     adv_len, s.Hkv, s.T_cap, s.C, s.W > 0 ? s.W : 1, nr);
+  // `done`, when given, is recorded by the finish launch itself (no separate marker).
+  hipExtLaunchKernelGGL(select_finish_kernel, dim3(units), dim3(SEL_THREADS), 0, st, nullptr, done, 0, seq_lens, w, idx,
+                        n_sel, adv_newest, adv_len, s.Hkv, s.T_cap, s.C, s.W > 0 ? s.W : 1, nr);
   return hipGetLastError();
 }
 
