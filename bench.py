@@ -121,7 +121,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--mode", choices=["two_streams", "one_stream"], default="one_stream")
+    ap.add_argument("--mode", choices=["two_streams", "one_stream"], default="two_streams")
     ap.add_argument("--kv-buffers", type=int, default=4)
     ap.add_argument("--kernel-launches", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -1,5 +1,4 @@
-// Score blocks (device functions), shared by the score launch and the fused
-// score + attention launch of a single-stream decode step.
+// Score blocks (device functions) of the score launch.
 // Token-level key scoring: score[b][g][i] = max over the G query heads of
 // KV head g of q_pred[b][h] . K[b][g][i].
 //
@@ -18,10 +17,13 @@
 // v_mfma_f32_16x16x32_bf16 per 32 coordinates, with the keys as the B operand
 // (lane l: key l%16, coordinates 8*(l/16)..+7 of each 32-wide step) and the
 // query heads as rows of the A operand.  Keys arrive with fully coalesced
-// non-temporal 16-byte loads (each wave-wide load covers whole key rows) and
-// are transposed into the MFMA layout through a per-wave, XOR-swizzled LDS
-// tile: loading 64-byte column slices of 16 rows straight into the operand
-// layout costs ~15% of the bandwidth on this part.  The
+// non-temporal 16-byte loads (each wave-wide load covers whole key rows; four
+// 16-key tiles in flight per wave) and are transposed into the MFMA layout
+// through two per-wave, XOR-swizzled LDS slots: loading 64-byte column slices
+// of 16 rows straight into the operand layout costs ~15% of the bandwidth on
+// this part.  Two slots instead of one per tile in flight keep the block at
+// 40 KiB of LDS, so four blocks (16 waves) share a CU; blocks of 512 keys keep
+// the tail of the launch short.  The
 // predicted query is fp32; it enters as two bf16 terms, hi = rne(q) and
 // lo = rne(q - hi), so the product keeps ~17 significant bits of q (relative
 // error <= 2^-18 per term) and accumulates in fp32.
@@ -38,7 +40,7 @@ namespace asp {
 
 constexpr int SCORE_THREADS = 256;
 constexpr int SCORE_WAVES = SCORE_THREADS / 64;
-constexpr int SCORE_KEYS_PER_BLOCK = 2048;
+constexpr int SCORE_KEYS_PER_BLOCK = 512;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -49,12 +51,13 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-constexpr int SCORE_MFMA_U = 4;  // 16-key tiles per wave and iteration
+constexpr int SCORE_MFMA_U = 4;     // 16-key tiles loaded per wave and iteration
+constexpr int SCORE_MFMA_SLOTS = 2;  // LDS transpose slots per wave (double buffer)
 
-// LDS of one bf16 score block: the per-wave transpose tiles, then the histogram.
+// LDS of one bf16 score block: the per-wave transpose slots, then the histogram.
 template <int D, bool HIST>
 constexpr size_t score_mfma_lds_bytes() {
-  return (size_t)SCORE_WAVES * SCORE_MFMA_U * 16 * (D * 2 / 16) * 16 + (HIST ? HIST_BINS * 4 : 0);
+  return (size_t)SCORE_WAVES * SCORE_MFMA_SLOTS * 16 * (D * 2 / 16) * 16 + (HIST ? HIST_BINS * 4 : 0);
 }
 
 // Score block (bx, unit) for bf16 keys; smem holds score_mfma_lds_bytes<D, HIST>().
@@ -68,8 +71,9 @@ __device__ __forceinline__ void score_mfma_block(const float* __restrict__ q_pre
   constexpr int RPI = 64 / CH;       // key rows per wave-wide load
   constexpr int NI = 16 / RPI;       // loads per 16-key tile
   constexpr int U = SCORE_MFMA_U;
-  u32x4 (*tile)[U][16][CH] = reinterpret_cast<u32x4 (*)[U][16][CH]>(smem);
-  uint32_t* lhist = reinterpret_cast<uint32_t*>(smem + (size_t)SCORE_WAVES * U * 16 * CH * 16);
+  constexpr int TB = SCORE_MFMA_SLOTS;
+  u32x4 (*tile)[TB][16][CH] = reinterpret_cast<u32x4 (*)[TB][16][CH]>(smem);
+  uint32_t* lhist = reinterpret_cast<uint32_t*>(smem + (size_t)SCORE_WAVES * TB * 16 * CH * 16);
 
   const int b = unit / Hkv, g = unit % Hkv;
   const int T = clampi(seq_lens[b], 0, T_cap);
@@ -121,26 +125,28 @@ __device__ __forceinline__ void score_mfma_block(const float* __restrict__ q_pre
         gld[u][i] = key < k1 ? __builtin_nontemporal_load(kb + (size_t)key * CH + lchunk) : u32x4{0u, 0u, 0u, 0u};
       }
     }
-    // Transpose through LDS: chunk q of tile row r is stored at q ^ (r % CH),
-    // which keeps both the row-wise writes and the column-wise reads spread
-    // over all banks.
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
+    // Transpose through LDS, one 16-key tile at a time through two slots:
+    // tile u+1 is written while the MFMAs read tile u.  Chunk q of tile row r
+    // is stored at q ^ (r % CH), which keeps both the row-wise writes and the
+    // column-wise reads spread over all banks.
+    auto put = [&](int u) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int r = RPI * i + lrow;
-        tile[wave][u][r][lchunk ^ (r % CH)] = gld[u][i];
+        tile[wave][u % TB][r][lchunk ^ (r % CH)] = gld[u][i];
       }
-    }
+    };
+    put(0);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      if (u + 1 < U) put(u + 1);
       f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        const bf16x8 bk = __builtin_bit_cast(bf16x8, tile[wave][u][j][(4 * s + c) ^ (j % CH)]);
+        const bf16x8 bk = __builtin_bit_cast(bf16x8, tile[wave][u % TB][j][(4 * s + c) ^ (j % CH)]);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[s], bk, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[s], bk, acc, 0, 0, 0);
       }
@@ -154,11 +160,11 @@ __device__ __forceinline__ void score_mfma_block(const float* __restrict__ q_pre
         sb[key] = m;
         if constexpr (HIST) atomicAdd(&lhist[order_key(m) >> HIST_SHIFT], 1u);
       }
+      // Slot u % TB is written again two tiles later (or next iteration).
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    // The next iteration overwrites this wave's tile.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
   if constexpr (HIST) {
     __syncthreads();
