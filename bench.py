@@ -58,20 +58,28 @@ def score_kernel_bytes(wl, seq_lens) -> int:
     return sum(Hkv * (T * D * 2 + T * 4 + G * D * 4) for T in seq_lens)
 
 
-def file_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+SCORE_SOURCES = [os.path.join(ROOT, "query_aware_sparse_amd", "csrc", f)
+                 for f in ("score.hip", "score_block.h", "asp_internal.h")]
 
 
-def measured_traffic(kernel_src: str):
+def sources_hash(paths) -> str:
+    """First 16 hex digits of the SHA-256 of the files' bytes, concatenated in order."""
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_sources):
     """HBM traffic of the score kernel from the committed rocprofv3 counter
-    summary, or None when the kernel source changed since it was taken."""
+    summary, or None when the kernel sources changed since it was taken."""
     path = os.path.join(ROOT, "profiles", "score_keys_qwen3-8b-layer_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_sha256_16") != file_hash(kernel_src):
+    if rec.get("source_sha256_16") != sources_hash(kernel_sources):
         return None
     return rec.get("bytes_per_launch")
 
@@ -250,7 +258,7 @@ def main() -> int:
     }
     sk_bytes = score_kernel_bytes(wl, lens_list)
     achieved = sk_bytes / (kern["score_us"] * 1e-6) / 1e9
-    traffic = measured_traffic(os.path.join(ROOT, "query_aware_sparse_amd", "csrc", "score.hip"))
+    traffic = measured_traffic(SCORE_SOURCES)
     roofline = {"kernel": "score_keys", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "algorithmic_bytes_per_launch": sk_bytes, "avg_launch_us": round(kern["score_us"], 2)}
