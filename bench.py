@@ -116,12 +116,12 @@ def cpu_baseline(wl, layer, q_t) -> dict:
         one_step()
         reps += 1
         el = time.perf_counter() - t0
-        if reps >= 3 or el > 20.0:
+        if (reps >= 3 and el >= 10.0) or el > 30.0:  # a bounded sample of ~10 s of CPU work
             break
     per_step = el / reps
     return {"value": 1.0 / per_step, "unit": "steps/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "full step of one layer (all %d units), %d timed repetitions after 1 warm-up, %.2f s each"
-                      % (wl.batch * wl.n_kv_heads, reps, per_step)}
+            "sample": "full step of one layer (all %d units), %d timed repetitions (%.1f s) after 1 warm-up, "
+                      "%.3f s each" % (wl.batch * wl.n_kv_heads, reps, el, per_step)}
 
 
 def main() -> int:
