@@ -165,7 +165,9 @@ def main() -> int:
     n_layer_steps = (args.warmup + args.steps) // L + 2
     attn = torch.cuda.Stream()
     sel = torch.cuda.Stream() if args.mode == "two_streams" else None
-    ws = torch.empty(A.asp_workspace_size(dims, cfg, A.OP_STEP), dtype=torch.uint8, device=dev)
+    # one step workspace per layer, as a decode loop over layers keeps them
+    ws_step = [torch.empty(A.asp_workspace_size(dims, cfg, A.OP_STEP), dtype=torch.uint8, device=dev)
+               for _ in range(L)]
     ws_dec = torch.empty(A.asp_workspace_size(dims, cfg, A.OP_DECODE), dtype=torch.uint8, device=dev)
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
     q_ready = A.HipEvent()
@@ -185,7 +187,7 @@ def main() -> int:
             A.asp_push_query(dims, cfg, qs[t], q_hist, newest, length)
         # bootstrap step: selection made from the ring, attended at once
         A.asp_step(dims, cfg, qs[wl.history_steps - 1], q_hist, newest, length, k, v, lens, None, None,
-                   lay["idx"][0], lay["nsel"][0], out, ws, idx_next_ready=lay["ev"][0])
+                   lay["idx"][0], lay["nsel"][0], out, ws_step[l], idx_next_ready=lay["ev"][0])
         layers.append(lay)
     torch.cuda.synchronize()
     log("setup: %d KV caches of %.2f GiB (K+V) in %.1f s" % (L, 2 * k.numel() * 2 / 2**30, time.perf_counter() - t0))
@@ -196,7 +198,7 @@ def main() -> int:
         nxt = 1 - cur
         q = lay["qs"][lay["t"]]
         A.asp_step(dims, cfg, q, lay["q_hist"], lay["newest"], lay["length"], lay["k"], lay["v"], lay["seq_lens"],
-                   lay["idx"][cur], lay["nsel"][cur], lay["idx"][nxt], lay["nsel"][nxt], out, ws,
+                   lay["idx"][cur], lay["nsel"][cur], lay["idx"][nxt], lay["nsel"][nxt], out, ws_step[i % L],
                    attn_stream=attn, sel_stream=sel, q_ready=q_ready, idx_cur_ready=lay["ev"][cur],
                    idx_next_ready=lay["ev"][nxt])
         lay["cur"] = nxt

@@ -169,18 +169,18 @@ asp_status asp_sparse_decode(const asp_dims* dims, const asp_cfg* cfg, const flo
  *    attn_stream (attention first); q_ready and idx_cur_ready are ignored (may
  *    be NULL); idx_next_ready, when not NULL, is recorded when the selection
  *    is written.
- *  - otherwise: q_ready is recorded on attn_stream (after whatever produced
- *    q_cur) and sel_stream waits for it; then q_ready is recorded again when
- *    the predictor launch on sel_stream completes, and attn_stream waits for
- *    that record (and for idx_cur_ready when it is not NULL) before the
- *    attention: the attention needs nothing from the predictor, but starting
- *    it then lets it overlap the HBM-bound scoring instead of slowing the
- *    latency-bound predictor.  The selection work runs on sel_stream;
- *    idx_next_ready is recorded on sel_stream when the selection is written
- *    (when not NULL).  q_ready must be a valid event.  The caller swaps
- *    idx/n_sel buffers and events between steps; because sel_stream waits for
- *    q_ready, the selection of step t never overwrites the buffer that step
- *    t-1's attention read.
+ *  - otherwise (two streams): attn_stream waits for idx_cur_ready, the event
+ *    recorded when the selection idx_cur was written (the idx_next_ready of
+ *    the step that made it, which must also be the last step that used this
+ *    workspace: in a decode loop each layer keeps its own workspace, idx/n_sel
+ *    buffer pair and event pair).  Then, on attn_stream: the ring push and the
+ *    prediction (q_ready is recorded when they complete), the attention over
+ *    idx_cur and its merge, which also advances the ring.  sel_stream waits for
+ *    q_ready, then scores and selects into idx_next/n_sel_next and records
+ *    idx_next_ready (when not NULL).  q_ready and idx_cur_ready must be valid
+ *    events.  The caller swaps idx/n_sel buffers and events between the steps
+ *    of a layer; the selection of step t writes the buffer that step t-1's
+ *    attention read, and is ordered after it through q_ready.
  * Bootstrap mode (idx_cur == NULL): everything runs on attn_stream: push,
  * predict, score, select into idx_next, then attention over idx_next.
  * Results of both modes do not depend on the stream arrangement (the kernels

@@ -206,7 +206,7 @@ asp_status asp_step(const asp_dims* dims, const asp_cfg* cfg, const float* q_cur
   if (!aligned16(ws)) return ASP_ERR_WORKSPACE;
   const bool pipelined = idx_cur != nullptr;
   const bool two_streams = pipelined && sel_stream != nullptr && sel_stream != attn_stream;
-  if (two_streams && q_ready == nullptr) return ASP_ERR_INVALID_ARG;
+  if (two_streams && (q_ready == nullptr || idx_cur_ready == nullptr)) return ASP_ERR_INVALID_ARG;
   const StepLayout lay = step_layout(s);
   if (ws == nullptr || ws_bytes < lay.total) return ASP_ERR_WORKSPACE;
   unsigned char* base = static_cast<unsigned char*>(ws);
@@ -232,22 +232,22 @@ asp_status asp_step(const asp_dims* dims, const asp_cfg* cfg, const float* q_cur
                                    attn_stream, idx_next_ready));
     return ASP_OK;
   }
-  // Two streams.  The selection stream starts once q_cur exists (q_ready, as
-  // recorded on the attention stream) and the previous step's attention, which
-  // read the buffer idx_next now overwrites, is done.  q_ready is then
-  // re-recorded by the predictor launch, and the attention stream waits for it
-  // as well: the attention (which needs none of the predictor's output) thus
-  // shares the GPU with the HBM-bound score pass rather than with the
-  // latency-bound predictor.  idx_next_ready is recorded by the last select
-  // launch.  Events recorded by a launch itself cost no extra queue packet.
-  ASP_TRY_HIP(hipEventRecord(q_ready, attn_stream));
+  // Two streams.  The attention stream first waits for idx_cur_ready (the
+  // selection the attention reads, made by the previous step with this
+  // workspace), then runs the predictor, so that the predictor overlaps the
+  // selection work of other layers' steps instead of sitting on the selection
+  // stream.  q_ready is recorded by the predictor launch itself and the
+  // selection stream waits for it; the attention's merge advances the ring,
+  // after every predictor block has read it and before the next predictor.
+  // idx_next_ready is recorded by the last select launch.  Events recorded by a
+  // launch itself cost no extra queue packet.
+  ASP_TRY_HIP(hipStreamWaitEvent(attn_stream, idx_cur_ready, 0));
+  ASP_TRY_HIP(asp::launch_predict(s, q_hist, hist_newest, hist_len, q_cur, q_pred, hist, attn_stream, q_ready));
   ASP_TRY_HIP(hipStreamWaitEvent(sel_stream, q_ready, 0));
-  ASP_TRY_HIP(asp::launch_predict(s, q_hist, hist_newest, hist_len, q_cur, q_pred, hist, sel_stream, q_ready));
-  if (idx_cur_ready) ASP_TRY_HIP(hipStreamWaitEvent(attn_stream, idx_cur_ready, 0));
-  ASP_TRY_HIP(hipStreamWaitEvent(attn_stream, q_ready, 0));
-  ASP_TRY_HIP(asp::launch_attend(s, q_cur, k, v, idx_cur, n_sel_cur, out, partials, attn_stream));
+  ASP_TRY_HIP(asp::launch_attend(s, q_cur, k, v, idx_cur, n_sel_cur, out, partials, attn_stream, hist_newest,
+                                 hist_len));
   ASP_TRY_HIP(asp::launch_score(s, q_pred, k, seq_lens, scores, hist, sel_stream));
-  ASP_TRY_HIP(asp::launch_select(s, scores, hist, seq_lens, idx_next, n_sel_next, hist_newest, hist_len, sel_ws,
+  ASP_TRY_HIP(asp::launch_select(s, scores, hist, seq_lens, idx_next, n_sel_next, nullptr, nullptr, sel_ws,
                                  sel_stream, idx_next_ready));
   return ASP_OK;
 }

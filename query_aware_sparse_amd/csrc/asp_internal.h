@@ -45,10 +45,13 @@ hipError_t launch_select(const Shape& s, const float* scores, const uint32_t* hi
                          int32_t* idx, int32_t* n_sel, int32_t* adv_newest, int32_t* adv_len, void* ws,
                          hipStream_t st, hipEvent_t done = nullptr);
 // Sparse attention: split-K partials into `partials`, then the merge into out.
+// adv_newest/adv_len (nullable): the merge launch advances the query ring.
 hipError_t launch_attend(const Shape& s, const float* q, const void* k, const void* v, const int32_t* idx,
-                         const int32_t* n_sel, float* out, void* partials, hipStream_t st);
+                         const int32_t* n_sel, float* out, void* partials, hipStream_t st,
+                         int32_t* adv_newest = nullptr, int32_t* adv_len = nullptr);
 // The merge alone (partials written by the attention blocks).
-hipError_t launch_merge(const Shape& s, const int32_t* n_sel, float* out, const void* partials, hipStream_t st);
+hipError_t launch_merge(const Shape& s, const int32_t* n_sel, float* out, const void* partials, hipStream_t st,
+                        int32_t* adv_newest = nullptr, int32_t* adv_len = nullptr);
 
 // ---------------------------------------------------------------- device helpers
 

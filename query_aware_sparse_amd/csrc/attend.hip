@@ -43,12 +43,22 @@ constexpr int MERGE_MAX_SPLITS = 256;
 __global__ void __launch_bounds__(128) merge_kernel(const float* __restrict__ part_acc,
                                                     const float* __restrict__ part_ml,
                                                     const int32_t* __restrict__ n_sel, float* __restrict__ out,
-                                                    int Hq, int Hkv, int G, int D, int C, int nsplit, int tpb) {
+                                                    int Hq, int Hkv, int G, int D, int C, int nsplit, int tpb,
+                                                    int32_t* __restrict__ adv_newest, int32_t* __restrict__ adv_len,
+                                                    int W) {
   constexpr int PER = MERGE_MAX_SPLITS / 64;
   __shared__ float sw[MERGE_MAX_SPLITS];
   __shared__ float s_inv_l;
   const int bh = blockIdx.x;
   const int b = bh / Hq, h = bh % Hq;
+  // Ring advance of a two-stream step (the predictor launch that read newest
+  // and len for this step has completed before the attention started).
+  if (adv_newest != nullptr && h == 0 && threadIdx.x == 0) {
+    int o = adv_newest[b] % W;
+    if (o < 0) o += W;
+    adv_newest[b] = o + 1 == W ? 0 : o + 1;
+    adv_len[b] = min(clampi(adv_len[b], 0, W) + 1, W);
+  }
   const int g = h / G, hh = h % G;
   const int unit = b * Hkv + g;
   const int n = clampi(n_sel[unit], 0, C);
@@ -115,7 +125,8 @@ static hipError_t launch_attend_d(const Shape& s, const float* q, const void* k,
 }
 
 hipError_t launch_attend(const Shape& s, const float* q, const void* k, const void* v, const int32_t* idx,
-                         const int32_t* n_sel, float* out, void* partials, hipStream_t st) {
+                         const int32_t* n_sel, float* out, void* partials, hipStream_t st, int32_t* adv_newest,
+                         int32_t* adv_len) {
   if (s.B == 0) return hipSuccess;
   const int nsplit = attend_num_splits(s);
   float* part_acc = static_cast<float*>(partials);
@@ -128,16 +139,18 @@ hipError_t launch_attend(const Shape& s, const float* q, const void* k, const vo
     e = s.D == 64 ? launch_attend_d<float, 64>(s, q, k, v, idx, n_sel, part_acc, part_ml, st)
                   : launch_attend_d<float, 128>(s, q, k, v, idx, n_sel, part_acc, part_ml, st);
   if (e != hipSuccess) return e;
-  return launch_merge(s, n_sel, out, partials, st);
+  return launch_merge(s, n_sel, out, partials, st, adv_newest, adv_len);
 }
 
-hipError_t launch_merge(const Shape& s, const int32_t* n_sel, float* out, const void* partials, hipStream_t st) {
+hipError_t launch_merge(const Shape& s, const int32_t* n_sel, float* out, const void* partials, hipStream_t st,
+                        int32_t* adv_newest, int32_t* adv_len) {
   if (s.B == 0) return hipSuccess;
   const int nsplit = attend_num_splits(s);
   const float* part_acc = static_cast<const float*>(partials);
   const float* part_ml = part_acc + (size_t)s.B * s.Hkv * nsplit * s.G * s.D;
   hipLaunchKernelGGL(merge_kernel, dim3(s.B * s.Hq), dim3(128), 0, st, part_acc, part_ml, n_sel, out, s.Hq, s.Hkv,
-                     s.G, s.D, s.C, nsplit, attend_tokens_per_block(s.D, s.kv));
+                     s.G, s.D, s.C, nsplit, attend_tokens_per_block(s.D, s.kv), adv_newest, adv_len,
+                     s.W > 0 ? s.W : 1);
   return hipGetLastError();
 }
 

@@ -283,7 +283,7 @@ __global__ void __launch_bounds__(SEL_THREADS) select_finish_kernel(const int32_
   const int r0 = min(tid * m, nreg), r1 = min(r0 + m, nreg);
   uint32_t local = 0u;
   for (int r = r0; r < r1; ++r) {
-    const uint32_t c = counts[r];
+    const uint32_t c = min(counts[r], (uint32_t)REGION);  // a region holds at most REGION candidates
     woff[r] = local;
     local += c;
   }

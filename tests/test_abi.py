@@ -123,6 +123,8 @@ def test_null_pointers_and_short_workspace_rejected(lib):
     #                   idx_cur n_sel_cur idx_nx nsel_nx out  ws    ws_bytes  attn  sel   events
     assert lib.asp_step(*args, one, None, one, one, one, one, 1 << 40, None, None, None, None, None) == 1
     assert lib.asp_step(*args, None, None, one, one, one, None, 0, None, None, None, None, None) == 3
-    # two distinct streams need a q_ready event
+    # two distinct streams need a q_ready event and an idx_cur_ready event
     assert lib.asp_step(*args, one, one, one, one, one, one, 1 << 40, ctypes.c_void_p(1), ctypes.c_void_p(2),
                         None, None, None) == 1
+    assert lib.asp_step(*args, one, one, one, one, one, one, 1 << 40, ctypes.c_void_p(1), ctypes.c_void_p(2),
+                        ctypes.c_void_p(3), None, None) == 1
