@@ -30,14 +30,15 @@ def _gpu():
 class Problem:
     """Device-resident inputs and state of one layer of a workload."""
 
-    def __init__(self, wl: wk.Workload, kv_device="cpu", layer=0, n_steps=8):
+    def __init__(self, wl: wk.Workload, kv_device="cpu", layer=0, n_steps=8, kv=None):
         self.wl = wl
         self.dims = A.Dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.t_cap,
                            A.KV_BF16 if wl.kv_dtype == "bf16" else A.KV_F32)
         self.cfg = A.Cfg(wl.window, wl.top_c, wl.lam)
         self.seq_lens = wk.make_seq_lens(wl).to(DEV)
-        k, v = wk.make_kv(wl, wk.make_seq_lens(wl), layer=layer, device=kv_device)
-        self.k, self.v = k.to(DEV), v.to(DEV)
+        if kv is None:  # else K/V already generated for this workload's batch and lengths
+            kv = wk.make_kv(wl, wk.make_seq_lens(wl), layer=layer, device=kv_device)
+        self.k, self.v = kv[0].to(DEV), kv[1].to(DEV)
         self.queries = wk.make_queries(wl, wl.history_steps + n_steps, layer=layer)
         self.q_hist, self.newest, self.length = [x.to(DEV) for x in wk.empty_history(wl)]
         B, Hq, Hkv, D, C = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.top_c
