@@ -60,6 +60,8 @@ def _load():
     lib.oracle_select.restype = None
     lib.oracle_attend.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P]
     lib.oracle_attend.restype = I
+    lib.oracle_overlap.argtypes = [I, I, I, P, P, P, P, P]
+    lib.oracle_overlap.restype = None
     _lib = lib
     return lib
 
@@ -173,4 +175,18 @@ def attend(q, k, v, idx, n_sel):
                                _ptr(n_sel), _ptr(out))
     if rc != 0:
         raise IndexError("oracle_attend: selected index outside [0, T_cap)")
+    return out
+
+
+def overlap(idx_a, n_a, idx_b, n_b, T_cap: int):
+    """Per unit, the number of distinct indices in [0, T_cap) present in both
+    selections (idx_*[..., C] int32, n_*[...] int32, leading dims = units) --
+    the set intersection behind the temporal-locality and prediction-recall
+    measurements of the reproduction card ("What reproduces")."""
+    idx_a, idx_b = _c(idx_a, np.int32), _c(idx_b, np.int32)
+    n_a, n_b = _c(n_a, np.int32), _c(n_b, np.int32)
+    C = idx_a.shape[-1]
+    units = int(np.prod(idx_a.shape[:-1]))
+    out = np.empty(idx_a.shape[:-1], np.int32)
+    _load().oracle_overlap(units, C, int(T_cap), _ptr(idx_a), _ptr(n_a), _ptr(idx_b), _ptr(n_b), _ptr(out))
     return out

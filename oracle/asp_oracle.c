@@ -357,3 +357,31 @@ int oracle_attend(int B, int Hq, int Hkv, int D, int T_cap, int kv_dtype, int C,
   }
   return rc;
 }
+
+/* Overlap of two selections per unit: the number of distinct token indices in
+ * [0, T_cap) present in both idx_a[u][0..n_a[u]) and idx_b[u][0..n_b[u]) (n
+ * clamped to [0, C]).  Reproduction card, "What reproduces": the temporal
+ * locality (overlap of top-k sets within a recent window) and the recall of the
+ * predicted selection against the true one are both such set intersections.
+ * A marker array per unit: 1 = in A, 2 = in A and already counted from B. */
+void oracle_overlap(int units, int C, int T_cap, const int* idx_a, const int* n_a, const int* idx_b,
+                    const int* n_b, int* out) {
+#pragma omp parallel for schedule(dynamic)
+  for (int u = 0; u < units; ++u) {
+    unsigned char* mark = (unsigned char*)calloc((size_t)(unsigned)T_cap, 1);
+    int na = n_a[u] < 0 ? 0 : (n_a[u] > C ? C : n_a[u]);
+    int nb = n_b[u] < 0 ? 0 : (n_b[u] > C ? C : n_b[u]);
+    const int* a = idx_a + (size_t)u * C;
+    const int* b = idx_b + (size_t)u * C;
+    for (int i = 0; i < na; ++i)
+      if (a[i] >= 0 && a[i] < T_cap) mark[a[i]] = 1;
+    int count = 0;
+    for (int j = 0; j < nb; ++j) {
+      if (b[j] < 0 || b[j] >= T_cap || mark[b[j]] != 1) continue;
+      mark[b[j]] = 2;
+      ++count;
+    }
+    out[u] = count;
+    free(mark);
+  }
+}
