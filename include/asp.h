@@ -143,6 +143,20 @@ asp_status asp_score_keys(const asp_dims* dims, const float* q_pred, const void*
 asp_status asp_select_topc(const asp_dims* dims, const asp_cfg* cfg, const float* scores, const int32_t* seq_lens,
                            int32_t* idx, int32_t* n_sel, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Overlap of two selections per unit, the diagnostic of the temporal locality
+ * and prediction recall claims ([card] "What reproduces (and what does not)":
+ * the overlap of top-k sets within a recent 16-query window, and the share of
+ * the true next-step top-k selection that the ridge-predicted query recovers).
+ * overlap[b][g] = the number of indices i in [0, t_cap) that appear both in
+ * idx_a[b][g][0..n_sel_a[b][g]) and in idx_b[b][g][0..n_sel_b[b][g]).  Both
+ * lists must be strictly ascending, as asp_select_topc and asp_step write
+ * them (other orders give unspecified counts); the n_sel values are clamped
+ * to [0, top_c].  idx_* [B][Hkv][top_c] int32, n_sel_* and overlap [B][Hkv]
+ * int32.  ASP_ERR_UNSUPPORTED when top_c > 32768. */
+asp_status asp_selection_overlap(const asp_dims* dims, const asp_cfg* cfg, const int32_t* idx_a,
+                                 const int32_t* n_sel_a, const int32_t* idx_b, const int32_t* n_sel_b,
+                                 int32_t* overlap, hipStream_t stream);
+
 /* Sparse decode attention over the selected tokens ([card] "Layout" and "Key
  * finding": attention over the top-C tokens only).  For every (b, h), with
  * g = h / G and S = idx[b][g][0..n_sel[b][g]):

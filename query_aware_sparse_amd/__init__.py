@@ -19,7 +19,7 @@ __all__ = [
     "OP_PUSH", "OP_PREDICT", "OP_SCORE", "OP_SELECT", "OP_DECODE", "OP_STEP",
     "KV_BF16", "KV_F32",
     "asp_workspace_size", "asp_status_string", "asp_push_query", "asp_predict_query", "asp_score_keys",
-    "asp_select_topc", "asp_sparse_decode", "asp_step",
+    "asp_select_topc", "asp_sparse_decode", "asp_step", "asp_selection_overlap",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -79,8 +79,9 @@ def load():
     lib.asp_select_topc.argtypes = [D, C, P, P, P, P, P, SZ, P]
     lib.asp_sparse_decode.argtypes = [D, C, P, P, P, P, P, P, P, SZ, P]
     lib.asp_step.argtypes = [D, C, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P, P, P, P, P]
+    lib.asp_selection_overlap.argtypes = [D, C, P, P, P, P, P, P]
     for name in ("asp_push_query", "asp_predict_query", "asp_score_keys", "asp_select_topc",
-                 "asp_sparse_decode", "asp_step"):
+                 "asp_sparse_decode", "asp_step", "asp_selection_overlap"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -221,6 +222,17 @@ def asp_select_topc(dims: Dims, cfg: Cfg, scores, seq_lens, idx, n_sel, ws=None,
     _raise("asp_select_topc", load().asp_select_topc(ctypes.byref(dims), ctypes.byref(cfg), _ptr(scores),
                                                      _ptr(seq_lens), _ptr(idx), _ptr(n_sel), wp, wb,
                                                      _stream_handle(stream)))
+
+
+def asp_selection_overlap(dims: Dims, cfg: Cfg, idx_a, n_sel_a, idx_b, n_sel_b, overlap, stream=None) -> None:
+    B, Hkv, C = dims.batch, dims.n_kv_heads, cfg.top_c
+    for name, t in (("idx_a", idx_a), ("idx_b", idx_b)):
+        _check(t, name, (B, Hkv, C), torch.int32)
+    for name, t in (("n_sel_a", n_sel_a), ("n_sel_b", n_sel_b), ("overlap", overlap)):
+        _check(t, name, (B, Hkv), torch.int32)
+    _raise("asp_selection_overlap", load().asp_selection_overlap(ctypes.byref(dims), ctypes.byref(cfg), _ptr(idx_a),
+                                                                 _ptr(n_sel_a), _ptr(idx_b), _ptr(n_sel_b),
+                                                                 _ptr(overlap), _stream_handle(stream)))
 
 
 def asp_sparse_decode(dims: Dims, cfg: Cfg, q, k, v, idx, n_sel, out, ws, stream=None) -> None:

@@ -176,6 +176,19 @@ asp_status asp_select_topc(const asp_dims* dims, const asp_cfg* cfg, const float
   return hip_status(asp::launch_select(s, scores, nullptr, seq_lens, idx, n_sel, nullptr, nullptr, ws, stream));
 }
 
+asp_status asp_selection_overlap(const asp_dims* dims, const asp_cfg* cfg, const int32_t* idx_a,
+                                 const int32_t* n_sel_a, const int32_t* idx_b, const int32_t* n_sel_b,
+                                 int32_t* overlap, hipStream_t stream) {
+  Shape s;
+  asp_status st = check_all(dims, cfg, &s);
+  if (st != ASP_OK) return st;
+  if (!idx_a || !n_sel_a || !idx_b || !n_sel_b || !overlap) return ASP_ERR_INVALID_ARG;
+  if (!aligned4(idx_a) || !aligned4(n_sel_a) || !aligned4(idx_b) || !aligned4(n_sel_b) || !aligned4(overlap))
+    return ASP_ERR_INVALID_ARG;
+  if (s.C > asp::overlap_max_c()) return ASP_ERR_UNSUPPORTED;
+  return hip_status(asp::launch_overlap(s, idx_a, n_sel_a, idx_b, n_sel_b, overlap, stream));
+}
+
 asp_status asp_sparse_decode(const asp_dims* dims, const asp_cfg* cfg, const float* q, const void* k, const void* v,
                              const int32_t* idx, const int32_t* n_sel, float* out, void* ws, size_t ws_bytes,
                              hipStream_t stream) {

@@ -44,6 +44,11 @@ size_t select_ws_bytes(const Shape& s, bool with_hist);
 hipError_t launch_select(const Shape& s, const float* scores, const uint32_t* hist, const int32_t* seq_lens,
                          int32_t* idx, int32_t* n_sel, int32_t* adv_newest, int32_t* adv_len, void* ws,
                          hipStream_t st, hipEvent_t done = nullptr);
+// Per unit, the number of indices that two ascending selections share
+// (s.C <= overlap_max_c()).
+int overlap_max_c();
+hipError_t launch_overlap(const Shape& s, const int32_t* idx_a, const int32_t* n_a, const int32_t* idx_b,
+                          const int32_t* n_b, int32_t* out, hipStream_t st);
 // Sparse attention: split-K partials into `partials`, then the merge into out.
 // adv_newest/adv_len (nullable): the merge launch advances the query ring.
 hipError_t launch_attend(const Shape& s, const float* q, const void* k, const void* v, const int32_t* idx,

@@ -1,0 +1,142 @@
+"""Prediction-quality diagnostics on synthetic inputs.
+
+Reproduction card, "What reproduces (and what does not)", claim C5: temporal
+locality of the top-k selection inside a recent 16-query window, and the share
+of the true next-step top-k selection that the ridge one-step-ahead prediction
+recovers.  The card gives the figures (on real queries of Qwen3-8B/32B-class
+models), not their definitions; the readings taken here:
+
+* the selection S(q) of a query q is the exact top-C of the GQA-group-max scores
+  max_h q_h . k_i, the rule the decode step applies to the predicted query;
+* temporal overlap at lag k: |S(q_t) & S(q_{t-k})| / |S(q_t)|; the window
+  figure is its mean over k = 1..window and over the steps that have a full
+  window behind them;
+* prediction recall: |S(q^_{t+1}) & S(q_{t+1})| / |S(q_{t+1})|, where q^_{t+1}
+  is the prediction made at step t from the ring of recent queries; beside it,
+  the "last query" baseline |S(q_t) & S(q_{t+1})| / |S(q_{t+1})|.
+
+Every score pass, selection, prediction and overlap count runs in the library's
+kernels (asp_score_keys, asp_select_topc, asp_push_query, asp_predict_query,
+asp_selection_overlap); this module only orders the calls and turns counts into
+ratios.  The synthetic queries are AR(1) sequences, so the numbers measure the
+predictor on that process, not on a model's queries.
+
+    python -m query_aware_sparse_amd.diagnostics --workload qwen3-8b-layer --steps 48
+"""
+from __future__ import annotations
+
+import argparse
+import json
+from typing import Dict, List, Tuple
+
+import torch
+
+from . import (Cfg, Dims, KV_BF16, KV_F32, OP_SELECT, asp_predict_query, asp_push_query, asp_score_keys,
+               asp_select_topc, asp_selection_overlap, asp_workspace_size)
+from . import workload as wk
+
+
+class Selector:
+    """Selections of arbitrary queries over one layer's keys (device resident)."""
+
+    def __init__(self, wl: wk.Workload, seq_lens: torch.Tensor, k: torch.Tensor, device: str):
+        self.wl = wl
+        self.dims = Dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.t_cap,
+                         KV_BF16 if wl.kv_dtype == "bf16" else KV_F32)
+        self.cfg = Cfg(wl.window, wl.top_c, wl.lam)
+        self.seq_lens, self.k = seq_lens, k
+        B, Hkv, C = wl.batch, wl.n_kv_heads, wl.top_c
+        self.scores = torch.empty((B, Hkv, wl.t_cap), dtype=torch.float32, device=device)
+        self.ws = torch.empty(asp_workspace_size(self.dims, self.cfg, OP_SELECT), dtype=torch.uint8, device=device)
+        self.device = device
+
+    def select(self, q: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+        wl = self.wl
+        idx = torch.empty((wl.batch, wl.n_kv_heads, wl.top_c), dtype=torch.int32, device=self.device)
+        n_sel = torch.empty((wl.batch, wl.n_kv_heads), dtype=torch.int32, device=self.device)
+        asp_score_keys(self.dims, q, self.k, self.seq_lens, self.scores)
+        asp_select_topc(self.dims, self.cfg, self.scores, self.seq_lens, idx, n_sel, ws=self.ws)
+        return idx, n_sel
+
+    def overlap(self, a, b) -> torch.Tensor:
+        out = torch.empty((self.wl.batch, self.wl.n_kv_heads), dtype=torch.int32, device=self.device)
+        asp_selection_overlap(self.dims, self.cfg, a[0], a[1], b[0], b[1], out)
+        return out
+
+
+def collect(wl: wk.Workload, steps: int, window: int = 16, layer: int = 0, device: str = "cuda") -> Dict:
+    """Selections and overlap counts of one synthetic layer.
+
+    Returns device tensors: ``true[t]`` = S(q_t) for every query t in
+    0 .. H+steps (H = wl.history_steps), ``pred[t]`` = S(q^_t) for t in
+    H+1 .. H+steps, and the counts ``lag[(t, k)]`` = |S(q_t) & S(q_{t-k})|,
+    ``rec_pred[t]`` and ``rec_last[t]`` (overlaps with S(q_t))."""
+    H = wl.history_steps
+    lens = wk.make_seq_lens(wl, device=device)
+    k, _ = wk.make_kv(wl, lens, layer=layer, device=device)
+    qs = wk.make_queries(wl, H + steps + 1, layer=layer, device=device)
+    sel = Selector(wl, lens, k, device)
+    true = [sel.select(qs[t]) for t in range(H + steps + 1)]
+    q_hist, newest, length = [x.to(device) for x in wk.empty_history(wl)]
+    for t in range(H):
+        asp_push_query(sel.dims, sel.cfg, qs[t], q_hist, newest, length)
+    q_pred = torch.empty_like(qs[0])
+    pred: Dict[int, Tuple[torch.Tensor, torch.Tensor]] = {}
+    rec_pred, rec_last = {}, {}
+    for t in range(H, H + steps):
+        asp_push_query(sel.dims, sel.cfg, qs[t], q_hist, newest, length)
+        asp_predict_query(sel.dims, sel.cfg, q_hist, newest, length, q_pred)   # q^_{t+1}
+        pred[t + 1] = sel.select(q_pred)
+        rec_pred[t + 1] = sel.overlap(pred[t + 1], true[t + 1])
+        rec_last[t + 1] = sel.overlap(true[t], true[t + 1])
+    lag = {}
+    for t in range(H, H + steps + 1):
+        for kk in range(1, window + 1):
+            if t - kk >= 0:
+                lag[(t, kk)] = sel.overlap(true[t], true[t - kk])
+    return {"true": true, "pred": pred, "lag": lag, "rec_pred": rec_pred, "rec_last": rec_last, "H": H,
+            "steps": steps, "window": window}
+
+
+def summarize(wl: wk.Workload, res: Dict) -> Dict:
+    """Ratios from the counts of ``collect`` (means over units and steps)."""
+    H, steps, window = res["H"], res["steps"], res["window"]
+
+    def ratio(count: torch.Tensor, base: torch.Tensor) -> float:
+        c, n = count.double(), base.double()
+        ok = n > 0
+        return float((c[ok] / n[ok]).mean()) if bool(ok.any()) else float("nan")
+
+    by_lag: List[float] = []
+    for kk in range(1, window + 1):
+        vals = [ratio(res["lag"][(t, kk)], res["true"][t][1]) for t in range(H, H + steps + 1)
+                if (t, kk) in res["lag"]]
+        by_lag.append(sum(vals) / len(vals))
+    full = [t for t in range(H, H + steps + 1) if t - window >= 0]
+    win = [sum(ratio(res["lag"][(t, kk)], res["true"][t][1]) for kk in range(1, window + 1)) / window for t in full]
+    rp = [ratio(res["rec_pred"][t], res["true"][t][1]) for t in sorted(res["rec_pred"])]
+    rl = [ratio(res["rec_last"][t], res["true"][t][1]) for t in sorted(res["rec_last"])]
+    return {
+        "workload": wl.name, "steps": steps, "window": window, "top_c": wl.top_c, "ring_window": wl.window,
+        "temporal_overlap_window_mean": sum(win) / len(win) if win else float("nan"),
+        "temporal_overlap_by_lag": by_lag,
+        "recall_predicted": sum(rp) / len(rp), "recall_last_query": sum(rl) / len(rl),
+        "recall_predicted_by_step": rp,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description="Prediction-quality diagnostics on synthetic inputs (one GPU).")
+    ap.add_argument("--workload", default="qwen3-8b-layer", choices=sorted(wk.CONFIGS))
+    ap.add_argument("--steps", type=int, default=48)
+    ap.add_argument("--window", type=int, default=16)
+    args = ap.parse_args()
+    wl = wk.CONFIGS[args.workload]
+    res = collect(wl, args.steps, args.window)
+    torch.cuda.synchronize()
+    print(json.dumps(summarize(wl, res)))
+    return 0
+
+
+if __name__ == "__main__":
+    raise SystemExit(main())

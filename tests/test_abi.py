@@ -29,7 +29,7 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "asp_workspace_size", "asp_status_string", "asp_push_query", "asp_predict_query", "asp_score_keys",
-        "asp_select_topc", "asp_sparse_decode", "asp_step"])
+        "asp_select_topc", "asp_sparse_decode", "asp_step", "asp_selection_overlap"])
 
 
 def test_library_exports_every_declared_symbol(lib):
