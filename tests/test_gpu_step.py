@@ -209,3 +209,56 @@ def test_step_modes_bit_identical_to_entry_points(wl_name):
         for s in range(n):
             for a, b in zip(runs["manual"][s], runs[mode][s]):
                 np.testing.assert_array_equal(a, b, err_msg="%s step %d" % (mode, s))
+
+
+@pytest.mark.parametrize("wl_name", ["g8-d64-w64", "g1-d128-w4"])
+def test_two_stream_layer_rotation_matches_entry_points(wl_name):
+    """The bench's schedule: L layers in rotation on two streams, one workspace,
+    idx pair and event pair per layer and one shared q_ready event; every step
+    of every layer equals the entry-point schedule of that layer."""
+    L, n = 3, 4
+    base = SMALL_STEP_CASES[wl_name]
+    probs = [Problem(base, kv_device=DEV, layer=l, n_steps=n) for l in range(L)]
+    for p in probs:
+        p.fill_history()
+    torch.cuda.synchronize()
+    rings = [(p.q_hist.clone(), p.newest.clone(), p.length.clone()) for p in probs]
+    manual = [_manual_run(p, n) for p in probs]
+    for p, r in zip(probs, rings):
+        p.q_hist.copy_(r[0]); p.newest.copy_(r[1]); p.length.copy_(r[2])
+    torch.cuda.synchronize()
+    B, Hkv, C = base.batch, base.n_kv_heads, base.top_c
+    d, c = probs[0].dims, probs[0].cfg
+    ws = [torch.empty(A.asp_workspace_size(d, c, A.OP_STEP), dtype=torch.uint8, device=DEV) for _ in range(L)]
+    idx = [[torch.full((B, Hkv, C), -5, dtype=torch.int32, device=DEV) for _ in range(2)] for _ in range(L)]
+    nsel = [[torch.zeros((B, Hkv), dtype=torch.int32, device=DEV) for _ in range(2)] for _ in range(L)]
+    ev = [[A.HipEvent(), A.HipEvent()] for _ in range(L)]
+    outs = [torch.empty_like(p.out) for p in probs]
+    q_ready = A.HipEvent()
+    attn, sel = torch.cuda.Stream(), torch.cuda.Stream()
+    attn.wait_stream(torch.cuda.current_stream())
+    got = [[] for _ in range(L)]
+    for s in range(n):
+        for l, p in enumerate(probs):  # one step of every layer, in layer order, nothing synchronised
+            q = p.queries[base.history_steps + s].to(DEV)
+            cur, nxt = s % 2, (s + 1) % 2
+            attn.wait_stream(torch.cuda.current_stream())
+            if s == 0:
+                A.asp_step(d, c, q, p.q_hist, p.newest, p.length, p.k, p.v, p.seq_lens, None, None, idx[l][nxt],
+                           nsel[l][nxt], outs[l], ws[l], attn_stream=attn, idx_next_ready=ev[l][nxt])
+            else:
+                A.asp_step(d, c, q, p.q_hist, p.newest, p.length, p.k, p.v, p.seq_lens, idx[l][cur], nsel[l][cur],
+                           idx[l][nxt], nsel[l][nxt], outs[l], ws[l], attn_stream=attn, sel_stream=sel,
+                           q_ready=q_ready, idx_cur_ready=ev[l][cur], idx_next_ready=ev[l][nxt])
+            # snapshots in each writer's stream order: the selection where it was written
+            # (the selection stream once pipelined), the rest after this step's merge
+            with torch.cuda.stream(attn if s == 0 else sel):
+                sel_snap = (idx[l][nxt].clone(), nsel[l][nxt].clone())
+            with torch.cuda.stream(attn):
+                got[l].append((outs[l].clone(),) + sel_snap + (p.q_hist.clone(), p.newest.clone(),
+                                                                p.length.clone()))
+    torch.cuda.synchronize()
+    for l in range(L):
+        for s in range(n):
+            for i, (a, b) in enumerate(zip(manual[l][s], got[l][s])):
+                np.testing.assert_array_equal(a, np_(b), err_msg="layer %d step %d field %d" % (l, s, i))
