@@ -26,9 +26,10 @@ hipError_t launch_push(const Shape& s, const float* q_cur, float* q_hist, int32_
 // Predictor.  With q_cur == nullptr it predicts from the ring as it stands.
 // With q_cur != nullptr it predicts from the ring after pushing q_cur (lag 0 is
 // q_cur, the ring supplies the older lags) and writes q_cur into each head's
-// next ring slot, but leaves newest/len unchanged: the select launch of the
-// same step advances them (it runs after every predictor workgroup has read
-// them).  hist_zero, when not null, is cleared ([B*Hkv][HIST_BINS]).
+// next ring slot, but leaves newest/len unchanged: a later launch of the same
+// step advances them (ring_advance, in the last select launch or, on two
+// streams, in the merge), once every predictor workgroup has read them.
+// hist_zero, when not null, is cleared ([B*Hkv][HIST_BINS]).
 // `done` (nullable) is recorded when the launch completes.
 hipError_t launch_predict(const Shape& s, float* q_hist, const int32_t* newest, const int32_t* len,
                           const float* q_cur, float* q_pred, uint32_t* hist_zero, hipStream_t st,
@@ -116,6 +117,15 @@ __device__ __forceinline__ uint32_t order_key(float s) {
 // Coarse histogram over the top 11 bits of order_key, per unit.
 constexpr int HIST_BINS = 2048;
 constexpr int HIST_SHIFT = 21;
+
+// One slot forward in sequence b's query ring: newest moves to the slot the
+// predictor of this step wrote (modulo W), the length grows up to W.
+__device__ __forceinline__ void ring_advance(int32_t* newest, int32_t* len, int b, int W) {
+  int o = newest[b] % W;
+  if (o < 0) o += W;
+  newest[b] = o + 1 == W ? 0 : o + 1;
+  len[b] = min(clampi(len[b], 0, W) + 1, W);
+}
 
 __device__ __forceinline__ double readlane_f64(double x, int lane) {
   const long long v = __double_as_longlong(x);

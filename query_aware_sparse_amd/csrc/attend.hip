@@ -53,12 +53,7 @@ __global__ void __launch_bounds__(128) merge_kernel(const float* __restrict__ pa
   const int b = bh / Hq, h = bh % Hq;
   // Ring advance of a two-stream step (the predictor launch that read newest
   // and len for this step has completed before the attention started).
-  if (adv_newest != nullptr && h == 0 && threadIdx.x == 0) {
-    int o = adv_newest[b] % W;
-    if (o < 0) o += W;
-    adv_newest[b] = o + 1 == W ? 0 : o + 1;
-    adv_len[b] = min(clampi(adv_len[b], 0, W) + 1, W);
-  }
+  if (adv_newest != nullptr && h == 0 && threadIdx.x == 0) ring_advance(adv_newest, adv_len, b, W);
   const int g = h / G, hh = h % G;
   const int unit = b * Hkv + g;
   const int n = clampi(n_sel[unit], 0, C);

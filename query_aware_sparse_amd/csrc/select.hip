@@ -252,14 +252,10 @@ __global__ void __launch_bounds__(SEL_THREADS) select_finish_kernel(const int32_
   const int c_eff = C < T ? C : T;
   int32_t* out = idx + (size_t)unit * C;
 
-  // Ring advance of a fused step: the predictor launch of the same step has
-  // read newest/len for every head and written the new query one slot ahead.
-  if (adv_newest != nullptr && unit % Hkv == 0 && tid == 0) {
-    int o = adv_newest[b] % W;
-    if (o < 0) o += W;
-    adv_newest[b] = o + 1 == W ? 0 : o + 1;
-    adv_len[b] = min(clampi(adv_len[b], 0, W) + 1, W);
-  }
+  // Ring advance of a step run on one stream: the predictor launch of the same
+  // step has read newest/len for every head and written the new query one slot
+  // ahead.
+  if (adv_newest != nullptr && unit % Hkv == 0 && tid == 0) ring_advance(adv_newest, adv_len, b, W);
   for (int j = c_eff + tid; j < C; j += SEL_THREADS) out[j] = -1;
   if (tid == 0) n_sel[unit] = c_eff;
   if (c_eff == T) {  // everything is selected (includes the empty row)
