@@ -30,12 +30,13 @@ def _gpu():
 class Problem:
     """Device-resident inputs and state of one layer of a workload."""
 
-    def __init__(self, wl: wk.Workload, kv_device="cpu", layer=0, n_steps=8, kv=None):
+    def __init__(self, wl: wk.Workload, kv_device="cpu", layer=0, n_steps=8, kv=None, lens=None):
         self.wl = wl
         self.dims = A.Dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.t_cap,
                            A.KV_BF16 if wl.kv_dtype == "bf16" else A.KV_F32)
         self.cfg = A.Cfg(wl.window, wl.top_c, wl.lam)
-        self.seq_lens = wk.make_seq_lens(wl).to(DEV)
+        # lens: context lengths that replace the workload's (K/V stay as generated)
+        self.seq_lens = (wk.make_seq_lens(wl) if lens is None else torch.tensor(lens, dtype=torch.int32)).to(DEV)
         if kv is None:  # else K/V already generated for this workload's batch and lengths
             kv = wk.make_kv(wl, wk.make_seq_lens(wl), layer=layer, device=kv_device)
         self.k, self.v = kv[0].to(DEV), kv[1].to(DEV)
@@ -192,7 +193,11 @@ SMALL_STEP_CASES = {
     # window 4, group 1
     "g1-d128-w4": wk.TINY.replace(name="g1-d128-w4", batch=2, n_q_heads=2, n_kv_heads=2, head_dim=128,
                                   t_cap=1000, kv_dtype="bf16", window=4, top_c=1000, history_steps=6),
+    # an empty sequence, one shorter than a split, one ending inside a split, one full
+    "g4-short-empty": wk.TINY.replace(name="g4-short-empty", batch=4, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                                      t_cap=2000, kv_dtype="bf16", window=8, top_c=700, history_steps=10),
 }
+STEP_LENS = {"g4-short-empty": [0, 37, 650, 2000]}
 
 
 @pytest.mark.parametrize("wl_name", ["tiny", "qwen3-8b-layer"] + list(SMALL_STEP_CASES))
@@ -201,7 +206,7 @@ def test_step_modes_bit_identical_to_entry_points(wl_name):
     n = 5
     runs = {}
     for mode in ("manual", "one_stream", "two_streams"):
-        p = Problem(wl, kv_device=DEV if wl.batch > 1 else "cpu", n_steps=n)
+        p = Problem(wl, kv_device=DEV if wl.batch > 1 else "cpu", n_steps=n, lens=STEP_LENS.get(wl_name))
         p.fill_history()
         torch.cuda.synchronize()
         runs[mode] = _manual_run(p, n) if mode == "manual" else _step_run(p, mode, n)
