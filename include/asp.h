@@ -183,18 +183,32 @@ asp_status asp_sparse_decode(const asp_dims* dims, const asp_cfg* cfg, const flo
  *    attn_stream (attention first); q_ready and idx_cur_ready are ignored (may
  *    be NULL); idx_next_ready, when not NULL, is recorded when the selection
  *    is written.
- *  - otherwise (two streams): attn_stream waits for idx_cur_ready, the event
- *    recorded when the selection idx_cur was written (the idx_next_ready of
- *    the step that made it, which must also be the last step that used this
- *    workspace: in a decode loop each layer keeps its own workspace, idx/n_sel
- *    buffer pair and event pair).  Then, on attn_stream: the ring push and the
- *    prediction (q_ready is recorded when they complete), the attention over
- *    idx_cur and its merge, which also advances the ring.  sel_stream waits for
- *    q_ready, then scores and selects into idx_next/n_sel_next and records
- *    idx_next_ready (when not NULL).  q_ready and idx_cur_ready must be valid
- *    events.  The caller swaps idx/n_sel buffers and events between the steps
- *    of a layer; the selection of step t writes the buffer that step t-1's
- *    attention read, and is ordered after it through q_ready.
+ *  - otherwise (two streams): the step forks onto two streams of the library
+ *    (created once per device, default priority, kept until the process
+ *    ends) and joins back through events, so that the score passes of
+ *    successive calls run back to back:
+ *      the library's predictor stream waits for attn_stream as it stands at
+ *      entry (q_cur is ready in attn_stream's order) and for idx_cur_ready,
+ *      then pushes q_cur into the ring and predicts (q_ready is recorded when
+ *      that completes); the library's score stream waits for q_ready and
+ *      scores; sel_stream waits for the scores, selects into
+ *      idx_next/n_sel_next, advances the ring and records idx_next_ready (when
+ *      not NULL); attn_stream waits for idx_cur_ready and runs the attention
+ *      over idx_cur and its merge.
+ *    idx_cur_ready is the event recorded when the selection idx_cur was
+ *    written (the idx_next_ready of the step that made it, which must also be
+ *    the last step that used this workspace: in a decode loop each layer keeps
+ *    its own workspace, idx/n_sel buffer pair and event pair).  q_ready and
+ *    idx_cur_ready must be valid events.  The caller swaps idx/n_sel buffers
+ *    and events between the steps of a layer; the selection of step t writes
+ *    the buffer that step t-1's attention read, and is ordered after it
+ *    through attn_stream's state at entry.  When the call returns, `out` is
+ *    complete in attn_stream's order; the selection and the ring are complete
+ *    in sel_stream's order (idx_next_ready).  Calls from several host threads
+ *    on one device are serialised inside the library.  The four streams
+ *    (with the default stream, five) should each have a hardware queue: HIP
+ *    gives a process 4 unless GPU_MAX_HW_QUEUES says otherwise, and streams
+ *    that share a queue run in submission order.
  * Bootstrap mode (idx_cur == NULL): everything runs on attn_stream: push,
  * predict, score, select into idx_next, then attention over idx_next.
  * Results of both modes do not depend on the stream arrangement (the kernels

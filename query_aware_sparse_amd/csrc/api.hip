@@ -3,6 +3,8 @@
 // entry point.
 #include <math.h>
 
+#include <mutex>
+
 #include "../../include/asp.h"
 #include "asp_internal.h"
 
@@ -97,6 +99,38 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
   do {                                             \
     if ((expr) != hipSuccess) return ASP_ERR_HIP;  \
   } while (0)
+
+// The two streams the pipelined step forks its predictor and its score pass
+// onto, with the events that join them: `in` marks the caller's attention
+// stream at entry (q_cur ready), `scored` the end of the score pass.  One set
+// per device, created on first use (default priority, non-blocking) and kept
+// until the process ends.  The events are re-recorded by every step; each
+// wait takes the record made just before it, under fork_mu.
+struct StepFork {
+  hipStream_t pred = nullptr, score = nullptr;
+  hipEvent_t in = nullptr, scored = nullptr;
+};
+constexpr int kMaxDevices = 64;
+StepFork g_fork[kMaxDevices];
+std::mutex g_fork_mu;
+
+// Called with g_fork_mu held.
+hipError_t step_fork(StepFork** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  StepFork& f = g_fork[dev];
+  if (f.scored == nullptr) {
+    const unsigned ev_flags = hipEventDisableTiming | hipEventDisableSystemFence;
+    if ((e = hipStreamCreateWithFlags(&f.pred, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipStreamCreateWithFlags(&f.score, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&f.in, ev_flags)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&f.scored, ev_flags)) != hipSuccess) return e;
+  }
+  *out = &f;
+  return hipSuccess;
+}
 
 // Selection work of one step: four launches.  The predictor pushes q_cur into
 // every head's ring slot and clears the coarse histograms; the score launch
@@ -245,23 +279,35 @@ asp_status asp_step(const asp_dims* dims, const asp_cfg* cfg, const float* q_cur
                                    attn_stream, idx_next_ready));
     return ASP_OK;
   }
-  // Two streams.  The attention stream first waits for idx_cur_ready (the
-  // selection the attention reads, made by the previous step with this
-  // workspace), then runs the predictor, so that the predictor overlaps the
-  // selection work of other layers' steps instead of sitting on the selection
-  // stream.  q_ready is recorded by the predictor launch itself and the
-  // selection stream waits for it; the attention's merge advances the ring,
-  // after every predictor block has read it and before the next predictor.
-  // idx_next_ready is recorded by the last select launch.  Events recorded by a
-  // launch itself cost no extra queue packet.
-  ASP_TRY_HIP(hipStreamWaitEvent(attn_stream, idx_cur_ready, 0));
-  ASP_TRY_HIP(asp::launch_predict(s, q_hist, hist_newest, hist_len, q_cur, q_pred, hist, attn_stream, q_ready));
-  ASP_TRY_HIP(hipStreamWaitEvent(sel_stream, q_ready, 0));
-  ASP_TRY_HIP(asp::launch_attend(s, q_cur, k, v, idx_cur, n_sel_cur, out, partials, attn_stream, hist_newest,
-                                 hist_len));
-  ASP_TRY_HIP(asp::launch_score(s, q_pred, k, seq_lens, scores, hist, sel_stream));
-  ASP_TRY_HIP(asp::launch_select(s, scores, hist, seq_lens, idx_next, n_sel_next, nullptr, nullptr, sel_ws,
+  // Two streams, forked four ways so that the score passes of successive
+  // calls run back to back while the latency-bound launches overlap them:
+  //  - the fork's predictor stream waits for attn_stream as it stands at entry
+  //    (q_cur ready, and with it the attention that produced q_cur in a decode
+  //    loop) and for idx_cur_ready (the previous selection made with this
+  //    workspace has finished with the histograms, the scores and the ring),
+  //    then pushes and predicts; the launch records q_ready;
+  //  - the fork's score stream waits for q_ready and scores; the launch records
+  //    the fork's `scored` event;
+  //  - sel_stream waits for `scored` and selects; its last launch advances the
+  //    ring and records idx_next_ready;
+  //  - attn_stream waits for idx_cur_ready and runs the attention and merge.
+  // The predictor waits for idx_cur_ready itself rather than through
+  // attn_stream: a chain of two cross-stream waits costs a step ~3 us more.
+  // Events recorded by a launch itself cost no extra queue packet.
+  std::lock_guard<std::mutex> lock(g_fork_mu);
+  StepFork* f = nullptr;
+  ASP_TRY_HIP(step_fork(&f));
+  ASP_TRY_HIP(hipEventRecord(f->in, attn_stream));
+  ASP_TRY_HIP(hipStreamWaitEvent(f->pred, f->in, 0));
+  ASP_TRY_HIP(hipStreamWaitEvent(f->pred, idx_cur_ready, 0));
+  ASP_TRY_HIP(asp::launch_predict(s, q_hist, hist_newest, hist_len, q_cur, q_pred, hist, f->pred, q_ready));
+  ASP_TRY_HIP(hipStreamWaitEvent(f->score, q_ready, 0));
+  ASP_TRY_HIP(asp::launch_score(s, q_pred, k, seq_lens, scores, hist, f->score, f->scored));
+  ASP_TRY_HIP(hipStreamWaitEvent(sel_stream, f->scored, 0));
+  ASP_TRY_HIP(asp::launch_select(s, scores, hist, seq_lens, idx_next, n_sel_next, hist_newest, hist_len, sel_ws,
                                  sel_stream, idx_next_ready));
+  ASP_TRY_HIP(hipStreamWaitEvent(attn_stream, idx_cur_ready, 0));
+  ASP_TRY_HIP(asp::launch_attend(s, q_cur, k, v, idx_cur, n_sel_cur, out, partials, attn_stream));
   return ASP_OK;
 }
 

@@ -2,6 +2,7 @@
 // Nothing here is part of the public C ABI (include/asp.h).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -35,9 +36,9 @@ hipError_t launch_predict(const Shape& s, float* q_hist, const int32_t* newest, 
                           const float* q_cur, float* q_pred, uint32_t* hist_zero, hipStream_t st,
                           hipEvent_t done = nullptr);
 // Scores; hist (nullable) accumulates the coarse histogram of every unit and
-// must be zero on entry.
+// must be zero on entry.  `done` (nullable) is recorded when the launch completes.
 hipError_t launch_score(const Shape& s, const float* q_pred, const void* k, const int32_t* seq_lens,
-                        float* scores, uint32_t* hist, hipStream_t st);
+                        float* scores, uint32_t* hist, hipStream_t st, hipEvent_t done = nullptr);
 // Top-C selection; hist (nullable) is the coarse histogram built by the score
 // launch (when null, one is built in ws first).  adv_newest/adv_len (nullable)
 // advance the query ring by one slot.  ws: select_ws_bytes(s, hist == nullptr).
@@ -58,6 +59,29 @@ hipError_t launch_attend(const Shape& s, const float* q, const void* k, const vo
 // The merge alone (partials written by the attention blocks).
 hipError_t launch_merge(const Shape& s, const int32_t* n_sel, float* out, const void* partials, hipStream_t st,
                         int32_t* adv_newest = nullptr, int32_t* adv_len = nullptr);
+
+// Whether `st` is being captured into a graph.
+inline bool capturing(hipStream_t st) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(st, &cs) == hipSuccess && cs == hipStreamCaptureStatusActive;
+}
+
+// Launch that records `done` (nullable) when the kernel completes.  Outside
+// stream capture the event rides on the kernel's own completion signal
+// (hipExtLaunchKernelGGL, no extra queue packet); under capture the kernel is
+// a plain launch and `done` an event-record node after it.
+template <typename... KArgs, typename... Args>
+hipError_t launch_recording(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t st, hipEvent_t done,
+                            Args... args) {
+  if (done != nullptr && !capturing(st)) {
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, nullptr, done, 0, args...);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && done != nullptr) e = hipEventRecord(done, st);
+  return e;
+}
 
 // ---------------------------------------------------------------- device helpers
 

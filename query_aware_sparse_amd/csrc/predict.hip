@@ -22,8 +22,6 @@
 //  4. the back substitutions of all windows run side by side, then each
 //     window's softmax runs across lanes, and the window predictions are
 //     pooled as one weighted sum of the lags.
-#include <hip/hip_ext.h>
-
 #include "asp_internal.h"
 
 namespace asp {
@@ -363,17 +361,17 @@ hipError_t launch_predict(const Shape& s, float* q_hist, const int32_t* newest, 
   if (s.B == 0) return done ? hipEventRecord(done, st) : hipSuccess;
   const dim3 grid(s.B * s.Hq), block(PRED_THREADS);
   const int P = s.W - 1;
-  // `done`, when given, is recorded by the launch itself (no separate marker).
-#define ASP_PRED_LAUNCH(PB)                                                                                         \
-  hipExtLaunchKernelGGL(predict_kernel<PB>, grid, block, 0, st, nullptr, done, 0, q_hist, newest, len, q_cur, q_pred, \
-                        hist_zero, s.Hq, s.Hkv, s.W, s.D, s.lambda)
-  if (P <= 3) ASP_PRED_LAUNCH(3);
-  else if (P <= 7) ASP_PRED_LAUNCH(7);
-  else if (P <= 15) ASP_PRED_LAUNCH(15);
-  else if (P <= 31) ASP_PRED_LAUNCH(31);
-  else ASP_PRED_LAUNCH(63);
+#define ASP_PRED_LAUNCH(PB)                                                                                    \
+  launch_recording(predict_kernel<PB>, grid, block, st, done, q_hist, newest, len, q_cur, q_pred, hist_zero, s.Hq, \
+                   s.Hkv, s.W, s.D, s.lambda)
+  hipError_t e;
+  if (P <= 3) e = ASP_PRED_LAUNCH(3);
+  else if (P <= 7) e = ASP_PRED_LAUNCH(7);
+  else if (P <= 15) e = ASP_PRED_LAUNCH(15);
+  else if (P <= 31) e = ASP_PRED_LAUNCH(31);
+  else e = ASP_PRED_LAUNCH(63);
 #undef ASP_PRED_LAUNCH
-  return hipGetLastError();
+  return e;
 }
 
 }  // namespace asp

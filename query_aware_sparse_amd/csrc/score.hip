@@ -27,37 +27,34 @@ __global__ void __launch_bounds__(SCORE_THREADS) score_valu_kernel(const float* 
 
 template <int D, bool HIST>
 static hipError_t launch_score_dh(const Shape& s, const float* q_pred, const void* k, const int32_t* seq_lens,
-                                  float* scores, uint32_t* hist, hipStream_t st) {
+                                  float* scores, uint32_t* hist, hipStream_t st, hipEvent_t done) {
   const dim3 grid((s.T_cap + SCORE_KEYS_PER_BLOCK - 1) / SCORE_KEYS_PER_BLOCK, s.B * s.Hkv);
   const dim3 block(SCORE_THREADS);
-#define ASP_SCORE_LAUNCH(GG)                                                                                   \
-  do {                                                                                                         \
-    if (s.kv == 0)                                                                                             \
-      hipLaunchKernelGGL((score_mfma_kernel<D, GG, HIST>), grid, block, 0, st, q_pred,                        \
-                         static_cast<const uint16_t*>(k), seq_lens, scores, hist, s.Hq, s.Hkv, s.T_cap);      \
-    else                                                                                                       \
-      hipLaunchKernelGGL((score_valu_kernel<D, GG, HIST>), grid, block, 0, st, q_pred,                        \
-                         static_cast<const float*>(k), seq_lens, scores, hist, s.Hq, s.Hkv, s.T_cap);         \
-  } while (0)
+#define ASP_SCORE_LAUNCH(GG)                                                                                    \
+  (s.kv == 0 ? launch_recording(score_mfma_kernel<D, GG, HIST>, grid, block, st, done, q_pred,                   \
+                                static_cast<const uint16_t*>(k), seq_lens, scores, hist, s.Hq, s.Hkv, s.T_cap)   \
+             : launch_recording(score_valu_kernel<D, GG, HIST>, grid, block, st, done, q_pred,                   \
+                                static_cast<const float*>(k), seq_lens, scores, hist, s.Hq, s.Hkv, s.T_cap))
+  hipError_t e;
   switch (s.G) {
-    case 1: ASP_SCORE_LAUNCH(1); break;
-    case 2: ASP_SCORE_LAUNCH(2); break;
-    case 4: ASP_SCORE_LAUNCH(4); break;
-    case 8: ASP_SCORE_LAUNCH(8); break;
+    case 1: e = ASP_SCORE_LAUNCH(1); break;
+    case 2: e = ASP_SCORE_LAUNCH(2); break;
+    case 4: e = ASP_SCORE_LAUNCH(4); break;
+    case 8: e = ASP_SCORE_LAUNCH(8); break;
     default: return hipErrorInvalidValue;
   }
 #undef ASP_SCORE_LAUNCH
-  return hipGetLastError();
+  return e;
 }
 
 hipError_t launch_score(const Shape& s, const float* q_pred, const void* k, const int32_t* seq_lens, float* scores,
-                        uint32_t* hist, hipStream_t st) {
-  if (s.B == 0) return hipSuccess;
+                        uint32_t* hist, hipStream_t st, hipEvent_t done) {
+  if (s.B == 0) return done ? hipEventRecord(done, st) : hipSuccess;
   if (hist != nullptr)
-    return s.D == 64 ? launch_score_dh<64, true>(s, q_pred, k, seq_lens, scores, hist, st)
-                     : launch_score_dh<128, true>(s, q_pred, k, seq_lens, scores, hist, st);
-  return s.D == 64 ? launch_score_dh<64, false>(s, q_pred, k, seq_lens, scores, nullptr, st)
-                   : launch_score_dh<128, false>(s, q_pred, k, seq_lens, scores, nullptr, st);
+    return s.D == 64 ? launch_score_dh<64, true>(s, q_pred, k, seq_lens, scores, hist, st, done)
+                     : launch_score_dh<128, true>(s, q_pred, k, seq_lens, scores, hist, st, done);
+  return s.D == 64 ? launch_score_dh<64, false>(s, q_pred, k, seq_lens, scores, nullptr, st, done)
+                   : launch_score_dh<128, false>(s, q_pred, k, seq_lens, scores, nullptr, st, done);
 }
 
 }  // namespace asp

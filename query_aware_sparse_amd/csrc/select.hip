@@ -21,8 +21,6 @@
 //    two radix digits over them alone, marks the chosen candidates in the
 //    bitmap and compacts the bitmap in index order: every output position is
 //    a prefix count of set bits.
-#include <hip/hip_ext.h>
-
 #include "asp_internal.h"
 
 namespace asp {
@@ -415,10 +413,10 @@ hipError_t launch_select(const Shape& s, const float* scores, const uint32_t* hi
   const int segs = (s.T_cap + SEG - 1) / SEG;
   hipLaunchKernelGGL(select_classify_kernel, dim3(segs, units), dim3(SEL_THREADS), 0, st, scores, hist, seq_lens, w,
                      s.Hkv, s.T_cap, s.C, nr);
-  // `done`, when given, is recorded by the finish launch itself (no separate marker).
-  hipExtLaunchKernelGGL(select_finish_kernel, dim3(units), dim3(SEL_THREADS), 0, st, nullptr, done, 0, seq_lens, w, idx,
-                        n_sel, adv_newest, adv_len, s.Hkv, s.T_cap, s.C, s.W > 0 ? s.W : 1, nr);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_recording(select_finish_kernel, dim3(units), dim3(SEL_THREADS), st, done, seq_lens, w, idx, n_sel,
+                          adv_newest, adv_len, s.Hkv, s.T_cap, s.C, s.W > 0 ? s.W : 1, nr);
 }
 
 }  // namespace asp

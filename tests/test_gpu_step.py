@@ -255,13 +255,14 @@ def test_two_stream_layer_rotation_matches_entry_points(wl_name):
                 A.asp_step(d, c, q, p.q_hist, p.newest, p.length, p.k, p.v, p.seq_lens, idx[l][cur], nsel[l][cur],
                            idx[l][nxt], nsel[l][nxt], outs[l], ws[l], attn_stream=attn, sel_stream=sel,
                            q_ready=q_ready, idx_cur_ready=ev[l][cur], idx_next_ready=ev[l][nxt])
-            # snapshots in each writer's stream order: the selection where it was written
-            # (the selection stream once pipelined), the rest after this step's merge
+            # snapshots in each writer's stream order: the attention output on the
+            # attention stream, the selection and the ring where the step completes
+            # them (the selection stream once pipelined)
             with torch.cuda.stream(attn if s == 0 else sel):
-                sel_snap = (idx[l][nxt].clone(), nsel[l][nxt].clone())
+                sel_snap = (idx[l][nxt].clone(), nsel[l][nxt].clone(), p.q_hist.clone(), p.newest.clone(),
+                            p.length.clone())
             with torch.cuda.stream(attn):
-                got[l].append((outs[l].clone(),) + sel_snap + (p.q_hist.clone(), p.newest.clone(),
-                                                                p.length.clone()))
+                got[l].append((outs[l].clone(),) + sel_snap)
     torch.cuda.synchronize()
     for l in range(L):
         for s in range(n):
