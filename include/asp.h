@@ -184,9 +184,12 @@ asp_status asp_sparse_decode(const asp_dims* dims, const asp_cfg* cfg, const flo
  *    be NULL); idx_next_ready, when not NULL, is recorded when the selection
  *    is written.
  *  - otherwise (two streams): the step forks onto two streams of the library
- *    (created once per device, default priority, kept until the process
- *    ends) and joins back through events, so that the score passes of
- *    successive calls run back to back:
+ *    (created once per device, default priority, kept until
+ *    asp_release_streams or the process ends) and joins back through events,
+ *    so that the score passes of successive calls run back to back; the
+ *    score stream is CU-masked to leave the last 32-CU group (one XCD) to
+ *    the latency-bound launches, and as a CU-masked stream it synchronises
+ *    with the legacy default stream:
  *      the library's predictor stream waits for attn_stream as it stands at
  *      entry (q_cur is ready in attn_stream's order) and for idx_cur_ready,
  *      then pushes q_cur into the ring and predicts (q_ready is recorded when
@@ -209,6 +212,8 @@ asp_status asp_sparse_decode(const asp_dims* dims, const asp_cfg* cfg, const flo
  *    (with the default stream, five) should each have a hardware queue: HIP
  *    gives a process 4 unless GPU_MAX_HW_QUEUES says otherwise, and streams
  *    that share a queue run in submission order.
+ * asp_step returns ASP_ERR_UNSUPPORTED when attn_stream or sel_stream is being
+ * captured into a graph.
  * Bootstrap mode (idx_cur == NULL): everything runs on attn_stream: push,
  * predict, score, select into idx_next, then attention over idx_next.
  * Results of both modes do not depend on the stream arrangement (the kernels
@@ -222,6 +227,15 @@ asp_status asp_step(const asp_dims* dims, const asp_cfg* cfg, const float* q_cur
                     int32_t* idx_next, int32_t* n_sel_next, float* out, void* ws, size_t ws_bytes,
                     hipStream_t attn_stream, hipStream_t sel_stream, hipEvent_t q_ready,
                     hipEvent_t idx_cur_ready, hipEvent_t idx_next_ready);
+
+/* Waits for and destroys the streams and events that two-stream asp_step
+ * calls created (on every device); the next such call creates them again.
+ * Call it before the process ends, with no asp_step call in progress: it lets
+ * the library's streams end before the HIP runtime is torn down, which some
+ * tools that wrap the runtime (profilers) need.  The Python binding calls it
+ * at interpreter exit.  Returns ASP_ERR_HIP if a HIP call failed (the
+ * remaining streams and events are still released). */
+asp_status asp_release_streams(void);
 
 #ifdef __cplusplus
 }

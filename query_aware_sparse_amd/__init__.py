@@ -8,6 +8,7 @@ library is not built, every call raises ``AspError``.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
 from typing import Optional
@@ -19,7 +20,7 @@ __all__ = [
     "OP_PUSH", "OP_PREDICT", "OP_SCORE", "OP_SELECT", "OP_DECODE", "OP_STEP",
     "KV_BF16", "KV_F32",
     "asp_workspace_size", "asp_status_string", "asp_push_query", "asp_predict_query", "asp_score_keys",
-    "asp_select_topc", "asp_sparse_decode", "asp_step", "asp_selection_overlap",
+    "asp_select_topc", "asp_sparse_decode", "asp_step", "asp_selection_overlap", "asp_release_streams",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -80,10 +81,13 @@ def load():
     lib.asp_sparse_decode.argtypes = [D, C, P, P, P, P, P, P, P, SZ, P]
     lib.asp_step.argtypes = [D, C, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P, P, P, P, P]
     lib.asp_selection_overlap.argtypes = [D, C, P, P, P, P, P, P]
+    lib.asp_release_streams.argtypes = []
     for name in ("asp_push_query", "asp_predict_query", "asp_score_keys", "asp_select_topc",
-                 "asp_sparse_decode", "asp_step", "asp_selection_overlap"):
+                 "asp_sparse_decode", "asp_step", "asp_selection_overlap", "asp_release_streams"):
         getattr(lib, name).restype = I32
     _lib = lib
+    # the library's streams end before the HIP runtime is torn down
+    atexit.register(lib.asp_release_streams)
     return lib
 
 
@@ -274,3 +278,9 @@ def asp_step(dims: Dims, cfg: Cfg, q_cur, q_hist, hist_newest, hist_len, k, v, s
                                        _ptr(hist_newest), _ptr(hist_len), _ptr(k), _ptr(v), _ptr(seq_lens),
                                        _ptr(idx_cur), _ptr(n_sel_cur), _ptr(idx_next), _ptr(n_sel_next), _ptr(out),
                                        wp, wb, attn, sel, _ev(q_ready), _ev(idx_cur_ready), _ev(idx_next_ready)))
+
+
+def asp_release_streams() -> None:
+    """Wait for and destroy the library's streams of two-stream asp_step calls
+    (they are created again by the next such call).  Also runs at exit."""
+    _raise("asp_release_streams", load().asp_release_streams())

@@ -103,8 +103,8 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 // The two streams the pipelined step forks its predictor and its score pass
 // onto, with the events that join them: `in` marks the caller's attention
 // stream at entry (q_cur ready), `scored` the end of the score pass.  One set
-// per device, created on first use (default priority, non-blocking) and kept
-// until the process ends.  The events are re-recorded by every step; each
+// per device, created on first use (default priority; the score stream has a
+// CU mask, see create_score_stream) and kept until the process ends.  The events are re-recorded by every step; each
 // wait takes the record made just before it, under fork_mu.
 struct StepFork {
   hipStream_t pred = nullptr, score = nullptr;
@@ -114,6 +114,28 @@ constexpr int kMaxDevices = 64;
 StepFork g_fork[kMaxDevices];
 std::mutex g_fork_mu;
 
+// The score stream's CU mask: every CU but those of the last 32-CU group.  On
+// MI355X (256 CUs) the mask words map to the eight XCDs, so the score passes
+// run on seven XCDs and leave the eighth to the latency-bound launches
+// (predictor, select, merge), which otherwise wait for CU slots behind score
+// blocks.  Measured at the Qwen3-8B layer shape: 107.7 us per step against
+// 111.1 us unmasked; masks that split an XCD (216, 232, 240 CUs) are slower
+// than either, since the score grid is spread evenly over the XCDs it may use.
+// Falls back to an unmasked stream where the device has one group or the mask
+// is refused.
+hipError_t create_score_stream(int dev, hipStream_t* st) {
+  int ncu = 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && ncu % 32 == 0 &&
+      ncu / 32 >= 2 && ncu / 32 <= 32) {
+    uint32_t mask[32] = {};
+    const int words = ncu / 32;
+    for (int w = 0; w + 1 < words; ++w) mask[w] = 0xffffffffu;
+    if (hipExtStreamCreateWithCUMask(st, (uint32_t)words, mask) == hipSuccess) return hipSuccess;
+    (void)hipGetLastError();  // refused: clear the error, fall back below
+  }
+  return hipStreamCreateWithFlags(st, hipStreamNonBlocking);
+}
+
 // Called with g_fork_mu held.
 hipError_t step_fork(StepFork** out) {
   int dev = 0;
@@ -121,12 +143,20 @@ hipError_t step_fork(StepFork** out) {
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   StepFork& f = g_fork[dev];
-  if (f.scored == nullptr) {
+  if (f.scored == nullptr) {  // all four are created together, or none is kept
     const unsigned ev_flags = hipEventDisableTiming | hipEventDisableSystemFence;
-    if ((e = hipStreamCreateWithFlags(&f.pred, hipStreamNonBlocking)) != hipSuccess) return e;
-    if ((e = hipStreamCreateWithFlags(&f.score, hipStreamNonBlocking)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&f.in, ev_flags)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&f.scored, ev_flags)) != hipSuccess) return e;
+    StepFork n;
+    if ((e = hipStreamCreateWithFlags(&n.pred, hipStreamNonBlocking)) == hipSuccess &&
+        (e = create_score_stream(dev, &n.score)) == hipSuccess &&
+        (e = hipEventCreateWithFlags(&n.in, ev_flags)) == hipSuccess &&
+        (e = hipEventCreateWithFlags(&n.scored, ev_flags)) == hipSuccess) {
+      f = n;
+    } else {
+      if (n.pred) (void)hipStreamDestroy(n.pred);
+      if (n.score) (void)hipStreamDestroy(n.score);
+      if (n.in) (void)hipEventDestroy(n.in);
+      return e;
+    }
   }
   *out = &f;
   return hipSuccess;
@@ -254,6 +284,10 @@ asp_status asp_step(const asp_dims* dims, const asp_cfg* cfg, const float* q_cur
   const bool pipelined = idx_cur != nullptr;
   const bool two_streams = pipelined && sel_stream != nullptr && sel_stream != attn_stream;
   if (two_streams && (q_ready == nullptr || idx_cur_ready == nullptr)) return ASP_ERR_INVALID_ARG;
+  // The step records events on its launches and forks onto the library's
+  // streams; recording it into a graph is not supported.
+  if (asp::capturing(attn_stream) || (sel_stream != nullptr && asp::capturing(sel_stream)))
+    return ASP_ERR_UNSUPPORTED;
   const StepLayout lay = step_layout(s);
   if (ws == nullptr || ws_bytes < lay.total) return ASP_ERR_WORKSPACE;
   unsigned char* base = static_cast<unsigned char*>(ws);
@@ -309,6 +343,34 @@ asp_status asp_step(const asp_dims* dims, const asp_cfg* cfg, const float* q_cur
   ASP_TRY_HIP(hipStreamWaitEvent(attn_stream, idx_cur_ready, 0));
   ASP_TRY_HIP(asp::launch_attend(s, q_cur, k, v, idx_cur, n_sel_cur, out, partials, attn_stream));
   return ASP_OK;
+}
+
+asp_status asp_release_streams(void) {
+  std::lock_guard<std::mutex> lock(g_fork_mu);
+  bool any = false;
+  for (const StepFork& f : g_fork) any |= f.scored != nullptr;
+  if (!any) return ASP_OK;  // nothing was created (no HIP call is made)
+  int cur = 0;
+  const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+  bool ok = true;
+  for (int dev = 0; dev < kMaxDevices; ++dev) {
+    StepFork& f = g_fork[dev];
+    if (f.scored == nullptr) continue;
+    ok &= hipSetDevice(dev) == hipSuccess;
+    for (hipStream_t* st : {&f.pred, &f.score}) {
+      if (*st == nullptr) continue;
+      ok &= hipStreamSynchronize(*st) == hipSuccess;
+      ok &= hipStreamDestroy(*st) == hipSuccess;
+      *st = nullptr;
+    }
+    for (hipEvent_t* ev : {&f.in, &f.scored}) {
+      if (*ev == nullptr) continue;
+      ok &= hipEventDestroy(*ev) == hipSuccess;
+      *ev = nullptr;
+    }
+  }
+  if (have_cur) ok &= hipSetDevice(cur) == hipSuccess;
+  return ok ? ASP_OK : ASP_ERR_HIP;
 }
 
 }  // extern "C"

@@ -66,21 +66,17 @@ inline bool capturing(hipStream_t st) {
   return hipStreamIsCapturing(st, &cs) == hipSuccess && cs == hipStreamCaptureStatusActive;
 }
 
-// Launch that records `done` (nullable) when the kernel completes.  Outside
-// stream capture the event rides on the kernel's own completion signal
-// (hipExtLaunchKernelGGL, no extra queue packet); under capture the kernel is
-// a plain launch and `done` an event-record node after it.
+// Launch that records `done` (nullable) when the kernel completes.  The event
+// rides on the kernel's own completion signal (hipExtLaunchKernelGGL), so it
+// costs no extra queue packet.
 template <typename... KArgs, typename... Args>
 hipError_t launch_recording(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t st, hipEvent_t done,
                             Args... args) {
-  if (done != nullptr && !capturing(st)) {
+  if (done != nullptr)
     hipExtLaunchKernelGGL(kernel, grid, block, 0, st, nullptr, done, 0, args...);
-    return hipGetLastError();
-  }
-  hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
-  hipError_t e = hipGetLastError();
-  if (e == hipSuccess && done != nullptr) e = hipEventRecord(done, st);
-  return e;
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- device helpers

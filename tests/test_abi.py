@@ -29,13 +29,18 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "asp_workspace_size", "asp_status_string", "asp_push_query", "asp_predict_query", "asp_score_keys",
-        "asp_select_topc", "asp_sparse_decode", "asp_step", "asp_selection_overlap"])
+        "asp_select_topc", "asp_sparse_decode", "asp_step", "asp_selection_overlap", "asp_release_streams"])
 
 
 def test_library_exports_every_declared_symbol(lib):
     raw = ctypes.CDLL(A.library_path())
     for name in declared_functions():
         assert hasattr(raw, name), name
+
+
+def test_release_streams_without_any_is_a_no_op(lib):
+    # no two-stream step has run in this process: nothing to release, no HIP call
+    A.asp_release_streams()
 
 
 def test_status_strings(lib):

@@ -6,7 +6,8 @@
   computed from the GPU's prediction, selection bit-exact on the GPU's fp32
   scores and within the 1e-5 * max|score| boundary gap of the oracle's own fp64
   selection, attention within 1e-2 on the GPU's selection.
-* asp_step (bootstrap, pipelined on one stream, pipelined on two streams) is
+* asp_step (bootstrap, pipelined on one stream, pipelined on two streams, also
+  with the library's streams released and created again mid-run) is
   bit-identical to the same schedule built from the individual entry points.
 """
 import numpy as np
@@ -128,8 +129,10 @@ def test_qwen3_8b_layer_full_shape_staged():
     _staged_check(p, p.queries[wl.history_steps])
 
 
-def _step_run(p: Problem, mode: str, n_steps: int):
-    """Run n_steps decode steps with asp_step in `mode`; return per-step outputs."""
+def _step_run(p: Problem, mode: str, n_steps: int, release_after=None):
+    """Run n_steps decode steps with asp_step in `mode`; return per-step outputs.
+    release_after: step after which the library's streams are released (the
+    next two-stream step creates them again)."""
     wl, d, c = p.wl, p.dims, p.cfg
     B, Hkv, C = wl.batch, wl.n_kv_heads, wl.top_c
     ws = torch.empty(A.asp_workspace_size(d, c, A.OP_STEP), dtype=torch.uint8, device=DEV)
@@ -156,6 +159,8 @@ def _step_run(p: Problem, mode: str, n_steps: int):
         torch.cuda.synchronize()
         results.append((np_(p.out).copy(), np_(idx[nxt]).copy(), np_(nsel[nxt]).copy(), np_(p.q_hist).copy(),
                         np_(p.newest).copy(), np_(p.length).copy()))
+        if s == release_after:
+            A.asp_release_streams()
     return results
 
 
@@ -205,12 +210,17 @@ def test_step_modes_bit_identical_to_entry_points(wl_name):
     wl = wk.CONFIGS.get(wl_name) or SMALL_STEP_CASES[wl_name]
     n = 5
     runs = {}
-    for mode in ("manual", "one_stream", "two_streams"):
+    for mode in ("manual", "one_stream", "two_streams", "two_streams_release"):
         p = Problem(wl, kv_device=DEV if wl.batch > 1 else "cpu", n_steps=n, lens=STEP_LENS.get(wl_name))
         p.fill_history()
         torch.cuda.synchronize()
-        runs[mode] = _manual_run(p, n) if mode == "manual" else _step_run(p, mode, n)
-    for mode in ("one_stream", "two_streams"):
+        if mode == "manual":
+            runs[mode] = _manual_run(p, n)
+        elif mode == "two_streams_release":  # the library's streams released mid-run and created again
+            runs[mode] = _step_run(p, "two_streams", n, release_after=2)
+        else:
+            runs[mode] = _step_run(p, mode, n)
+    for mode in ("one_stream", "two_streams", "two_streams_release"):
         for s in range(n):
             for a, b in zip(runs["manual"][s], runs[mode][s]):
                 np.testing.assert_array_equal(a, b, err_msg="%s step %d" % (mode, s))
