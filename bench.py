@@ -10,6 +10,11 @@ the same schedule serially.  Four independent KV caches (layers) are used in
 rotation so that no step reads KV that the previous step left in the 256 MB
 last-level cache; every step uses a fresh AR(1) query.
 
+--workload measures one layer of another workload shape (the Qwen3-8B stack
+layer, the Qwen3-32B layer or the ragged long-CoT batch; --top-c and --window
+override C and W); the roofline's measured traffic is then null, since the
+committed counter summary is of the Qwen3-8B layer.
+
 Prints one JSON line on stdout.  Everything else goes to stderr.
 """
 from __future__ import annotations
@@ -137,6 +142,11 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--mode", choices=["two_streams", "one_stream"], default="two_streams")
     ap.add_argument("--kv-buffers", type=int, default=4)
+    ap.add_argument("--workload", default="qwen3-8b-layer",
+                    choices=["qwen3-8b-layer", "qwen3-8b-stack", "qwen3-32b", "ragged-long-cot"],
+                    help="one decoder layer of this workload (the headline metric is qwen3-8b-layer)")
+    ap.add_argument("--top-c", type=int, default=None, help="override the workload's selection budget C")
+    ap.add_argument("--window", type=int, default=None, help="override the workload's ridge window W")
     ap.add_argument("--kernel-launches", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -163,7 +173,12 @@ def main() -> int:
         log("copied %d MiB x5" % args.copy_calibration_mib)
         return 0
 
-    wl = wk.Q8B_LAYER
+    wl = wk.CONFIGS[args.workload]
+    if args.top_c is not None:
+        wl = wl.replace(top_c=args.top_c)
+    if args.window is not None:
+        wl = wl.replace(window=args.window, history_steps=max(wl.history_steps, args.window + 4))
+    headline = wl == wk.Q8B_LAYER  # the counter summary in profiles/ is of this workload
     dims = A.Dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.t_cap, A.KV_BF16)
     cfg = A.Cfg(wl.window, wl.top_c, wl.lam)
     B, Hq, Hkv, D, C = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.top_c
@@ -267,7 +282,7 @@ def main() -> int:
     }
     sk_bytes = score_kernel_bytes(wl, lens_list)
     achieved = sk_bytes / (kern["score_us"] * 1e-6) / 1e9
-    traffic = measured_traffic(SCORE_SOURCES)
+    traffic = measured_traffic(SCORE_SOURCES) if headline else None
     roofline = {"kernel": "score_keys", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "algorithmic_bytes_per_launch": sk_bytes, "avg_launch_us": round(kern["score_us"], 2)}
@@ -284,9 +299,10 @@ def main() -> int:
         "metric": METRIC, "value": round(steps_per_s, 2), "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": "qwen3-8b-layer", "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": D,
+        "config": {"workload": wl.name, "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": D,
                    "context": wl.t_cap, "top_c": C, "window": wl.window, "kv_dtype": "bf16",
-                   "kv_buffers": L, "mode": args.mode},
+                   "kv_buffers": L, "mode": args.mode,
+                   **({"context_range": list(wl.seq_len_range)} if wl.seq_len_range else {})},
         "achieved_GBps": round(nbytes["score_select_attend"] * steps_per_s / 1e9, 1),
         "achieved_GBps_full_step": round(nbytes["full_step"] * steps_per_s / 1e9, 1),
         "bytes_per_step": nbytes,
