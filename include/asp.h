@@ -127,9 +127,15 @@ asp_status asp_predict_query(const asp_dims* dims, const asp_cfg* cfg, const flo
  *   scores[b][g][i] = max over the G query heads h of g of q_pred[b][h] . K[b][g][i]
  * accumulated in fp32 (no 1/sqrt(D): a ranking is scale-free).  Entries at
  * i >= seq_lens[b] are not written.  q_pred[B][Hq][D] fp32,
- * k[B][Hkv][t_cap][D] in dims->kv_dtype, scores[B][Hkv][t_cap] fp32. */
+ * k[B][Hkv][t_cap][D] in dims->kv_dtype, scores[B][Hkv][t_cap] fp32.
+ * hist: NULL, or [B][Hkv][ASP_HIST_BINS] uint32, 16-byte aligned, which the
+ * call overwrites with each unit's coarse histogram: bin j counts the scores
+ * i < seq_lens[b] whose order key (the scores' monotone map to uint32 that
+ * asp_select_topc ranks by) has j as its top 11 bits.  Passing it on to
+ * asp_select_topc saves that call a pass over the scores. */
+#define ASP_HIST_BINS 2048
 asp_status asp_score_keys(const asp_dims* dims, const float* q_pred, const void* k, const int32_t* seq_lens,
-                          float* scores, hipStream_t stream);
+                          float* scores, uint32_t* hist, hipStream_t stream);
 
 /* Exact top-C selection per unit ([card] "Key finding": C = 2k tokens; [summary]
  * "Key results").  C_eff = min(C, seq_lens[b]); the C_eff tokens i < seq_lens[b]
@@ -137,11 +143,16 @@ asp_status asp_score_keys(const asp_dims* dims, const float* q_pred, const void*
  * go to the lower index; NaN ranks as -inf; -0 ties with +0), are written to
  * idx[b][g][0..C_eff) in ascending index order, idx[b][g][C_eff..C) = -1, and
  * n_sel[b][g] = C_eff.  scores[B][Hkv][t_cap] fp32, idx[B][Hkv][C] int32,
- * n_sel[B][Hkv] int32.  ws/ws_bytes: asp_workspace_size(ASP_OP_SELECT) bytes
- * of device scratch (about 4.2 bytes per key slot plus 8 KiB per unit; its
- * contents need no initialisation and are not kept between calls). */
-asp_status asp_select_topc(const asp_dims* dims, const asp_cfg* cfg, const float* scores, const int32_t* seq_lens,
-                           int32_t* idx, int32_t* n_sel, void* ws, size_t ws_bytes, hipStream_t stream);
+ * n_sel[B][Hkv] int32.  hist: NULL, or the coarse histograms of these scores
+ * as asp_score_keys writes them (16-byte aligned); with NULL the call builds
+ * them first.  A histogram that does not match the scores gives an
+ * unspecified selection (never an access outside the arguments).
+ * ws/ws_bytes: asp_workspace_size(ASP_OP_SELECT) bytes of device scratch
+ * (about 4.2 bytes per key slot plus 8 KiB per unit; its contents need no
+ * initialisation and are not kept between calls). */
+asp_status asp_select_topc(const asp_dims* dims, const asp_cfg* cfg, const float* scores, const uint32_t* hist,
+                           const int32_t* seq_lens, int32_t* idx, int32_t* n_sel, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
 
 /* Overlap of two selections per unit, the diagnostic of the temporal locality
  * and prediction recall claims ([card] "What reproduces (and what does not)":

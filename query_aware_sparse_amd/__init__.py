@@ -18,7 +18,7 @@ import torch
 __all__ = [
     "AspError", "Dims", "Cfg", "HipEvent", "library_path", "load",
     "OP_PUSH", "OP_PREDICT", "OP_SCORE", "OP_SELECT", "OP_DECODE", "OP_STEP",
-    "KV_BF16", "KV_F32",
+    "KV_BF16", "KV_F32", "HIST_BINS",
     "asp_workspace_size", "asp_status_string", "asp_push_query", "asp_predict_query", "asp_score_keys",
     "asp_select_topc", "asp_sparse_decode", "asp_step", "asp_selection_overlap", "asp_release_streams",
 ]
@@ -28,6 +28,7 @@ _LIB_PATH = os.path.join(_HERE, "libasp.so")
 
 OP_PUSH, OP_PREDICT, OP_SCORE, OP_SELECT, OP_DECODE, OP_STEP = range(6)
 KV_BF16, KV_F32 = 0, 1
+HIST_BINS = 2048  # bins of the coarse score histograms (ASP_HIST_BINS)
 _STATUS_NAMES = {0: "ASP_OK", 1: "ASP_ERR_INVALID_ARG", 2: "ASP_ERR_UNSUPPORTED", 3: "ASP_ERR_WORKSPACE",
                  4: "ASP_ERR_HIP"}
 
@@ -76,8 +77,8 @@ def load():
     lib.asp_status_string.restype = ctypes.c_char_p
     lib.asp_push_query.argtypes = [D, C, P, P, P, P, P]
     lib.asp_predict_query.argtypes = [D, C, P, P, P, P, P]
-    lib.asp_score_keys.argtypes = [D, P, P, P, P, P]
-    lib.asp_select_topc.argtypes = [D, C, P, P, P, P, P, SZ, P]
+    lib.asp_score_keys.argtypes = [D, P, P, P, P, P, P]
+    lib.asp_select_topc.argtypes = [D, C, P, P, P, P, P, P, SZ, P]
     lib.asp_sparse_decode.argtypes = [D, C, P, P, P, P, P, P, P, SZ, P]
     lib.asp_step.argtypes = [D, C, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P, P, P, P, P]
     lib.asp_selection_overlap.argtypes = [D, C, P, P, P, P, P, P]
@@ -204,27 +205,34 @@ def asp_predict_query(dims: Dims, cfg: Cfg, q_hist, hist_newest, hist_len, q_pre
                                                          _stream_handle(stream)))
 
 
-def asp_score_keys(dims: Dims, q_pred, k, seq_lens, scores, stream=None) -> None:
+def asp_score_keys(dims: Dims, q_pred, k, seq_lens, scores, hist=None, stream=None) -> None:
+    """hist: None, or an int32 [B][Hkv][HIST_BINS] tensor that receives the
+    coarse histograms (a uint32 count per bin, stored in int32)."""
     B, Hq, Hkv, D, T = dims.batch, dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.t_cap
     _check(q_pred, "q_pred", (B, Hq, D), torch.float32)
     _check(k, "k", (B, Hkv, T, D), _kv_dtype(dims))
     _check(seq_lens, "seq_lens", (B,), torch.int32)
     _check(scores, "scores", (B, Hkv, T), torch.float32)
+    if hist is not None:
+        _check(hist, "hist", (B, Hkv, HIST_BINS), torch.int32)
     _raise("asp_score_keys", load().asp_score_keys(ctypes.byref(dims), _ptr(q_pred), _ptr(k), _ptr(seq_lens),
-                                                   _ptr(scores), _stream_handle(stream)))
+                                                   _ptr(scores), _ptr(hist), _stream_handle(stream)))
 
 
-def asp_select_topc(dims: Dims, cfg: Cfg, scores, seq_lens, idx, n_sel, ws=None, stream=None) -> None:
+def asp_select_topc(dims: Dims, cfg: Cfg, scores, seq_lens, idx, n_sel, ws=None, stream=None, hist=None) -> None:
+    """hist: None, or the histograms asp_score_keys wrote for these scores."""
     B, Hkv, T, C = dims.batch, dims.n_kv_heads, dims.t_cap, cfg.top_c
     _check(scores, "scores", (B, Hkv, T), torch.float32)
     _check(seq_lens, "seq_lens", (B,), torch.int32)
     _check(idx, "idx", (B, Hkv, C), torch.int32)
     _check(n_sel, "n_sel", (B, Hkv), torch.int32)
+    if hist is not None:
+        _check(hist, "hist", (B, Hkv, HIST_BINS), torch.int32)
     if ws is None:  # scratch of the selection launches, sized by the library
         ws = torch.empty(asp_workspace_size(dims, cfg, OP_SELECT), dtype=torch.uint8, device=scores.device)
     wp, wb = _ws(ws)
     _raise("asp_select_topc", load().asp_select_topc(ctypes.byref(dims), ctypes.byref(cfg), _ptr(scores),
-                                                     _ptr(seq_lens), _ptr(idx), _ptr(n_sel), wp, wb,
+                                                     _ptr(hist), _ptr(seq_lens), _ptr(idx), _ptr(n_sel), wp, wb,
                                                      _stream_handle(stream)))
 
 

@@ -10,6 +10,8 @@
 
 using asp::Shape;
 
+static_assert(ASP_HIST_BINS == asp::HIST_BINS, "the public histogram size is the kernels'");
+
 namespace {
 
 constexpr int32_t kMaxTCap = 1 << 22;
@@ -219,25 +221,28 @@ asp_status asp_predict_query(const asp_dims* dims, const asp_cfg* cfg, const flo
 }
 
 asp_status asp_score_keys(const asp_dims* dims, const float* q_pred, const void* k, const int32_t* seq_lens,
-                          float* scores, hipStream_t stream) {
+                          float* scores, uint32_t* hist, hipStream_t stream) {
   Shape s;
   asp_status st = check_dims(dims, &s);
   if (st != ASP_OK) return st;
   if (!q_pred || !k || !seq_lens || !scores) return ASP_ERR_INVALID_ARG;
-  if (!aligned16(k) || !aligned4(q_pred) || !aligned4(scores)) return ASP_ERR_INVALID_ARG;
-  return hip_status(asp::launch_score(s, q_pred, k, seq_lens, scores, nullptr, stream));
+  if (!aligned16(k) || !aligned4(q_pred) || !aligned4(scores) || !aligned16(hist)) return ASP_ERR_INVALID_ARG;
+  if (hist != nullptr)  // the score launch adds to the histograms
+    ASP_TRY_HIP(asp::launch_clear_u32(hist, (size_t)s.B * s.Hkv * asp::HIST_BINS, stream));
+  return hip_status(asp::launch_score(s, q_pred, k, seq_lens, scores, hist, stream));
 }
 
-asp_status asp_select_topc(const asp_dims* dims, const asp_cfg* cfg, const float* scores, const int32_t* seq_lens,
-                           int32_t* idx, int32_t* n_sel, void* ws, size_t ws_bytes, hipStream_t stream) {
+asp_status asp_select_topc(const asp_dims* dims, const asp_cfg* cfg, const float* scores, const uint32_t* hist,
+                           const int32_t* seq_lens, int32_t* idx, int32_t* n_sel, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
   Shape s;
   asp_status st = check_all(dims, cfg, &s);
   if (st != ASP_OK) return st;
   if (!scores || !seq_lens || !idx || !n_sel) return ASP_ERR_INVALID_ARG;
-  if (!aligned4(scores)) return ASP_ERR_INVALID_ARG;
+  if (!aligned4(scores) || !aligned16(hist)) return ASP_ERR_INVALID_ARG;
   const size_t need = ws_bytes_for(s, ASP_OP_SELECT);
   if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return ASP_ERR_WORKSPACE;
-  return hip_status(asp::launch_select(s, scores, nullptr, seq_lens, idx, n_sel, nullptr, nullptr, ws, stream));
+  return hip_status(asp::launch_select(s, scores, hist, seq_lens, idx, n_sel, nullptr, nullptr, ws, stream));
 }
 
 asp_status asp_selection_overlap(const asp_dims* dims, const asp_cfg* cfg, const int32_t* idx_a,

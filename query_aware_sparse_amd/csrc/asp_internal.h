@@ -39,6 +39,8 @@ hipError_t launch_predict(const Shape& s, float* q_hist, const int32_t* newest, 
 // must be zero on entry.  `done` (nullable) is recorded when the launch completes.
 hipError_t launch_score(const Shape& s, const float* q_pred, const void* k, const int32_t* seq_lens,
                         float* scores, uint32_t* hist, hipStream_t st, hipEvent_t done = nullptr);
+// Zero fill of n words (a kernel, so that it can also stand in a captured graph).
+hipError_t launch_clear_u32(uint32_t* p, size_t n, hipStream_t st);
 // Top-C selection; hist (nullable) is the coarse histogram built by the score
 // launch (when null, one is built in ws first).  adv_newest/adv_len (nullable)
 // advance the query ring by one slot.  ws: select_ws_bytes(s, hist == nullptr).

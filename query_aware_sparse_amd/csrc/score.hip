@@ -47,6 +47,17 @@ static hipError_t launch_score_dh(const Shape& s, const float* q_pred, const voi
   return e;
 }
 
+__global__ void __launch_bounds__(256) clear_u32_kernel(uint32_t* __restrict__ p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
+}
+
+hipError_t launch_clear_u32(uint32_t* p, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const size_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(clear_u32_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_score(const Shape& s, const float* q_pred, const void* k, const int32_t* seq_lens, float* scores,
                         uint32_t* hist, hipStream_t st, hipEvent_t done) {
   if (s.B == 0) return done ? hipEventRecord(done, st) : hipSuccess;

@@ -84,12 +84,12 @@ BAD_CFG = [
 
 def _call_score(lib, d):
     one = ctypes.c_void_p(16)   # never dereferenced: validation fails first
-    return lib.asp_score_keys(ctypes.byref(d), one, one, one, one, None)
+    return lib.asp_score_keys(ctypes.byref(d), one, one, one, one, None, None)
 
 
 def _call_select(lib, d, c, ws=None, nbytes=0):
     one = ctypes.c_void_p(16)
-    return lib.asp_select_topc(ctypes.byref(d), ctypes.byref(c), one, one, one, one, ws, nbytes, None)
+    return lib.asp_select_topc(ctypes.byref(d), ctypes.byref(c), one, None, one, one, one, ws, nbytes, None)
 
 
 def _call_decode(lib, d, c, ws=None, nbytes=0, null_out=False):
@@ -113,7 +113,13 @@ def test_invalid_cfg_rejected_before_any_launch(lib, cfg, code):
 def test_null_pointers_and_short_workspace_rejected(lib):
     d, c = _dims(), A.Cfg(16, 2048, 1e-2)
     assert lib.asp_score_keys(ctypes.byref(d), None, ctypes.c_void_p(16), ctypes.c_void_p(16),
-                              ctypes.c_void_p(16), None) == 1
+                              ctypes.c_void_p(16), None, None) == 1
+    # a histogram that is not 16-byte aligned
+    assert lib.asp_score_keys(ctypes.byref(d), ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16),
+                              ctypes.c_void_p(16), ctypes.c_void_p(20), None) == 1
+    assert lib.asp_select_topc(ctypes.byref(d), ctypes.byref(c), ctypes.c_void_p(16), ctypes.c_void_p(20),
+                               ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(256),
+                               1 << 40, None) == 1
     assert _call_decode(lib, d, c, ctypes.c_void_p(256), 1 << 30, null_out=True) == 1
     need = A.asp_workspace_size(d, c, A.OP_DECODE)
     assert _call_decode(lib, d, c, None, 0) == 3
@@ -121,7 +127,7 @@ def test_null_pointers_and_short_workspace_rejected(lib):
     assert _call_select(lib, d, c, None, 0) == 3
     assert _call_select(lib, d, c, ctypes.c_void_p(256), need_sel - 1) == 3
     assert _call_decode(lib, d, c, ctypes.c_void_p(256), need - 1) == 3
-    assert lib.asp_score_keys(None, None, None, None, None, None) == 1
+    assert lib.asp_score_keys(None, None, None, None, None, None, None) == 1
     one = ctypes.c_void_p(16)
     # asp_step: idx_cur without n_sel_cur; missing workspace
     args = [ctypes.byref(d), ctypes.byref(c)] + [one] * 7  # q_cur .. seq_lens

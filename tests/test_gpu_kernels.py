@@ -5,6 +5,7 @@ element by element:
   * ring push: bit-exact;
   * predictor: max-abs error within 1e-4 of max|q_pred| per (sequence, head);
   * scores: bit-exact on small-integer inputs, else within 1e-5 * max|score|;
+    the optional coarse histograms count the GPU's own scores exactly;
   * selection: bit-exact index sets on identical fp32 scores;
   * attention: max-abs error 1e-2 on the same index set (fp32 accumulation of
     bf16 inputs; observed errors are ~1e-6).
@@ -136,6 +137,58 @@ def test_score_random_inputs_within_tolerance(kv, G):
         for g in range(Hkv):
             err = np.abs(got[b, g, :T] - ref[b, g, :T]).max()
             assert err <= 1e-5 * np.abs(ref[b, g, :T]).max(), (b, g, err)
+
+
+def _coarse_bins(scores: np.ndarray) -> np.ndarray:
+    """Top 11 bits of the order key of fp32 scores: NaN ranks as -inf, -0 as +0,
+    negative values reversed below the positive ones (the selection's ranking)."""
+    u = scores.astype(np.float32).view(np.uint32).copy()
+    u[np.isnan(scores)] = np.uint32(0xFF800000)
+    u[u == np.uint32(0x80000000)] = np.uint32(0)
+    key = np.where(u >> 31, ~u, u | np.uint32(0x80000000)).astype(np.uint32)
+    return (key >> 21).astype(np.int64)
+
+
+@pytest.mark.parametrize("kv,G", [("bf16", 4), ("bf16", 8), ("f32", 2)])
+def test_score_histogram_counts_the_gpu_scores(kv, G):
+    B, Hkv, D, T_cap = 3, 2, 128, 5003
+    Hq = G * Hkv
+    q, k = _score_inputs(B, Hq, Hkv, D, T_cap, kv, False, seed=11 + G)
+    lens = torch.tensor([T_cap, 1777, 0], dtype=torch.int32)
+    dims = dims_for(A, B, Hq, Hkv, D, T_cap, kv)
+    s_plain = torch.empty((B, Hkv, T_cap), dtype=torch.float32, device=DEV)
+    s_hist = torch.empty_like(s_plain)
+    hist = torch.full((B, Hkv, A.HIST_BINS), 12345, dtype=torch.int32, device=DEV)  # overwritten
+    A.asp_score_keys(dims, q.to(DEV), k.to(DEV), lens.to(DEV), s_plain)
+    A.asp_score_keys(dims, q.to(DEV), k.to(DEV), lens.to(DEV), s_hist, hist=hist)
+    got, h = np_(s_hist), np_(hist)
+    for b in range(B):
+        T = int(lens[b])
+        np.testing.assert_array_equal(got[b, :, :T], np_(s_plain)[b, :, :T])  # same arithmetic
+        for g in range(Hkv):
+            ref = np.bincount(_coarse_bins(got[b, g, :T]), minlength=A.HIST_BINS)
+            np.testing.assert_array_equal(h[b, g], ref)
+
+
+def test_select_with_the_score_histogram():
+    B, Hkv, G, D, T_cap, C = 3, 2, 4, 128, 33000, 2048
+    q, k = _score_inputs(B, G * Hkv, Hkv, D, T_cap, "bf16", False, seed=21)
+    lens = torch.tensor([T_cap, 20001, 1500], dtype=torch.int32, device=DEV)
+    dims = dims_for(A, B, G * Hkv, Hkv, D, T_cap, "bf16")
+    cfg = A.Cfg(16, C, 1e-2)
+    scores = torch.empty((B, Hkv, T_cap), dtype=torch.float32, device=DEV)
+    hist = torch.empty((B, Hkv, A.HIST_BINS), dtype=torch.int32, device=DEV)
+    A.asp_score_keys(dims, q.to(DEV), k.to(DEV), lens, scores, hist=hist)
+    out = []
+    for h in (hist, None):
+        idx = torch.full((B, Hkv, C), -9, dtype=torch.int32, device=DEV)
+        n_sel = torch.full((B, Hkv), -9, dtype=torch.int32, device=DEV)
+        A.asp_select_topc(dims, cfg, scores, lens, idx, n_sel, hist=h)
+        out.append((np_(idx), np_(n_sel)))
+    ri, rn = oracle.select(np_(scores), np_(lens), C)
+    for idx, n_sel in out:
+        np.testing.assert_array_equal(n_sel, rn)
+        np.testing.assert_array_equal(idx, ri)
 
 
 def _select_case(B, Hkv, T_cap, lens, C, seed, kind):
