@@ -30,11 +30,6 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-# The pipelined step keeps four streams busy at once (attention, predictor,
-# score pass, selection) beside the default stream; each needs a hardware
-# queue of its own, or streams that share one run in submission order.  HIP
-# reads this before its first call (its default is 4 queues per process).
-os.environ["GPU_MAX_HW_QUEUES"] = str(max(8, int(os.environ.get("GPU_MAX_HW_QUEUES", "4"))))
 
 METRIC = "sparse decode steps/s + achieved HBM GB/s (score+select+attend), 32k ctx C=2048"
 HBM_PEAK_GBPS = 8000.0
@@ -157,6 +152,11 @@ def main() -> int:
               "(--gpus %d was requested)" % args.gpus, file=sys.stderr)
         return 2
 
+    # The pipelined step keeps four streams busy at once (attention, predictor,
+    # score pass, selection) beside the default stream; each needs a hardware
+    # queue of its own, or streams that share one run in submission order.
+    # HIP reads this at its first call (its default is 4 queues per process).
+    os.environ["GPU_MAX_HW_QUEUES"] = str(max(8, int(os.environ.get("GPU_MAX_HW_QUEUES", "4"))))
     import torch
     import query_aware_sparse_amd as A
     from query_aware_sparse_amd import workload as wk
