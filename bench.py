@@ -46,13 +46,15 @@ def step_bytes(wl, seq_lens) -> dict:
     rows 2*C_eff*D*2, the index write and read 8*C_eff, and the predicted query
     read, actual query read and output write 3*G*D*4.  The full step adds the
     query history read G*W*D*4 and the predicted query write G*D*4 per unit.
-    The transient score rows are excluded.
+    With a newest-token window of r tokens, its K and V rows 2*r*D*2 are added
+    (counted apart from the selection, which may overlap them).  The transient
+    score rows are excluded.
     """
     D, G, C, W, Hkv = wl.head_dim, wl.group, wl.top_c, wl.window, wl.n_kv_heads
     core = 0
     for T in seq_lens:
-        ce = min(C, T)
-        core += Hkv * (T * D * 2 + 2 * ce * D * 2 + 8 * ce + 3 * G * D * 4)
+        ce, r = min(C, T), min(wl.recent, T)
+        core += Hkv * (T * D * 2 + 2 * (ce + r) * D * 2 + 8 * ce + 3 * G * D * 4)
     full = core + wl.batch * Hkv * (G * W * D * 4 + G * D * 4)
     return {"score_select_attend": core, "full_step": full}
 
@@ -142,6 +144,7 @@ def main() -> int:
                     help="one decoder layer of this workload (the headline metric is qwen3-8b-layer)")
     ap.add_argument("--top-c", type=int, default=None, help="override the workload's selection budget C")
     ap.add_argument("--window", type=int, default=None, help="override the workload's ridge window W")
+    ap.add_argument("--recent", type=int, default=0, help="newest tokens attended beside the selection")
     ap.add_argument("--kernel-launches", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -178,9 +181,11 @@ def main() -> int:
         wl = wl.replace(top_c=args.top_c)
     if args.window is not None:
         wl = wl.replace(window=args.window, history_steps=max(wl.history_steps, args.window + 4))
+    if args.recent:
+        wl = wl.replace(recent=args.recent)
     headline = wl == wk.Q8B_LAYER  # the counter summary in profiles/ is of this workload
     dims = A.Dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.t_cap, A.KV_BF16)
-    cfg = A.Cfg(wl.window, wl.top_c, wl.lam)
+    cfg = A.Cfg(wl.window, wl.top_c, wl.lam, wl.recent)
     B, Hq, Hkv, D, C = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.top_c
     L = args.kv_buffers
     n_layer_steps = (args.warmup + args.steps) // L + 2
@@ -277,7 +282,8 @@ def main() -> int:
         "select_us": time_entry(lambda i: A.asp_select_topc(dims, cfg, scores, layers[0]["seq_lens"], idx_t, nsel_t,
                                                             stream=attn), n),
         "attend_us": time_entry(lambda i: A.asp_sparse_decode(dims, cfg, layers[i % L]["qs"][0], layers[i % L]["k"],
-                                                              layers[i % L]["v"], layers[i % L]["idx"][0],
+                                                              layers[i % L]["v"], layers[i % L]["seq_lens"],
+                                                              layers[i % L]["idx"][0],
                                                               layers[i % L]["nsel"][0], out, ws_dec, stream=attn), n),
     }
     sk_bytes = score_kernel_bytes(wl, lens_list)
@@ -300,7 +306,7 @@ def main() -> int:
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": D,
-                   "context": wl.t_cap, "top_c": C, "window": wl.window, "kv_dtype": "bf16",
+                   "context": wl.t_cap, "top_c": C, "window": wl.window, "recent": wl.recent, "kv_dtype": "bf16",
                    "kv_buffers": L, "mode": args.mode,
                    **({"context_range": list(wl.seq_len_range)} if wl.seq_len_range else {})},
         "achieved_GBps": round(nbytes["score_select_attend"] * steps_per_s / 1e9, 1),

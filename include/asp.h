@@ -69,13 +69,16 @@ typedef struct {
 } asp_dims;
 
 /* Method configuration.  window W: ring length, a multiple of 4 in [4, 64];
- * top_c C: tokens kept per unit, 1 <= C <= t_cap (and C <= 256 attention
- * blocks: 32768 for bf16 and head_dim 128, else ASP_ERR_UNSUPPORTED);
- * lambda: ridge penalty, finite and > 0. */
+ * top_c C: tokens kept per unit, 1 <= C <= t_cap; lambda: ridge penalty,
+ * finite and > 0; recent R: the attention also attends each sequence's
+ * newest R tokens [seq_len - R, seq_len) beside the selection (0 = off;
+ * 0 <= R <= t_cap).  C + R may span at most 256 attention blocks (32768
+ * tokens for bf16 and head_dim 128), else ASP_ERR_UNSUPPORTED. */
 typedef struct {
   int32_t window;
   int32_t top_c;
   double lambda;
+  int32_t recent;
 } asp_cfg;
 
 typedef enum {
@@ -170,23 +173,28 @@ asp_status asp_selection_overlap(const asp_dims* dims, const asp_cfg* cfg, const
 
 /* Sparse decode attention over the selected tokens ([card] "Layout" and "Key
  * finding": attention over the top-C tokens only).  For every (b, h), with
- * g = h / G and S = idx[b][g][0..n_sel[b][g]):
+ * g = h / G, n = n_sel[b][g] clamped to [0, C], T = seq_lens[b] clamped to
+ * [0, t_cap] and r = min(cfg->recent, T), the attended list S holds the
+ * entries idx[b][g][j], j < n, that lie in [0, t_cap) and outside [T - r, T)
+ * (as listed: asp_select_topc writes distinct ones), then every token of
+ * [T - r, T) once:
  *   out[b][h] = sum_{i in S} exp(s_i - m) V[b][g][i] / sum_{i in S} exp(s_i - m),
  *   s_i = q[b][h] . K[b][g][i] / sqrt(D), m = max s_i;
- * out = 0 when S is empty.  Accumulation is fp32 (online softmax over
- * split-K partials merged by log-sum-exp).  q[B][Hq][D] fp32, k/v
- * [B][Hkv][t_cap][D] in dims->kv_dtype, out[B][Hq][D] fp32.
- * ws/ws_bytes: asp_workspace_size(ASP_OP_DECODE) bytes. */
+ * out = 0 when S is empty.  Accumulation is fp32 (online softmax over split-K partials merged
+ * by log-sum-exp).  q[B][Hq][D] fp32, k/v [B][Hkv][t_cap][D] in
+ * dims->kv_dtype, seq_lens[B] int32 (may be NULL when cfg->recent is 0),
+ * out[B][Hq][D] fp32.  ws/ws_bytes: asp_workspace_size(ASP_OP_DECODE) bytes. */
 asp_status asp_sparse_decode(const asp_dims* dims, const asp_cfg* cfg, const float* q, const void* k, const void* v,
-                             const int32_t* idx, const int32_t* n_sel, float* out, void* ws, size_t ws_bytes,
-                             hipStream_t stream);
+                             const int32_t* seq_lens, const int32_t* idx, const int32_t* n_sel, float* out, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
 
 /* One decode step of one layer ([abstract], second component; [summary]
  * "Approach": selection for the next step is taken off the decode critical
  * path and overlapped with the current step's attention).
  *
  * Pipelined mode (idx_cur != NULL): attention with the actual query q_cur over
- * the selection idx_cur/n_sel_cur (made by the previous step) writes out; and,
+ * the selection idx_cur/n_sel_cur (made by the previous step) and, with
+ * cfg->recent > 0, the newest tokens (as asp_sparse_decode) writes out; and,
  * independently, q_cur is pushed into the ring, the next query is predicted,
  * keys are scored and the next step's selection is written to
  * idx_next/n_sel_next.

@@ -178,6 +178,34 @@ def attend(q, k, v, idx, n_sel):
     return out
 
 
+def attend_with_recent(q, k, v, idx, n_sel, seq_lens, recent: int):
+    """Attention over each unit's selection and its sequence's newest `recent`
+    tokens: the entries idx[j], j < n, with 0 <= idx[j] < T_cap and outside
+    [T - r, T) (as listed), followed by every token of [T - r, T) once;
+    n = n_sel clamped to [0, C], T = seq_len clamped to [0, T_cap],
+    r = min(recent, T).  The pages do not treat tokens newer than the
+    selection; this is the library's optional newest-token window, written as
+    the list of attended tokens followed by attend()."""
+    B, Hkv, T_cap = np.shape(k)[:3]
+    idx = np.asarray(idx, np.int32)
+    n_sel = np.asarray(n_sel, np.int32)
+    lens = np.asarray(seq_lens, np.int32)
+    C = idx.shape[2]
+    width = C + max(int(recent), 0)
+    u_idx = np.full((B, Hkv, max(width, 1)), -1, np.int32)
+    u_n = np.zeros((B, Hkv), np.int32)
+    for b in range(B):
+        T = min(max(int(lens[b]), 0), T_cap)
+        r = min(max(int(recent), 0), T)
+        for g in range(Hkv):
+            n = min(max(int(n_sel[b, g]), 0), C)
+            sel = [int(x) for x in idx[b, g, :n] if 0 <= x < T_cap and not (T - r <= x < T)]
+            tokens = sel + list(range(T - r, T))
+            u_idx[b, g, :len(tokens)] = tokens
+            u_n[b, g] = len(tokens)
+    return attend(q, k, v, u_idx, u_n)
+
+
 def overlap(idx_a, n_a, idx_b, n_b, T_cap: int):
     """Per unit, the number of distinct indices in [0, T_cap) present in both
     selections (idx_*[..., C] int32, n_*[...] int32, leading dims = units) --

@@ -50,8 +50,10 @@ class Dims(ctypes.Structure):
 
 
 class Cfg(ctypes.Structure):
-    """asp_cfg: window (ring length W), top_c (C), lam (ridge lambda)."""
-    _fields_ = [("window", ctypes.c_int32), ("top_c", ctypes.c_int32), ("lam", ctypes.c_double)]
+    """asp_cfg: window (ring length W), top_c (C), lam (ridge lambda), recent
+    (newest tokens attended beside the selection; 0 by default)."""
+    _fields_ = [("window", ctypes.c_int32), ("top_c", ctypes.c_int32), ("lam", ctypes.c_double),
+                ("recent", ctypes.c_int32)]
 
 
 _lib = None
@@ -79,7 +81,7 @@ def load():
     lib.asp_predict_query.argtypes = [D, C, P, P, P, P, P]
     lib.asp_score_keys.argtypes = [D, P, P, P, P, P, P]
     lib.asp_select_topc.argtypes = [D, C, P, P, P, P, P, P, SZ, P]
-    lib.asp_sparse_decode.argtypes = [D, C, P, P, P, P, P, P, P, SZ, P]
+    lib.asp_sparse_decode.argtypes = [D, C, P, P, P, P, P, P, P, P, SZ, P]
     lib.asp_step.argtypes = [D, C, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P, P, P, P, P]
     lib.asp_selection_overlap.argtypes = [D, C, P, P, P, P, P, P]
     lib.asp_release_streams.argtypes = []
@@ -247,17 +249,21 @@ def asp_selection_overlap(dims: Dims, cfg: Cfg, idx_a, n_sel_a, idx_b, n_sel_b, 
                                                                  _ptr(overlap), _stream_handle(stream)))
 
 
-def asp_sparse_decode(dims: Dims, cfg: Cfg, q, k, v, idx, n_sel, out, ws, stream=None) -> None:
+def asp_sparse_decode(dims: Dims, cfg: Cfg, q, k, v, seq_lens, idx, n_sel, out, ws, stream=None) -> None:
+    """seq_lens may be None when cfg.recent is 0."""
     B, Hq, Hkv, D, T, C = dims.batch, dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.t_cap, cfg.top_c
     _check(q, "q", (B, Hq, D), torch.float32)
     _check(k, "k", (B, Hkv, T, D), _kv_dtype(dims))
     _check(v, "v", (B, Hkv, T, D), _kv_dtype(dims))
+    if seq_lens is not None:
+        _check(seq_lens, "seq_lens", (B,), torch.int32)
     _check(idx, "idx", (B, Hkv, C), torch.int32)
     _check(n_sel, "n_sel", (B, Hkv), torch.int32)
     _check(out, "out", (B, Hq, D), torch.float32)
     wp, wb = _ws(ws)
     _raise("asp_sparse_decode", load().asp_sparse_decode(ctypes.byref(dims), ctypes.byref(cfg), _ptr(q), _ptr(k),
-                                                         _ptr(v), _ptr(idx), _ptr(n_sel), _ptr(out), wp, wb,
+                                                         _ptr(v), _ptr(seq_lens), _ptr(idx), _ptr(n_sel), _ptr(out),
+                                                         wp, wb,
                                                          _stream_handle(stream)))
 
 

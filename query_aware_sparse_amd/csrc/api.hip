@@ -42,6 +42,7 @@ asp_status check_dims(const asp_dims* d, Shape* s) {
   s->W = 0;
   s->C = 0;
   s->lambda = 0.0;
+  s->R = 0;
   return ASP_OK;
 }
 
@@ -50,11 +51,14 @@ asp_status check_cfg(const asp_cfg* c, Shape* s) {
   if (c->window < 4 || c->window > 64 || c->window % 4 != 0) return ASP_ERR_INVALID_ARG;
   if (c->top_c < 1 || c->top_c > s->T_cap) return ASP_ERR_INVALID_ARG;
   if (!(c->lambda > 0.0) || !isfinite(c->lambda)) return ASP_ERR_INVALID_ARG;
-  if ((c->top_c + asp::attend_tokens_per_block(s->D, s->kv) - 1) / asp::attend_tokens_per_block(s->D, s->kv) > 256)
+  if (c->recent < 0 || c->recent > s->T_cap) return ASP_ERR_INVALID_ARG;
+  const int tpb = asp::attend_tokens_per_block(s->D, s->kv);
+  if (((int64_t)c->top_c + c->recent + tpb - 1) / tpb > 256)
     return ASP_ERR_UNSUPPORTED;  // more attention splits than the merge handles
   s->W = c->window;
   s->C = c->top_c;
   s->lambda = c->lambda;
+  s->R = c->recent;
   return ASP_OK;
 }
 
@@ -259,16 +263,17 @@ asp_status asp_selection_overlap(const asp_dims* dims, const asp_cfg* cfg, const
 }
 
 asp_status asp_sparse_decode(const asp_dims* dims, const asp_cfg* cfg, const float* q, const void* k, const void* v,
-                             const int32_t* idx, const int32_t* n_sel, float* out, void* ws, size_t ws_bytes,
-                             hipStream_t stream) {
+                             const int32_t* seq_lens, const int32_t* idx, const int32_t* n_sel, float* out, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
   Shape s;
   asp_status st = check_all(dims, cfg, &s);
   if (st != ASP_OK) return st;
   if (!q || !k || !v || !idx || !n_sel || !out) return ASP_ERR_INVALID_ARG;
+  if (s.R > 0 && seq_lens == nullptr) return ASP_ERR_INVALID_ARG;
   if (!aligned16(k) || !aligned16(v) || !aligned4(q) || !aligned4(out)) return ASP_ERR_INVALID_ARG;
   const size_t need = ws_bytes_for(s, ASP_OP_DECODE);
   if (ws == nullptr || ws_bytes < need) return ASP_ERR_WORKSPACE;
-  return hip_status(asp::launch_attend(s, q, k, v, idx, n_sel, out, ws, stream));
+  return hip_status(asp::launch_attend(s, q, k, v, seq_lens, idx, n_sel, out, ws, stream));
 }
 
 asp_status asp_step(const asp_dims* dims, const asp_cfg* cfg, const float* q_cur, float* q_hist,
@@ -306,12 +311,12 @@ asp_status asp_step(const asp_dims* dims, const asp_cfg* cfg, const float* q_cur
     st = run_selection(s, q_cur, q_hist, hist_newest, hist_len, k, seq_lens, idx_next, n_sel_next, q_pred, scores,
                        hist, sel_ws, attn_stream);
     if (st != ASP_OK) return st;
-    ASP_TRY_HIP(asp::launch_attend(s, q_cur, k, v, idx_next, n_sel_next, out, partials, attn_stream));
+    ASP_TRY_HIP(asp::launch_attend(s, q_cur, k, v, seq_lens, idx_next, n_sel_next, out, partials, attn_stream));
     if (idx_next_ready) ASP_TRY_HIP(hipEventRecord(idx_next_ready, attn_stream));
     return ASP_OK;
   }
   if (!two_streams) {
-    ASP_TRY_HIP(asp::launch_attend(s, q_cur, k, v, idx_cur, n_sel_cur, out, partials, attn_stream));
+    ASP_TRY_HIP(asp::launch_attend(s, q_cur, k, v, seq_lens, idx_cur, n_sel_cur, out, partials, attn_stream));
     ASP_TRY_HIP(asp::launch_predict(s, q_hist, hist_newest, hist_len, q_cur, q_pred, hist, attn_stream));
     ASP_TRY_HIP(asp::launch_score(s, q_pred, k, seq_lens, scores, hist, attn_stream));
     ASP_TRY_HIP(asp::launch_select(s, scores, hist, seq_lens, idx_next, n_sel_next, hist_newest, hist_len, sel_ws,
@@ -346,7 +351,7 @@ asp_status asp_step(const asp_dims* dims, const asp_cfg* cfg, const float* q_cur
   ASP_TRY_HIP(asp::launch_select(s, scores, hist, seq_lens, idx_next, n_sel_next, hist_newest, hist_len, sel_ws,
                                  sel_stream, idx_next_ready));
   ASP_TRY_HIP(hipStreamWaitEvent(attn_stream, idx_cur_ready, 0));
-  ASP_TRY_HIP(asp::launch_attend(s, q_cur, k, v, idx_cur, n_sel_cur, out, partials, attn_stream));
+  ASP_TRY_HIP(asp::launch_attend(s, q_cur, k, v, seq_lens, idx_cur, n_sel_cur, out, partials, attn_stream));
   return ASP_OK;
 }
 

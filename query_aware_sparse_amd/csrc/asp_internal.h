@@ -14,6 +14,7 @@ struct Shape {
   int B, Hq, Hkv, G, D, T_cap, kv;  // kv: 0 = bf16, 1 = fp32
   int W, C;
   double lambda;
+  int R;  // newest tokens attended beside the selection
 };
 
 // Attention split size: tokens handled by one workgroup of the split-K
@@ -53,14 +54,17 @@ hipError_t launch_select(const Shape& s, const float* scores, const uint32_t* hi
 int overlap_max_c();
 hipError_t launch_overlap(const Shape& s, const int32_t* idx_a, const int32_t* n_a, const int32_t* idx_b,
                           const int32_t* n_b, int32_t* out, hipStream_t st);
-// Sparse attention: split-K partials into `partials`, then the merge into out.
-// adv_newest/adv_len (nullable): the merge launch advances the query ring.
-hipError_t launch_attend(const Shape& s, const float* q, const void* k, const void* v, const int32_t* idx,
-                         const int32_t* n_sel, float* out, void* partials, hipStream_t st,
+// Sparse attention over the selection and the newest s.R tokens: split-K
+// partials into `partials`, then the merge into out.  seq_lens may be null
+// when s.R == 0.  adv_newest/adv_len (nullable): the merge launch advances the
+// query ring.
+hipError_t launch_attend(const Shape& s, const float* q, const void* k, const void* v, const int32_t* seq_lens,
+                         const int32_t* idx, const int32_t* n_sel, float* out, void* partials, hipStream_t st,
                          int32_t* adv_newest = nullptr, int32_t* adv_len = nullptr);
 // The merge alone (partials written by the attention blocks).
-hipError_t launch_merge(const Shape& s, const int32_t* n_sel, float* out, const void* partials, hipStream_t st,
-                        int32_t* adv_newest = nullptr, int32_t* adv_len = nullptr);
+hipError_t launch_merge(const Shape& s, const int32_t* seq_lens, const int32_t* n_sel, float* out,
+                        const void* partials, hipStream_t st, int32_t* adv_newest = nullptr,
+                        int32_t* adv_len = nullptr);
 
 // Whether `st` is being captured into a graph.
 inline bool capturing(hipStream_t st) {

@@ -12,7 +12,7 @@ int attend_tokens_per_block(int D, int kv) {
 
 int attend_num_splits(const Shape& s) {
   const int tpb = attend_tokens_per_block(s.D, s.kv);
-  return (s.C + tpb - 1) / tpb;
+  return (s.C + s.R + tpb - 1) / tpb;
 }
 
 size_t attend_partials_bytes(const Shape& s) {
@@ -20,17 +20,18 @@ size_t attend_partials_bytes(const Shape& s) {
   return units * attend_num_splits(s) * s.G * (s.D + 2) * sizeof(float);
 }
 
-template <typename KV, int D, int G>
+template <typename KV, int D, int G, bool RECENT>
 __global__ void __launch_bounds__(ATT_THREADS) attend_kernel(const float* __restrict__ q, const KV* __restrict__ k,
                                                              const KV* __restrict__ v,
+                                                             const int32_t* __restrict__ seq_lens,
                                                              const int32_t* __restrict__ idx,
                                                              const int32_t* __restrict__ n_sel,
                                                              float* __restrict__ part_acc,
                                                              float* __restrict__ part_ml, int Hq, int Hkv, int T_cap,
-                                                             int C, int nsplit) {
+                                                             int C, int R, int nsplit) {
   __shared__ __align__(16) unsigned char smem[attend_lds_bytes<D, G>()];
-  attend_block<KV, D, G>(q, k, v, idx, n_sel, part_acc, part_ml, Hq, Hkv, T_cap, C, nsplit, blockIdx.x, blockIdx.y,
-                         smem);
+  attend_block<KV, D, G, RECENT>(q, k, v, seq_lens, idx, n_sel, part_acc, part_ml, Hq, Hkv, T_cap, C, R, nsplit,
+                                 blockIdx.x, blockIdx.y, smem);
 }
 
 // One workgroup per (sequence, query head): log-sum-exp merge of the partials.
@@ -42,8 +43,10 @@ constexpr int MERGE_MAX_SPLITS = 256;
 
 __global__ void __launch_bounds__(128) merge_kernel(const float* __restrict__ part_acc,
                                                     const float* __restrict__ part_ml,
+                                                    const int32_t* __restrict__ seq_lens,
                                                     const int32_t* __restrict__ n_sel, float* __restrict__ out,
-                                                    int Hq, int Hkv, int G, int D, int C, int nsplit, int tpb,
+                                                    int Hq, int Hkv, int G, int D, int T_cap, int C, int R,
+                                                    int nsplit, int tpb,
                                                     int32_t* __restrict__ adv_newest, int32_t* __restrict__ adv_len,
                                                     int W) {
   constexpr int PER = MERGE_MAX_SPLITS / 64;
@@ -56,8 +59,8 @@ __global__ void __launch_bounds__(128) merge_kernel(const float* __restrict__ pa
   if (adv_newest != nullptr && h == 0 && threadIdx.x == 0) ring_advance(adv_newest, adv_len, b, W);
   const int g = h / G, hh = h % G;
   const int unit = b * Hkv + g;
-  const int n = clampi(n_sel[unit], 0, C);
-  const int ns = min((n + tpb - 1) / tpb, MERGE_MAX_SPLITS);
+  const AttendList al = attend_list(n_sel, seq_lens, unit, Hkv, C, R, T_cap);
+  const int ns = min((al.n + al.r + tpb - 1) / tpb, MERGE_MAX_SPLITS);
   const int t = threadIdx.x;
   if (t < 64) {
     float m[PER], l[PER];
@@ -99,15 +102,22 @@ __global__ void __launch_bounds__(128) merge_kernel(const float* __restrict__ pa
 }
 
 template <typename KV, int D>
-static hipError_t launch_attend_d(const Shape& s, const float* q, const void* k, const void* v, const int32_t* idx,
-                                  const int32_t* n_sel, float* part_acc, float* part_ml, hipStream_t st) {
+static hipError_t launch_attend_d(const Shape& s, const float* q, const void* k, const void* v,
+                                  const int32_t* seq_lens, const int32_t* idx, const int32_t* n_sel, float* part_acc,
+                                  float* part_ml, hipStream_t st) {
   const int nsplit = attend_num_splits(s);
   const dim3 grid(nsplit, s.B * s.Hkv);
   const KV* kk = static_cast<const KV*>(k);
   const KV* vv = static_cast<const KV*>(v);
-#define ASP_ATT_LAUNCH(GG)                                                                                   \
-  hipLaunchKernelGGL((attend_kernel<KV, D, GG>), grid, dim3(ATT_THREADS), 0, st, q, kk, vv, idx, n_sel, part_acc, \
-                     part_ml, s.Hq, s.Hkv, s.T_cap, s.C, nsplit)
+#define ASP_ATT_LAUNCH(GG)                                                                                     \
+  do {                                                                                                             \
+    if (s.R > 0)                                                                                                   \
+      hipLaunchKernelGGL((attend_kernel<KV, D, GG, true>), grid, dim3(ATT_THREADS), 0, st, q, kk, vv, seq_lens,     \
+                         idx, n_sel, part_acc, part_ml, s.Hq, s.Hkv, s.T_cap, s.C, s.R, nsplit);                    \
+    else                                                                                                           \
+      hipLaunchKernelGGL((attend_kernel<KV, D, GG, false>), grid, dim3(ATT_THREADS), 0, st, q, kk, vv, seq_lens,    \
+                         idx, n_sel, part_acc, part_ml, s.Hq, s.Hkv, s.T_cap, s.C, 0, nsplit);                      \
+  } while (0)
   switch (s.G) {
     case 1: ASP_ATT_LAUNCH(1); break;
     case 2: ASP_ATT_LAUNCH(2); break;
@@ -119,33 +129,33 @@ static hipError_t launch_attend_d(const Shape& s, const float* q, const void* k,
   return hipGetLastError();
 }
 
-hipError_t launch_attend(const Shape& s, const float* q, const void* k, const void* v, const int32_t* idx,
-                         const int32_t* n_sel, float* out, void* partials, hipStream_t st, int32_t* adv_newest,
-                         int32_t* adv_len) {
+hipError_t launch_attend(const Shape& s, const float* q, const void* k, const void* v, const int32_t* seq_lens,
+                         const int32_t* idx, const int32_t* n_sel, float* out, void* partials, hipStream_t st,
+                         int32_t* adv_newest, int32_t* adv_len) {
   if (s.B == 0) return hipSuccess;
   const int nsplit = attend_num_splits(s);
   float* part_acc = static_cast<float*>(partials);
   float* part_ml = part_acc + (size_t)s.B * s.Hkv * nsplit * s.G * s.D;
   hipError_t e;
   if (s.kv == 0)
-    e = s.D == 64 ? launch_attend_d<uint16_t, 64>(s, q, k, v, idx, n_sel, part_acc, part_ml, st)
-                  : launch_attend_d<uint16_t, 128>(s, q, k, v, idx, n_sel, part_acc, part_ml, st);
+    e = s.D == 64 ? launch_attend_d<uint16_t, 64>(s, q, k, v, seq_lens, idx, n_sel, part_acc, part_ml, st)
+                  : launch_attend_d<uint16_t, 128>(s, q, k, v, seq_lens, idx, n_sel, part_acc, part_ml, st);
   else
-    e = s.D == 64 ? launch_attend_d<float, 64>(s, q, k, v, idx, n_sel, part_acc, part_ml, st)
-                  : launch_attend_d<float, 128>(s, q, k, v, idx, n_sel, part_acc, part_ml, st);
+    e = s.D == 64 ? launch_attend_d<float, 64>(s, q, k, v, seq_lens, idx, n_sel, part_acc, part_ml, st)
+                  : launch_attend_d<float, 128>(s, q, k, v, seq_lens, idx, n_sel, part_acc, part_ml, st);
   if (e != hipSuccess) return e;
-  return launch_merge(s, n_sel, out, partials, st, adv_newest, adv_len);
+  return launch_merge(s, seq_lens, n_sel, out, partials, st, adv_newest, adv_len);
 }
 
-hipError_t launch_merge(const Shape& s, const int32_t* n_sel, float* out, const void* partials, hipStream_t st,
-                        int32_t* adv_newest, int32_t* adv_len) {
+hipError_t launch_merge(const Shape& s, const int32_t* seq_lens, const int32_t* n_sel, float* out,
+                        const void* partials, hipStream_t st, int32_t* adv_newest, int32_t* adv_len) {
   if (s.B == 0) return hipSuccess;
   const int nsplit = attend_num_splits(s);
   const float* part_acc = static_cast<const float*>(partials);
   const float* part_ml = part_acc + (size_t)s.B * s.Hkv * nsplit * s.G * s.D;
-  hipLaunchKernelGGL(merge_kernel, dim3(s.B * s.Hq), dim3(128), 0, st, part_acc, part_ml, n_sel, out, s.Hq, s.Hkv,
-                     s.G, s.D, s.C, nsplit, attend_tokens_per_block(s.D, s.kv), adv_newest, adv_len,
-                     s.W > 0 ? s.W : 1);
+  hipLaunchKernelGGL(merge_kernel, dim3(s.B * s.Hq), dim3(128), 0, st, part_acc, part_ml, seq_lens, n_sel, out,
+                     s.Hq, s.Hkv, s.G, s.D, s.T_cap, s.C, s.R, nsplit, attend_tokens_per_block(s.D, s.kv),
+                     adv_newest, adv_len, s.W > 0 ? s.W : 1);
   return hipGetLastError();
 }
 

@@ -7,7 +7,9 @@
 // "Key finding" (the method attends to the C selected tokens only); research-map
 // summary of AsyncSpade, "Approach" (the selection is consumed by the inference
 // step).  Reading taken: the attention query is the actual current query, the
-// prediction only chooses the tokens.
+// prediction only chooses the tokens.  Optionally the newest R tokens of each
+// sequence are attended beside the selection (a selected index among them
+// counts once); the pages are silent on tokens newer than the selection.
 //
 // Grid: (split, unit).  A workgroup of 4 wavefronts gathers up to
 // 4 * 8 * KPW selected K and V rows of one unit (each row read once and used by
@@ -44,13 +46,32 @@ constexpr size_t attend_lds_bytes() {
   return (size_t)ATT_WAVES * G * (D + 2) * sizeof(float);
 }
 
+// Token list of a unit: its n selected entries, then the newest r tokens
+// [lo, lo + r) of the sequence (r = min(R, seq_len); none when R == 0).
+struct AttendList {
+  int n, r, lo;
+};
+__device__ __forceinline__ AttendList attend_list(const int32_t* __restrict__ n_sel,
+                                                  const int32_t* __restrict__ seq_lens, int unit, int Hkv, int C,
+                                                  int R, int T_cap) {
+  AttendList a;
+  a.n = clampi(n_sel[unit], 0, C);
+  const int T = R > 0 ? clampi(seq_lens[unit / Hkv], 0, T_cap) : 0;
+  a.r = min(R, T);
+  a.lo = T - a.r;
+  return a;
+}
+
 // Attention block (split, unit); smem holds attend_lds_bytes<D, G>().
-template <typename KV, int D, int G>
+// RECENT: the newest-token window is on (R > 0); without it the token list is
+// the selection alone.
+template <typename KV, int D, int G, bool RECENT>
 __device__ __forceinline__ void attend_block(const float* __restrict__ q, const KV* __restrict__ k,
-                                             const KV* __restrict__ v, const int32_t* __restrict__ idx,
-                                             const int32_t* __restrict__ n_sel, float* __restrict__ part_acc,
-                                             float* __restrict__ part_ml, int Hq, int Hkv, int T_cap, int C,
-                                             int nsplit, int split, int unit, unsigned char* smem) {
+                                             const KV* __restrict__ v, const int32_t* __restrict__ seq_lens,
+                                             const int32_t* __restrict__ idx, const int32_t* __restrict__ n_sel,
+                                             float* __restrict__ part_acc, float* __restrict__ part_ml, int Hq,
+                                             int Hkv, int T_cap, int C, int R, int nsplit, int split, int unit,
+                                             unsigned char* smem) {
   constexpr int EPL = 16 / (int)sizeof(KV);
   constexpr int LPK = D / EPL;
   constexpr int KPW = 64 / LPK;
@@ -61,9 +82,9 @@ __device__ __forceinline__ void attend_block(const float* __restrict__ q, const 
   float (*sm_acc)[G][D] = reinterpret_cast<float (*)[G][D]>(smem + (size_t)2 * ATT_WAVES * G * sizeof(float));
 
   const int b = unit / Hkv, g = unit % Hkv;
-  const int n = clampi(n_sel[unit], 0, C);
+  const AttendList al = attend_list(n_sel, seq_lens, unit, Hkv, C, RECENT ? R : 0, T_cap);
   const int tok0 = split * TPB;
-  if (tok0 >= n) return;
+  if (tok0 >= al.n + al.r) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane % LPK, kl = lane / LPK;
 
@@ -84,8 +105,21 @@ __device__ __forceinline__ void attend_block(const float* __restrict__ q, const 
 #pragma unroll
   for (int i = 0; i < ATT_NL; ++i) {
     const int t = tok0 + wave * TPW + i * KPW + kl;
-    const int id = t < n ? ib[t] : -1;
-    ok[i] = id >= 0 && id < T_cap;
+    int id = -1;
+    bool in_list = false;
+    if constexpr (RECENT) {
+      if (t < al.n) {  // a selected entry inside the recent range is attended there
+        id = ib[t];
+        in_list = id >= 0 && id < T_cap && !(id >= al.lo && id < al.lo + al.r);
+      } else if (t < al.n + al.r) {
+        id = al.lo + (t - al.n);
+        in_list = true;
+      }
+    } else {
+      id = t < al.n ? ib[t] : -1;
+      in_list = id >= 0 && id < T_cap;
+    }
+    ok[i] = in_list;
     tk[i] = ok[i] ? id : 0;
   }
   const KV* kb = k + (size_t)unit * T_cap * D + sub * EPL;

@@ -49,6 +49,7 @@ class Workload:
     heavy_factor: float = 3.0
     seq_len_range: Optional[Tuple[int, int]] = None  # ragged lengths, inclusive
     history_steps: int = 0             # queries drawn before the first decode step
+    recent: int = 0                    # newest tokens attended beside the selection (asp_cfg.recent)
     ar_a: float = 0.9
     ar_sigma: float = 0.3
     seed: int = 0

@@ -79,6 +79,8 @@ BAD_CFG = [
     (A.Cfg(6, 64, 1e-2), 1), (A.Cfg(0, 64, 1e-2), 1), (A.Cfg(68, 64, 1e-2), 1), (A.Cfg(16, 0, 1e-2), 1),
     (A.Cfg(16, 40000, 1e-2), 1), (A.Cfg(16, 64, 0.0), 1), (A.Cfg(16, 64, -1.0), 1),
     (A.Cfg(16, 64, float("nan")), 1), (A.Cfg(16, 64, float("inf")), 1),
+    (A.Cfg(16, 64, 1e-2, -1), 1), (A.Cfg(16, 64, 1e-2, 40000), 1),
+    (A.Cfg(16, 32768, 1e-2, 128), 2),   # C + R past 256 attention splits (128 tokens each here)
 ]
 
 
@@ -94,7 +96,7 @@ def _call_select(lib, d, c, ws=None, nbytes=0):
 
 def _call_decode(lib, d, c, ws=None, nbytes=0, null_out=False):
     one = ctypes.c_void_p(16)
-    return lib.asp_sparse_decode(ctypes.byref(d), ctypes.byref(c), one, one, one, one, one,
+    return lib.asp_sparse_decode(ctypes.byref(d), ctypes.byref(c), one, one, one, None, one, one,
                                  None if null_out else one, ws, nbytes, None)
 
 
@@ -121,6 +123,8 @@ def test_null_pointers_and_short_workspace_rejected(lib):
                                ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(256),
                                1 << 40, None) == 1
     assert _call_decode(lib, d, c, ctypes.c_void_p(256), 1 << 30, null_out=True) == 1
+    # recent tokens need the sequence lengths
+    assert _call_decode(lib, d, A.Cfg(16, 2048, 1e-2, 16), ctypes.c_void_p(256), 1 << 40) == 1
     need = A.asp_workspace_size(d, c, A.OP_DECODE)
     assert _call_decode(lib, d, c, None, 0) == 3
     need_sel = A.asp_workspace_size(d, c, A.OP_SELECT)

@@ -51,7 +51,7 @@ def _full_shape_check(p: Problem, units):
     ring1 = _ring(p)
     idx0, n0 = p.idx.clone(), p.n_sel.clone()
     # The next step through the entry points (reference for the pipelined step).
-    A.asp_sparse_decode(d, c, q1.to(DEV), p.k, p.v, idx0, n0, p.out, p.ws_dec)
+    A.asp_sparse_decode(d, c, q1.to(DEV), p.k, p.v, p.seq_lens, idx0, n0, p.out, p.ws_dec)
     A.asp_push_query(d, c, q1.to(DEV), p.q_hist, p.newest, p.length)
     A.asp_predict_query(d, c, p.q_hist, p.newest, p.length, p.q_pred)
     A.asp_score_keys(d, p.q_pred, p.k, p.seq_lens, p.scores)

@@ -8,7 +8,7 @@ element by element:
     the optional coarse histograms count the GPU's own scores exactly;
   * selection: bit-exact index sets on identical fp32 scores;
   * attention: max-abs error 1e-2 on the same index set (fp32 accumulation of
-    bf16 inputs; observed errors are ~1e-6).
+    bf16 inputs; observed errors are ~1e-6), also with the newest-token window.
 Sizes span several workgroup tiles and a ragged tail.
 """
 import numpy as np
@@ -255,7 +255,7 @@ def test_select_all_equal_and_c_equals_t():
         np.testing.assert_array_equal(np_(n_sel), rn)
 
 
-def _attend_case(B, Hkv, G, D, T_cap, C, kv, n_sels, seed, sorted_idx=True):
+def _attend_case(B, Hkv, G, D, T_cap, C, kv, n_sels, seed, sorted_idx=True, recent=0, lens=None):
     Hq = Hkv * G
     q = wk.randn((B, Hq, D), seed=seed)
     k = (wk.randn((B, Hkv, T_cap, D), seed=seed, sub=1) * 2).to(torch.bfloat16 if kv == "bf16" else torch.float32)
@@ -270,12 +270,16 @@ def _attend_case(B, Hkv, G, D, T_cap, C, kv, n_sels, seed, sorted_idx=True):
             idx[b, g, :n] = np.sort(sel) if sorted_idx else sel
             n_sel[b, g] = n
     dims = dims_for(A, B, Hq, Hkv, D, T_cap, kv)
-    cfg = A.Cfg(8, C, 1e-2)
+    cfg = A.Cfg(8, C, 1e-2, recent)
     ws = torch.empty(A.asp_workspace_size(dims, cfg, A.OP_DECODE), dtype=torch.uint8, device=DEV)
     out = torch.full((B, Hq, D), 99.0, dtype=torch.float32, device=DEV)
-    A.asp_sparse_decode(dims, cfg, q.to(DEV), k.to(DEV), v.to(DEV), torch.from_numpy(idx).to(DEV),
+    glens = None if lens is None else torch.tensor(lens, dtype=torch.int32, device=DEV)
+    A.asp_sparse_decode(dims, cfg, q.to(DEV), k.to(DEV), v.to(DEV), glens, torch.from_numpy(idx).to(DEV),
                         torch.from_numpy(n_sel).to(DEV), out, ws)
-    ref = oracle.attend(q.numpy(), kv_np(k), kv_np(v), idx, n_sel)
+    if recent:
+        ref = oracle.attend_with_recent(q.numpy(), kv_np(k), kv_np(v), idx, n_sel, np.array(lens, np.int32), recent)
+    else:
+        ref = oracle.attend(q.numpy(), kv_np(k), kv_np(v), idx, n_sel)
     err = np.abs(np_(out).astype(np.float64) - ref).max()
     assert err <= 1e-2, err
     return err
@@ -286,6 +290,16 @@ def _attend_case(B, Hkv, G, D, T_cap, C, kv, n_sels, seed, sorted_idx=True):
 @pytest.mark.parametrize("G", [1, 2, 4, 8])
 def test_attend_matches_oracle(kv, D, G):
     err = _attend_case(2, 2, G, D, 3000, 700, kv, [700, 513, 1, 0], seed=G + D)
+    assert err < 1e-4
+
+
+@pytest.mark.parametrize("kv,G,D", [("bf16", 4, 128), ("f32", 2, 64), ("bf16", 8, 64)])
+@pytest.mark.parametrize("recent", [1, 100, 700])
+def test_attend_with_the_newest_tokens(kv, G, D, recent):
+    # Selections drawn over the whole cache overlap the recent window; lengths
+    # include an empty sequence and ones shorter than the window.
+    lens = [3000, 1000, 60, 0]
+    err = _attend_case(4, 2, G, D, 3000, 300, kv, [300, 0, 17, 1], seed=recent + G, recent=recent, lens=lens)
     assert err < 1e-4
 
 

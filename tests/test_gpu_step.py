@@ -35,7 +35,7 @@ class Problem:
         self.wl = wl
         self.dims = A.Dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.t_cap,
                            A.KV_BF16 if wl.kv_dtype == "bf16" else A.KV_F32)
-        self.cfg = A.Cfg(wl.window, wl.top_c, wl.lam)
+        self.cfg = A.Cfg(wl.window, wl.top_c, wl.lam, wl.recent)
         # lens: context lengths that replace the workload's (K/V stay as generated)
         self.seq_lens = (wk.make_seq_lens(wl) if lens is None else torch.tensor(lens, dtype=torch.int32)).to(DEV)
         if kv is None:  # else K/V already generated for this workload's batch and lengths
@@ -66,7 +66,7 @@ def _staged_check(p: Problem, q_t: torch.Tensor, units=None):
     A.asp_predict_query(d, c, p.q_hist, p.newest, p.length, p.q_pred)
     A.asp_score_keys(d, p.q_pred, p.k, p.seq_lens, p.scores)
     A.asp_select_topc(d, c, p.scores, p.seq_lens, p.idx, p.n_sel)
-    A.asp_sparse_decode(d, c, q_t.to(DEV), p.k, p.v, p.idx, p.n_sel, p.out, p.ws_dec)
+    A.asp_sparse_decode(d, c, q_t.to(DEV), p.k, p.v, p.seq_lens, p.idx, p.n_sel, p.out, p.ws_dec)
     torch.cuda.synchronize()
     bs = list(range(p.wl.batch)) if units is None else units
     oh, on, ol = oracle.push(q_t.numpy(), *hist_before)
@@ -172,7 +172,7 @@ def _manual_run(p: Problem, n_steps: int):
     for s in range(n_steps):
         q = p.queries[wl.history_steps + s].to(DEV)
         if s > 0:
-            A.asp_sparse_decode(d, c, q, p.k, p.v, idx_prev, n_prev, p.out, p.ws_dec)
+            A.asp_sparse_decode(d, c, q, p.k, p.v, p.seq_lens, idx_prev, n_prev, p.out, p.ws_dec)
         A.asp_push_query(d, c, q, p.q_hist, p.newest, p.length)
         A.asp_predict_query(d, c, p.q_hist, p.newest, p.length, p.q_pred)
         A.asp_score_keys(d, p.q_pred, p.k, p.seq_lens, p.scores)
@@ -180,7 +180,7 @@ def _manual_run(p: Problem, n_steps: int):
         n_sel = torch.empty_like(p.n_sel)
         A.asp_select_topc(d, c, p.scores, p.seq_lens, idx, n_sel)
         if s == 0:
-            A.asp_sparse_decode(d, c, q, p.k, p.v, idx, n_sel, p.out, p.ws_dec)
+            A.asp_sparse_decode(d, c, q, p.k, p.v, p.seq_lens, idx, n_sel, p.out, p.ws_dec)
         torch.cuda.synchronize()
         results.append((np_(p.out).copy(), np_(idx).copy(), np_(n_sel).copy(), np_(p.q_hist).copy(),
                         np_(p.newest).copy(), np_(p.length).copy()))
@@ -201,8 +201,12 @@ SMALL_STEP_CASES = {
     # an empty sequence, one shorter than a split, one ending inside a split, one full
     "g4-short-empty": wk.TINY.replace(name="g4-short-empty", batch=4, n_q_heads=8, n_kv_heads=2, head_dim=128,
                                       t_cap=2000, kv_dtype="bf16", window=8, top_c=700, history_steps=10),
+    # the newest 200 tokens attended beside the selection (which overlaps them)
+    "g4-recent": wk.TINY.replace(name="g4-recent", batch=4, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                                 t_cap=2000, kv_dtype="bf16", window=8, top_c=300, history_steps=10, recent=200),
 }
-STEP_LENS = {"g4-short-empty": [0, 37, 650, 2000]}
+STEP_LENS_RECENT = [2000, 150, 0, 1234]
+STEP_LENS = {"g4-short-empty": [0, 37, 650, 2000], "g4-recent": STEP_LENS_RECENT}
 
 
 @pytest.mark.parametrize("wl_name", ["tiny", "qwen3-8b-layer"] + list(SMALL_STEP_CASES))
@@ -226,7 +230,7 @@ def test_step_modes_bit_identical_to_entry_points(wl_name):
                 np.testing.assert_array_equal(a, b, err_msg="%s step %d" % (mode, s))
 
 
-@pytest.mark.parametrize("wl_name", ["g8-d64-w64", "g1-d128-w4"])
+@pytest.mark.parametrize("wl_name", ["g8-d64-w64", "g1-d128-w4", "g4-recent"])
 def test_two_stream_layer_rotation_matches_entry_points(wl_name):
     """The bench's schedule: L layers in rotation on two streams, one workspace,
     idx pair and event pair per layer and one shared q_ready event; every step

@@ -106,3 +106,54 @@ def test_empty_selection_gives_zero_and_bad_index_raises(orc):
     idx[0, 0, 0] = 4
     with pytest.raises(IndexError):
         orc.attend(q, k, k, idx, np.array([[1]], np.int32))
+
+
+# ---- the union with the newest tokens (the library's optional recent window)
+
+def test_recent_window_alone_is_dense_attention_over_the_tail(orc):
+    # No selection: the newest r tokens of each sequence, i.e. dense attention
+    # over rows [T - r, T).
+    r_ = np.random.default_rng(7)
+    B, Hkv, G, T_cap, D = 2, 2, 2, 200, 64
+    q = r_.standard_normal((B, Hkv * G, D)).astype(np.float32)
+    k = r_.standard_normal((B, Hkv, T_cap, D)).astype(np.float32)
+    v = r_.standard_normal((B, Hkv, T_cap, D)).astype(np.float32)
+    lens, recent = np.array([150, 40], np.int32), 50
+    idx = np.full((B, Hkv, 8), -1, np.int32)
+    out = orc.attend_with_recent(q, k, v, idx, np.zeros((B, Hkv), np.int32), lens, recent)
+    for b in range(B):
+        T = int(lens[b]); lo = max(T - recent, 0)
+        ref = sdpa_dense(q[b:b + 1], k[b:b + 1, :, lo:T].astype(np.float64), v[b:b + 1, :, lo:T].astype(np.float64),
+                         T - lo)
+        np.testing.assert_allclose(out[b:b + 1], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_recent_window_counts_a_selected_token_once(orc):
+    # The selection overlaps the window (and repeats an index): the union is
+    # attended with each token once, the same as dense attention over it.
+    r_ = np.random.default_rng(8)
+    B, Hkv, G, T_cap, D = 1, 1, 4, 300, 64
+    q = r_.standard_normal((B, G, D)).astype(np.float32)
+    k = r_.standard_normal((B, Hkv, T_cap, D)).astype(np.float32)
+    v = r_.standard_normal((B, Hkv, T_cap, D)).astype(np.float32)
+    T, recent = 250, 20
+    sel = np.array([[[3, 17, 235, 240, 240, 249, -1, 400]]], np.int32)   # 235.. in the window; -1, 400 skipped
+    out = orc.attend_with_recent(q, k, v, sel, np.array([[8]], np.int32), np.array([T], np.int32), recent)
+    union = np.array(sorted({3, 17} | set(range(T - recent, T))))
+    ref = sdpa_dense(q, k[:, :, union].astype(np.float64), v[:, :, union].astype(np.float64), len(union))
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_recent_window_longer_than_the_sequence_and_zero_recent(orc):
+    r_ = np.random.default_rng(9)
+    q = r_.standard_normal((1, 2, 64)).astype(np.float32)
+    k = r_.standard_normal((1, 1, 64, 64)).astype(np.float32)
+    sel = np.array([[[5, 9, -1]]], np.int32)
+    n = np.array([[2]], np.int32)
+    # recent = 0 is the plain selection
+    np.testing.assert_array_equal(orc.attend_with_recent(q, k, k, sel, n, np.array([30], np.int32), 0),
+                                  orc.attend(q, k, k, sel, n))
+    # recent past the length covers the whole sequence: dense over [0, T)
+    out = orc.attend_with_recent(q, k, k, sel, n, np.array([30], np.int32), 1000)
+    ref = sdpa_dense(q, k[:, :, :30].astype(np.float64), k[:, :, :30].astype(np.float64), 30)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)
