@@ -1,7 +1,6 @@
-// Attention blocks (device functions), shared by the attention launch and the
-// fused score + attention launch of a single-stream decode step.
-// Sparse decode attention over the selected tokens, split-K with an fp32
-// softmax and a log-sum-exp merge.
+// Attention block (device function) of the attention launch: sparse decode
+// attention over the selected tokens, split-K with an fp32 softmax and a
+// log-sum-exp merge.
 //
 // Sources: reproduction card, "Layout" (full versus top-C sparse attention) and
 // "Key finding" (the method attends to the C selected tokens only); research-map
