@@ -29,8 +29,8 @@ hipError_t launch_push(const Shape& s, const float* q_cur, float* q_hist, int32_
 // With q_cur != nullptr it predicts from the ring after pushing q_cur (lag 0 is
 // q_cur, the ring supplies the older lags) and writes q_cur into each head's
 // next ring slot, but leaves newest/len unchanged: a later launch of the same
-// step advances them (ring_advance, in the last select launch or, on two
-// streams, in the merge), once every predictor workgroup has read them.
+// step advances them (ring_advance, in the last select launch), once every
+// predictor workgroup has read them.
 // hist_zero, when not null, is cleared ([B*Hkv][HIST_BINS]).
 // `done` (nullable) is recorded when the launch completes.
 hipError_t launch_predict(const Shape& s, float* q_hist, const int32_t* newest, const int32_t* len,
@@ -56,15 +56,12 @@ hipError_t launch_overlap(const Shape& s, const int32_t* idx_a, const int32_t* n
                           const int32_t* n_b, int32_t* out, hipStream_t st);
 // Sparse attention over the selection and the newest s.R tokens: split-K
 // partials into `partials`, then the merge into out.  seq_lens may be null
-// when s.R == 0.  adv_newest/adv_len (nullable): the merge launch advances the
-// query ring.
+// when s.R == 0.
 hipError_t launch_attend(const Shape& s, const float* q, const void* k, const void* v, const int32_t* seq_lens,
-                         const int32_t* idx, const int32_t* n_sel, float* out, void* partials, hipStream_t st,
-                         int32_t* adv_newest = nullptr, int32_t* adv_len = nullptr);
+                         const int32_t* idx, const int32_t* n_sel, float* out, void* partials, hipStream_t st);
 // The merge alone (partials written by the attention blocks).
 hipError_t launch_merge(const Shape& s, const int32_t* seq_lens, const int32_t* n_sel, float* out,
-                        const void* partials, hipStream_t st, int32_t* adv_newest = nullptr,
-                        int32_t* adv_len = nullptr);
+                        const void* partials, hipStream_t st);
 
 // Whether `st` is being captured into a graph.
 inline bool capturing(hipStream_t st) {

@@ -46,17 +46,12 @@ __global__ void __launch_bounds__(128) merge_kernel(const float* __restrict__ pa
                                                     const int32_t* __restrict__ seq_lens,
                                                     const int32_t* __restrict__ n_sel, float* __restrict__ out,
                                                     int Hq, int Hkv, int G, int D, int T_cap, int C, int R,
-                                                    int nsplit, int tpb,
-                                                    int32_t* __restrict__ adv_newest, int32_t* __restrict__ adv_len,
-                                                    int W) {
+                                                    int nsplit, int tpb) {
   constexpr int PER = MERGE_MAX_SPLITS / 64;
   __shared__ float sw[MERGE_MAX_SPLITS];
   __shared__ float s_inv_l;
   const int bh = blockIdx.x;
   const int b = bh / Hq, h = bh % Hq;
-  // Ring advance of a two-stream step (the predictor launch that read newest
-  // and len for this step has completed before the attention started).
-  if (adv_newest != nullptr && h == 0 && threadIdx.x == 0) ring_advance(adv_newest, adv_len, b, W);
   const int g = h / G, hh = h % G;
   const int unit = b * Hkv + g;
   const AttendList al = attend_list(n_sel, seq_lens, unit, Hkv, C, R, T_cap);
@@ -130,8 +125,7 @@ static hipError_t launch_attend_d(const Shape& s, const float* q, const void* k,
 }
 
 hipError_t launch_attend(const Shape& s, const float* q, const void* k, const void* v, const int32_t* seq_lens,
-                         const int32_t* idx, const int32_t* n_sel, float* out, void* partials, hipStream_t st,
-                         int32_t* adv_newest, int32_t* adv_len) {
+                         const int32_t* idx, const int32_t* n_sel, float* out, void* partials, hipStream_t st) {
   if (s.B == 0) return hipSuccess;
   const int nsplit = attend_num_splits(s);
   float* part_acc = static_cast<float*>(partials);
@@ -144,18 +138,17 @@ hipError_t launch_attend(const Shape& s, const float* q, const void* k, const vo
     e = s.D == 64 ? launch_attend_d<float, 64>(s, q, k, v, seq_lens, idx, n_sel, part_acc, part_ml, st)
                   : launch_attend_d<float, 128>(s, q, k, v, seq_lens, idx, n_sel, part_acc, part_ml, st);
   if (e != hipSuccess) return e;
-  return launch_merge(s, seq_lens, n_sel, out, partials, st, adv_newest, adv_len);
+  return launch_merge(s, seq_lens, n_sel, out, partials, st);
 }
 
 hipError_t launch_merge(const Shape& s, const int32_t* seq_lens, const int32_t* n_sel, float* out,
-                        const void* partials, hipStream_t st, int32_t* adv_newest, int32_t* adv_len) {
+                        const void* partials, hipStream_t st) {
   if (s.B == 0) return hipSuccess;
   const int nsplit = attend_num_splits(s);
   const float* part_acc = static_cast<const float*>(partials);
   const float* part_ml = part_acc + (size_t)s.B * s.Hkv * nsplit * s.G * s.D;
   hipLaunchKernelGGL(merge_kernel, dim3(s.B * s.Hq), dim3(128), 0, st, part_acc, part_ml, seq_lens, n_sel, out,
-                     s.Hq, s.Hkv, s.G, s.D, s.T_cap, s.C, s.R, nsplit, attend_tokens_per_block(s.D, s.kv),
-                     adv_newest, adv_len, s.W > 0 ? s.W : 1);
+                     s.Hq, s.Hkv, s.G, s.D, s.T_cap, s.C, s.R, nsplit, attend_tokens_per_block(s.D, s.kv));
   return hipGetLastError();
 }
 
