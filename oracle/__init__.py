@@ -5,8 +5,9 @@ the CPU-baseline leg of ``bench.py`` may import this package.  It shares no
 code with the HIP library in ``query_aware_sparse_amd`` and never calls it.
 
 The arithmetic lives in ``asp_oracle.c`` (compiled with gcc, no fast-math);
-this module only builds it, marshals numpy arrays through ctypes and shapes
-the results.  Each wrapper names the definition it follows; the C file states
+this module only builds it, marshals numpy arrays through ctypes, shapes the
+results, and lists the tokens of the optional newest-token window
+(``attend_with_recent``) before handing them to the C attention.  Each wrapper names the definition it follows; the C file states
 the readings adopted where the pages are silent.
 """
 from __future__ import annotations
