@@ -157,7 +157,7 @@ __device__ __forceinline__ void score_mfma_block(const float* __restrict__ q_pre
       if constexpr (G == 8) m = fmaxf(m, __shfl_xor(m, 16));
       const int key = base + u * 16 + j;
       if (c == 0 && key < k1) {
-        __builtin_nontemporal_store(m, sb + key);
+        sb[key] = m;  // a plain store: the select launches read the row back soon after
         if constexpr (HIST) atomicAdd(&lhist[order_key(m) >> HIST_SHIFT], 1u);
       }
       // Slot u % TB is written again two tiles later (or next iteration).
