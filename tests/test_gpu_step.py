@@ -230,13 +230,14 @@ def test_step_modes_bit_identical_to_entry_points(wl_name):
                 np.testing.assert_array_equal(a, b, err_msg="%s step %d" % (mode, s))
 
 
-@pytest.mark.parametrize("wl_name", ["g8-d64-w64", "g1-d128-w4", "g4-recent"])
-def test_two_stream_layer_rotation_matches_entry_points(wl_name):
+@pytest.mark.parametrize("wl_name,L,n", [("g8-d64-w64", 3, 4), ("g1-d128-w4", 3, 4), ("g4-recent", 3, 4),
+                                         ("qwen3-8b-layer", 4, 3)])
+def test_two_stream_layer_rotation_matches_entry_points(wl_name, L, n):
     """The bench's schedule: L layers in rotation on two streams, one workspace,
     idx pair and event pair per layer and one shared q_ready event; every step
-    of every layer equals the entry-point schedule of that layer."""
-    L, n = 3, 4
-    base = SMALL_STEP_CASES[wl_name]
+    of every layer equals the entry-point schedule of that layer (at the bench
+    shape too: four 1 GiB layers)."""
+    base = wk.CONFIGS.get(wl_name) or SMALL_STEP_CASES[wl_name]
     probs = [Problem(base, kv_device=DEV, layer=l, n_steps=n) for l in range(L)]
     for p in probs:
         p.fill_history()
