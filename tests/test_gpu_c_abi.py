@@ -1,0 +1,24 @@
+"""The C ABI from C++ alone (GPU required): tests/c_abi/step_check.cpp, built by
+__graft_entry__.build(), runs a layer's pipelined steps on one stream and on two
+streams through include/asp.h with hipMalloc'd buffers and checks that every
+step's output, selection and query ring agree bit for bit."""
+import os
+import subprocess
+
+import pytest
+
+from asp_testutil import require_gpu
+
+pytestmark = pytest.mark.gpu
+
+BIN = os.path.join(os.path.dirname(__file__), "c_abi", "step_check")
+
+
+def test_c_abi_pipelined_steps_agree_across_stream_modes():
+    require_gpu()
+    assert os.path.exists(BIN), "tests/c_abi/step_check is not built; run __graft_entry__.build()"
+    r = subprocess.run([BIN], capture_output=True, text=True, timeout=120)
+    print(r.stdout, r.stderr, flush=True)
+    assert r.returncode == 0, r.stderr
+    assert "c-abi step check: ok" in r.stdout
+    assert r.stdout.count("agree") == 6
