@@ -21,10 +21,16 @@
  *    must be 16-byte aligned, else ASP_ERR_WORKSPACE.
  *  - A "unit" is one (sequence b, KV head g); G = n_q_heads / n_kv_heads query
  *    heads h = g*G .. g*G+G-1 share KV head g.
- *  - The library allocates nothing, frees nothing, keeps no state between calls
- *    and never waits on the host: work is enqueued on the given stream(s) and
- *    the call returns.  Calls are re-entrant; two calls that write the same
- *    buffers (or share a workspace) must be ordered by the caller.
+ *  - The library allocates no device memory, keeps no data between calls and
+ *    never waits on the host: work is enqueued on the given stream(s) and the
+ *    call returns.  The one piece of library state is the pair of streams and
+ *    pair of events that asp_step creates per device on its first two-stream
+ *    call (released by asp_release_streams).  Calls are re-entrant; two calls
+ *    that write the same buffers (or share a workspace) must be ordered by the
+ *    caller.
+ *  - Every entry point except asp_step enqueues kernel launches only (no
+ *    memset or copy node, no event), so a sequence of them can be captured
+ *    into a HIP graph on one stream and replayed.
  *  - Arguments are validated on the host before anything is enqueued; on any
  *    error nothing is enqueued.  Values that live in device memory (seq_lens,
  *    hist_newest, hist_len, idx, n_sel) cannot be checked on the host: the
