@@ -60,10 +60,12 @@ def step_bytes(wl, seq_lens) -> dict:
 
 
 def score_kernel_bytes(wl, seq_lens) -> int:
-    """Algorithmic bytes of one score launch: the K rows read, the predicted
-    queries read and the fp32 score row written."""
+    """Algorithmic bytes of one score launch of the step (the candidate
+    route): the K rows read and the predicted queries read.  The candidates it
+    writes (about 2*C_eff (key, index) pairs per unit) are the implementation's
+    own traffic, as the score rows are not part of the method's bytes."""
     D, Hkv, G = wl.head_dim, wl.n_kv_heads, wl.group
-    return sum(Hkv * (T * D * 2 + T * 4 + G * D * 4) for T in seq_lens)
+    return sum(Hkv * (T * D * 2 + G * D * 4) for T in seq_lens)
 
 
 SCORE_SOURCES = [os.path.join(ROOT, "query_aware_sparse_amd", "csrc", f)
@@ -82,7 +84,7 @@ def sources_hash(paths) -> str:
 def measured_traffic(kernel_sources):
     """HBM traffic of the score kernel from the committed rocprofv3 counter
     summary, or None when the kernel sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", "score_keys_qwen3-8b-layer_traffic.json")
+    path = os.path.join(ROOT, "profiles", "score_candidates_qwen3-8b-layer_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -266,21 +268,33 @@ def main() -> int:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / n  # us per launch
 
-    q_pred = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    # Each layer's predicted query from its ring as the steps left it, so that
+    # the candidate launches see the hints of that layer's steady state.
+    q_pred = [torch.empty((B, Hq, D), dtype=torch.float32, device=dev) for _ in range(L)]
     scores = torch.empty((B, Hkv, wl.t_cap), dtype=torch.float32, device=dev)
     idx_t = torch.empty((B, Hkv, C), dtype=torch.int32, device=dev)
     nsel_t = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
-    for lay in layers:
-        A.asp_predict_query(dims, cfg, lay["q_hist"], lay["newest"], lay["length"], q_pred, stream=attn)
+    for l, lay in enumerate(layers):
+        A.asp_predict_query(dims, cfg, lay["q_hist"], lay["newest"], lay["length"], q_pred[l], stream=attn)
     n = args.kernel_launches
+
+    def lay_(i):
+        return layers[i % L]
+
     kern = {
-        "predict_us": time_entry(lambda i: A.asp_predict_query(dims, cfg, layers[i % L]["q_hist"],
-                                                               layers[i % L]["newest"], layers[i % L]["length"],
-                                                               q_pred, stream=attn), n),
-        "score_us": time_entry(lambda i: A.asp_score_keys(dims, q_pred, layers[i % L]["k"], layers[i % L]["seq_lens"],
-                                                          scores, stream=attn), n),
-        "select_us": time_entry(lambda i: A.asp_select_topc(dims, cfg, scores, layers[0]["seq_lens"], idx_t, nsel_t,
-                                                            stream=attn), n),
+        "predict_us": time_entry(lambda i: A.asp_predict_query(dims, cfg, lay_(i)["q_hist"], lay_(i)["newest"],
+                                                               lay_(i)["length"], q_pred[i % L], stream=attn), n),
+        # the step's score launch: keys at or above the layer's hints kept as candidates
+        "score_us": time_entry(lambda i: A.asp_score_candidates(dims, cfg, q_pred[i % L], lay_(i)["k"],
+                                                                lay_(i)["seq_lens"], ws_step[i % L], stream=attn), n),
+        "select_us": time_entry(lambda i: A.asp_select_candidates(dims, cfg, q_pred[i % L], lay_(i)["k"],
+                                                                  lay_(i)["seq_lens"], idx_t, nsel_t, ws_step[i % L],
+                                                                  stream=attn), n),
+        # the score-row route of the standalone entry points, for comparison
+        "score_keys_us": time_entry(lambda i: A.asp_score_keys(dims, q_pred[i % L], lay_(i)["k"],
+                                                               lay_(i)["seq_lens"], scores, stream=attn), n),
+        "select_topc_us": time_entry(lambda i: A.asp_select_topc(dims, cfg, scores, layers[0]["seq_lens"], idx_t,
+                                                                 nsel_t, stream=attn), n),
         "attend_us": time_entry(lambda i: A.asp_sparse_decode(dims, cfg, layers[i % L]["qs"][0], layers[i % L]["k"],
                                                               layers[i % L]["v"], layers[i % L]["seq_lens"],
                                                               layers[i % L]["idx"][0],
@@ -289,7 +303,7 @@ def main() -> int:
     sk_bytes = score_kernel_bytes(wl, lens_list)
     achieved = sk_bytes / (kern["score_us"] * 1e-6) / 1e9
     traffic = measured_traffic(SCORE_SOURCES) if headline else None
-    roofline = {"kernel": "score_keys", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+    roofline = {"kernel": "score_candidates", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "algorithmic_bytes_per_launch": sk_bytes, "avg_launch_us": round(kern["score_us"], 2)}
     log("per-kernel us: %s" % json.dumps({k_: round(v_, 2) for k_, v_ in kern.items()}))

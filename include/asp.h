@@ -93,7 +93,8 @@ typedef enum {
   ASP_OP_SCORE = 2,
   ASP_OP_SELECT = 3,
   ASP_OP_DECODE = 4,
-  ASP_OP_STEP = 5
+  ASP_OP_STEP = 5,
+  ASP_OP_CANDIDATES = 6
 } asp_op;
 
 /* Bytes of device workspace the entry point for `op` needs (0 if none), or 0
@@ -162,6 +163,35 @@ asp_status asp_score_keys(const asp_dims* dims, const float* q_pred, const void*
 asp_status asp_select_topc(const asp_dims* dims, const asp_cfg* cfg, const float* scores, const uint32_t* hist,
                            const int32_t* seq_lens, int32_t* idx, int32_t* n_sel, void* ws, size_t ws_bytes,
                            hipStream_t stream);
+
+/* The same selection by the route asp_step takes ([card] "Key finding"; the
+ * candidate route is a property of this implementation, not of the pages).
+ * asp_score_candidates runs the score pass of asp_score_keys but writes no
+ * score rows: per unit it keeps, as candidates, the keys whose order key is at
+ * or above the unit's threshold hint.  asp_select_candidates then selects the
+ * exact top C_eff among them; a unit left with fewer than C_eff candidates is
+ * first rescored with every key kept.  idx and n_sel therefore equal, bit for
+ * bit, those of asp_score_keys followed by asp_select_topc, whatever the hints
+ * hold.  Each selection stores the unit's next hint: the lower edge of the bin
+ * of the top 22 bits of the order key that holds the 2*C_eff-th kept key, or,
+ * when fewer keys were kept, the current hint moved down by the key range the
+ * shortfall would take at the density of the kept keys just above it.  Scores
+ * close to those of the previous step thus cost one pass over the keys plus
+ * about 2*C_eff candidate writes per unit.
+ * ws/ws_bytes: asp_workspace_size(ASP_OP_CANDIDATES) bytes, 16-byte aligned
+ * (about 8 bytes per key slot).  Its first 4*batch*n_kv_heads bytes are the
+ * hints ([B][Hkv] uint32), carried from one selection to the next; any value
+ * is valid (a zeroed workspace keeps every key on its first use).
+ * asp_score_candidates: q_pred, k and seq_lens as in asp_score_keys.
+ * asp_select_candidates: selects from what the last asp_score_candidates call
+ * on this workspace kept; q_pred, k and seq_lens must be that call's (a
+ * rescoring reads them); idx and n_sel as in asp_select_topc.  Two calls that
+ * share a workspace must be ordered by the caller. */
+asp_status asp_score_candidates(const asp_dims* dims, const asp_cfg* cfg, const float* q_pred, const void* k,
+                                const int32_t* seq_lens, void* ws, size_t ws_bytes, hipStream_t stream);
+asp_status asp_select_candidates(const asp_dims* dims, const asp_cfg* cfg, const float* q_pred, const void* k,
+                                 const int32_t* seq_lens, int32_t* idx, int32_t* n_sel, void* ws, size_t ws_bytes,
+                                 hipStream_t stream);
 
 /* Overlap of two selections per unit, the diagnostic of the temporal locality
  * and prediction recall claims ([card] "What reproduces (and what does not)":
@@ -240,12 +270,17 @@ asp_status asp_sparse_decode(const asp_dims* dims, const asp_cfg* cfg, const flo
  * asp_step returns ASP_ERR_UNSUPPORTED when attn_stream or sel_stream is being
  * captured into a graph.
  * Bootstrap mode (idx_cur == NULL): everything runs on attn_stream: push,
- * predict, score, select into idx_next, then attention over idx_next.
- * Results of both modes do not depend on the stream arrangement (the kernels
- * are deterministic).
+ * predict, score, select into idx_next, then attention over idx_next; the
+ * workspace's hints are reset first, so that this selection keeps every key.
+ * Every mode selects by the candidate route of asp_score_candidates and
+ * asp_select_candidates, so the selection equals that of asp_score_keys with
+ * asp_select_topc; results do not depend on the stream arrangement (the
+ * kernels are deterministic).
  * Shapes as in the entry points above; ws/ws_bytes:
- * asp_workspace_size(ASP_OP_STEP) bytes, used by both streams (disjoint
- * regions), so it must not be shared with a concurrent step. */
+ * asp_workspace_size(ASP_OP_STEP) bytes, 16-byte aligned, used by all the
+ * streams (disjoint regions), so it must not be shared with a concurrent step.
+ * Its first 4*batch*n_kv_heads bytes are the per-unit threshold hints of the
+ * candidate route, which each step updates for the next step of the layer. */
 asp_status asp_step(const asp_dims* dims, const asp_cfg* cfg, const float* q_cur, float* q_hist,
                     int32_t* hist_newest, int32_t* hist_len, const void* k, const void* v,
                     const int32_t* seq_lens, const int32_t* idx_cur, const int32_t* n_sel_cur,

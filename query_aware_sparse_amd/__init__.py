@@ -17,16 +17,17 @@ import torch
 
 __all__ = [
     "AspError", "Dims", "Cfg", "HipEvent", "library_path", "load",
-    "OP_PUSH", "OP_PREDICT", "OP_SCORE", "OP_SELECT", "OP_DECODE", "OP_STEP",
+    "OP_PUSH", "OP_PREDICT", "OP_SCORE", "OP_SELECT", "OP_DECODE", "OP_STEP", "OP_CANDIDATES",
     "KV_BF16", "KV_F32", "HIST_BINS",
     "asp_workspace_size", "asp_status_string", "asp_push_query", "asp_predict_query", "asp_score_keys",
-    "asp_select_topc", "asp_sparse_decode", "asp_step", "asp_selection_overlap", "asp_release_streams",
+    "asp_select_topc", "asp_score_candidates", "asp_select_candidates", "asp_sparse_decode", "asp_step",
+    "asp_selection_overlap", "asp_release_streams",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libasp.so")
 
-OP_PUSH, OP_PREDICT, OP_SCORE, OP_SELECT, OP_DECODE, OP_STEP = range(6)
+OP_PUSH, OP_PREDICT, OP_SCORE, OP_SELECT, OP_DECODE, OP_STEP, OP_CANDIDATES = range(7)
 KV_BF16, KV_F32 = 0, 1
 HIST_BINS = 2048  # bins of the coarse score histograms (ASP_HIST_BINS)
 _STATUS_NAMES = {0: "ASP_OK", 1: "ASP_ERR_INVALID_ARG", 2: "ASP_ERR_UNSUPPORTED", 3: "ASP_ERR_WORKSPACE",
@@ -81,12 +82,15 @@ def load():
     lib.asp_predict_query.argtypes = [D, C, P, P, P, P, P]
     lib.asp_score_keys.argtypes = [D, P, P, P, P, P, P]
     lib.asp_select_topc.argtypes = [D, C, P, P, P, P, P, P, SZ, P]
+    lib.asp_score_candidates.argtypes = [D, C, P, P, P, P, SZ, P]
+    lib.asp_select_candidates.argtypes = [D, C, P, P, P, P, P, P, SZ, P]
     lib.asp_sparse_decode.argtypes = [D, C, P, P, P, P, P, P, P, P, SZ, P]
     lib.asp_step.argtypes = [D, C, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P, P, P, P, P]
     lib.asp_selection_overlap.argtypes = [D, C, P, P, P, P, P, P]
     lib.asp_release_streams.argtypes = []
     for name in ("asp_push_query", "asp_predict_query", "asp_score_keys", "asp_select_topc",
-                 "asp_sparse_decode", "asp_step", "asp_selection_overlap", "asp_release_streams"):
+                 "asp_score_candidates", "asp_select_candidates", "asp_sparse_decode", "asp_step",
+                 "asp_selection_overlap", "asp_release_streams"):
         getattr(lib, name).restype = I32
     _lib = lib
     # the library's streams end before the HIP runtime is torn down
@@ -236,6 +240,36 @@ def asp_select_topc(dims: Dims, cfg: Cfg, scores, seq_lens, idx, n_sel, ws=None,
     _raise("asp_select_topc", load().asp_select_topc(ctypes.byref(dims), ctypes.byref(cfg), _ptr(scores),
                                                      _ptr(hist), _ptr(seq_lens), _ptr(idx), _ptr(n_sel), wp, wb,
                                                      _stream_handle(stream)))
+
+
+def _check_candidates(dims: Dims, cfg: Cfg, q_pred, k, seq_lens, ws):
+    B, Hq, Hkv, D, T = dims.batch, dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.t_cap
+    _check(q_pred, "q_pred", (B, Hq, D), torch.float32)
+    _check(k, "k", (B, Hkv, T, D), _kv_dtype(dims))
+    _check(seq_lens, "seq_lens", (B,), torch.int32)
+    if ws is None:
+        raise AspError("the candidate workspace carries the threshold hints between calls: pass one "
+                       "(asp_workspace_size(dims, cfg, OP_CANDIDATES) bytes)")
+    return _ws(ws)
+
+
+def asp_score_candidates(dims: Dims, cfg: Cfg, q_pred, k, seq_lens, ws, stream=None) -> None:
+    """Score pass that keeps, per unit, the keys at or above the hint held in ws."""
+    wp, wb = _check_candidates(dims, cfg, q_pred, k, seq_lens, ws)
+    _raise("asp_score_candidates", load().asp_score_candidates(ctypes.byref(dims), ctypes.byref(cfg), _ptr(q_pred),
+                                                               _ptr(k), _ptr(seq_lens), wp, wb,
+                                                               _stream_handle(stream)))
+
+
+def asp_select_candidates(dims: Dims, cfg: Cfg, q_pred, k, seq_lens, idx, n_sel, ws, stream=None) -> None:
+    """Exact top-C from the candidates of the last asp_score_candidates call on ws."""
+    B, Hkv, C = dims.batch, dims.n_kv_heads, cfg.top_c
+    wp, wb = _check_candidates(dims, cfg, q_pred, k, seq_lens, ws)
+    _check(idx, "idx", (B, Hkv, C), torch.int32)
+    _check(n_sel, "n_sel", (B, Hkv), torch.int32)
+    _raise("asp_select_candidates", load().asp_select_candidates(ctypes.byref(dims), ctypes.byref(cfg), _ptr(q_pred),
+                                                                 _ptr(k), _ptr(seq_lens), _ptr(idx), _ptr(n_sel), wp,
+                                                                 wb, _stream_handle(stream)))
 
 
 def asp_selection_overlap(dims: Dims, cfg: Cfg, idx_a, n_sel_a, idx_b, n_sel_b, overlap, stream=None) -> None:

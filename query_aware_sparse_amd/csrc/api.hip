@@ -69,19 +69,17 @@ asp_status check_all(const asp_dims* d, const asp_cfg* c, Shape* s) {
 }
 
 struct StepLayout {
-  size_t q_pred, scores, hist, select, partials, total;
+  size_t cand, q_pred, partials, total;
 };
 
-// Workspace of asp_step: predicted queries, score rows, coarse histograms and
-// the selection's scratch (selection stream), attention partials (attention
-// stream).
+// Workspace of asp_step: the candidate workspace (threshold hints first, kept
+// from one step of the layer to the next; candidate regions) and the predicted
+// queries (selection streams), attention partials (attention stream).
 StepLayout step_layout(const Shape& s) {
   StepLayout l;
-  l.q_pred = 0;
-  l.scores = align_up(l.q_pred + (size_t)s.B * s.Hq * s.D * sizeof(float));
-  l.hist = align_up(l.scores + (size_t)s.B * s.Hkv * s.T_cap * sizeof(float));
-  l.select = align_up(l.hist + (size_t)s.B * s.Hkv * asp::HIST_BINS * sizeof(uint32_t));
-  l.partials = align_up(l.select + asp::select_ws_bytes(s, false));
+  l.cand = 0;
+  l.q_pred = align_up(l.cand + asp::cand_ws_bytes(s));
+  l.partials = align_up(l.q_pred + (size_t)s.B * s.Hq * s.D * sizeof(float));
   l.total = align_up(l.partials + asp::attend_partials_bytes(s));
   return l;
 }
@@ -91,6 +89,7 @@ size_t ws_bytes_for(const Shape& s, asp_op op) {
     case ASP_OP_SELECT: return align_up(asp::select_ws_bytes(s, true));
     case ASP_OP_DECODE: return align_up(asp::attend_partials_bytes(s));
     case ASP_OP_STEP: return step_layout(s).total;
+    case ASP_OP_CANDIDATES: return align_up(asp::cand_ws_bytes(s));
     default: return 0;
   }
 }
@@ -168,16 +167,22 @@ hipError_t step_fork(StepFork** out) {
   return hipSuccess;
 }
 
-// Selection work of one step: four launches.  The predictor pushes q_cur into
-// every head's ring slot and clears the coarse histograms; the score launch
-// fills the histograms; the two select launches use them, and the last one
-// advances the ring.
+// Selection work of one step on one stream: the predictor pushes q_cur into
+// every head's ring slot and predicts; the score launch keeps the candidates;
+// the select launches pick from them (rescoring the units left short), and the
+// first advances the ring.
 asp_status run_selection(const Shape& s, const float* q_cur, float* q_hist, int32_t* newest, int32_t* len,
                          const void* k, const int32_t* seq_lens, int32_t* idx, int32_t* n_sel, float* q_pred,
-                         float* scores, uint32_t* hist, void* sel_ws, hipStream_t st) {
-  ASP_TRY_HIP(asp::launch_predict(s, q_hist, newest, len, q_cur, q_pred, hist, st));
-  ASP_TRY_HIP(asp::launch_score(s, q_pred, k, seq_lens, scores, hist, st));
-  ASP_TRY_HIP(asp::launch_select(s, scores, hist, seq_lens, idx, n_sel, newest, len, sel_ws, st));
+                         const asp::CandWs& cw, hipStream_t st, hipEvent_t done) {
+  ASP_TRY_HIP(asp::launch_predict(s, q_hist, newest, len, q_cur, q_pred, nullptr, st));
+  ASP_TRY_HIP(asp::launch_score_candidates(s, q_pred, k, seq_lens, cw, false, st));
+  ASP_TRY_HIP(asp::launch_select_candidates(s, q_pred, k, seq_lens, cw, idx, n_sel, newest, len, st, done));
+  return ASP_OK;
+}
+
+// Candidate workspace checks shared by the candidate entry points.
+asp_status check_cand_ws(const Shape& s, void* ws, size_t ws_bytes) {
+  if (ws == nullptr || ws_bytes < asp::cand_ws_bytes(s) || !aligned16(ws)) return ASP_ERR_WORKSPACE;
   return ASP_OK;
 }
 
@@ -249,6 +254,33 @@ asp_status asp_select_topc(const asp_dims* dims, const asp_cfg* cfg, const float
   return hip_status(asp::launch_select(s, scores, hist, seq_lens, idx, n_sel, nullptr, nullptr, ws, stream));
 }
 
+asp_status asp_score_candidates(const asp_dims* dims, const asp_cfg* cfg, const float* q_pred, const void* k,
+                                const int32_t* seq_lens, void* ws, size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  asp_status st = check_all(dims, cfg, &s);
+  if (st != ASP_OK) return st;
+  if (!q_pred || !k || !seq_lens) return ASP_ERR_INVALID_ARG;
+  if (!aligned16(k) || !aligned4(q_pred) || !aligned4(seq_lens)) return ASP_ERR_INVALID_ARG;
+  st = check_cand_ws(s, ws, ws_bytes);
+  if (st != ASP_OK) return st;
+  return hip_status(asp::launch_score_candidates(s, q_pred, k, seq_lens, asp::cand_carve(s, ws), false, stream));
+}
+
+asp_status asp_select_candidates(const asp_dims* dims, const asp_cfg* cfg, const float* q_pred, const void* k,
+                                 const int32_t* seq_lens, int32_t* idx, int32_t* n_sel, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+  Shape s;
+  asp_status st = check_all(dims, cfg, &s);
+  if (st != ASP_OK) return st;
+  if (!q_pred || !k || !seq_lens || !idx || !n_sel) return ASP_ERR_INVALID_ARG;
+  if (!aligned16(k) || !aligned4(q_pred) || !aligned4(seq_lens) || !aligned4(idx) || !aligned4(n_sel))
+    return ASP_ERR_INVALID_ARG;
+  st = check_cand_ws(s, ws, ws_bytes);
+  if (st != ASP_OK) return st;
+  return hip_status(asp::launch_select_candidates(s, q_pred, k, seq_lens, asp::cand_carve(s, ws), idx, n_sel,
+                                                  nullptr, nullptr, stream));
+}
+
 asp_status asp_selection_overlap(const asp_dims* dims, const asp_cfg* cfg, const int32_t* idx_a,
                                  const int32_t* n_sel_a, const int32_t* idx_b, const int32_t* n_sel_b,
                                  int32_t* overlap, hipStream_t stream) {
@@ -301,15 +333,16 @@ asp_status asp_step(const asp_dims* dims, const asp_cfg* cfg, const float* q_cur
   const StepLayout lay = step_layout(s);
   if (ws == nullptr || ws_bytes < lay.total) return ASP_ERR_WORKSPACE;
   unsigned char* base = static_cast<unsigned char*>(ws);
+  const asp::CandWs cw = asp::cand_carve(s, base + lay.cand);
   float* q_pred = reinterpret_cast<float*>(base + lay.q_pred);
-  float* scores = reinterpret_cast<float*>(base + lay.scores);
-  uint32_t* hist = reinterpret_cast<uint32_t*>(base + lay.hist);
-  void* sel_ws = base + lay.select;
   void* partials = base + lay.partials;
 
   if (!pipelined) {
-    st = run_selection(s, q_cur, q_hist, hist_newest, hist_len, k, seq_lens, idx_next, n_sel_next, q_pred, scores,
-                       hist, sel_ws, attn_stream);
+    // A first step: whatever the workspace holds, every key is kept (hint 0)
+    // rather than left to the rescoring launch.
+    ASP_TRY_HIP(asp::launch_clear_u32(cw.hint, (size_t)s.B * s.Hkv, attn_stream));
+    st = run_selection(s, q_cur, q_hist, hist_newest, hist_len, k, seq_lens, idx_next, n_sel_next, q_pred, cw,
+                       attn_stream, nullptr);
     if (st != ASP_OK) return st;
     ASP_TRY_HIP(asp::launch_attend(s, q_cur, k, v, seq_lens, idx_next, n_sel_next, out, partials, attn_stream));
     if (idx_next_ready) ASP_TRY_HIP(hipEventRecord(idx_next_ready, attn_stream));
@@ -317,23 +350,20 @@ asp_status asp_step(const asp_dims* dims, const asp_cfg* cfg, const float* q_cur
   }
   if (!two_streams) {
     ASP_TRY_HIP(asp::launch_attend(s, q_cur, k, v, seq_lens, idx_cur, n_sel_cur, out, partials, attn_stream));
-    ASP_TRY_HIP(asp::launch_predict(s, q_hist, hist_newest, hist_len, q_cur, q_pred, hist, attn_stream));
-    ASP_TRY_HIP(asp::launch_score(s, q_pred, k, seq_lens, scores, hist, attn_stream));
-    ASP_TRY_HIP(asp::launch_select(s, scores, hist, seq_lens, idx_next, n_sel_next, hist_newest, hist_len, sel_ws,
-                                   attn_stream, idx_next_ready));
-    return ASP_OK;
+    return run_selection(s, q_cur, q_hist, hist_newest, hist_len, k, seq_lens, idx_next, n_sel_next, q_pred, cw,
+                         attn_stream, idx_next_ready);
   }
   // Two streams, forked four ways so that the score passes of successive
   // calls run back to back while the latency-bound launches overlap them:
   //  - the fork's predictor stream waits for attn_stream as it stands at entry
   //    (q_cur ready, and with it the attention that produced q_cur in a decode
   //    loop) and for idx_cur_ready (the previous selection made with this
-  //    workspace has finished with the histograms, the scores and the ring),
+  //    workspace has finished with the candidates, the hints and the ring),
   //    then pushes and predicts; the launch records q_ready;
   //  - the fork's score stream waits for q_ready and scores; the launch records
   //    the fork's `scored` event;
-  //  - sel_stream waits for `scored` and selects; its last launch advances the
-  //    ring and records idx_next_ready;
+  //  - sel_stream waits for `scored` and selects (its first launch advances
+  //    the ring); the last launch records idx_next_ready;
   //  - attn_stream waits for idx_cur_ready and runs the attention and merge.
   // The predictor waits for idx_cur_ready itself rather than through
   // attn_stream: a chain of two cross-stream waits costs a step ~3 us more.
@@ -344,12 +374,12 @@ asp_status asp_step(const asp_dims* dims, const asp_cfg* cfg, const float* q_cur
   ASP_TRY_HIP(hipEventRecord(f->in, attn_stream));
   ASP_TRY_HIP(hipStreamWaitEvent(f->pred, f->in, 0));
   ASP_TRY_HIP(hipStreamWaitEvent(f->pred, idx_cur_ready, 0));
-  ASP_TRY_HIP(asp::launch_predict(s, q_hist, hist_newest, hist_len, q_cur, q_pred, hist, f->pred, q_ready));
+  ASP_TRY_HIP(asp::launch_predict(s, q_hist, hist_newest, hist_len, q_cur, q_pred, nullptr, f->pred, q_ready));
   ASP_TRY_HIP(hipStreamWaitEvent(f->score, q_ready, 0));
-  ASP_TRY_HIP(asp::launch_score(s, q_pred, k, seq_lens, scores, hist, f->score, f->scored));
+  ASP_TRY_HIP(asp::launch_score_candidates(s, q_pred, k, seq_lens, cw, false, f->score, f->scored));
   ASP_TRY_HIP(hipStreamWaitEvent(sel_stream, f->scored, 0));
-  ASP_TRY_HIP(asp::launch_select(s, scores, hist, seq_lens, idx_next, n_sel_next, hist_newest, hist_len, sel_ws,
-                                 sel_stream, idx_next_ready));
+  ASP_TRY_HIP(asp::launch_select_candidates(s, q_pred, k, seq_lens, cw, idx_next, n_sel_next, hist_newest, hist_len,
+                                            sel_stream, idx_next_ready));
   ASP_TRY_HIP(hipStreamWaitEvent(attn_stream, idx_cur_ready, 0));
   ASP_TRY_HIP(asp::launch_attend(s, q_cur, k, v, seq_lens, idx_cur, n_sel_cur, out, partials, attn_stream));
   return ASP_OK;

@@ -49,6 +49,39 @@ size_t select_ws_bytes(const Shape& s, bool with_hist);
 hipError_t launch_select(const Shape& s, const float* scores, const uint32_t* hist, const int32_t* seq_lens,
                          int32_t* idx, int32_t* n_sel, int32_t* adv_newest, int32_t* adv_len, void* ws,
                          hipStream_t st, hipEvent_t done = nullptr);
+// Candidate path of the selection (the pipelined step, asp_score_candidates
+// and asp_select_candidates).  Each unit carries a threshold hint, an order
+// key: the score launch keeps every key at or above it as a (key, index)
+// candidate, in per-wave regions of CAND_REGION consecutive keys, and writes
+// no score rows.  The select launches pick the exact top C_eff from the
+// candidates; a unit left with fewer than C_eff candidates is rescored with
+// every key kept, so the result never depends on the hint.  Each selection
+// stores the next hint: a bin edge of the key that keeps about 2 C_eff
+// candidates of the scores it saw.
+constexpr int CAND_REGION = 128;       // keys of one wave of a score block
+constexpr int CAND_BLOCK_KEYS = 512;   // keys of one score block (four waves)
+struct CandWs {
+  uint32_t* hint;    // [units] threshold hint (order key)
+  uint32_t* flag;    // [units] 1: the unit is rescored with every key kept
+  uint32_t* rcount;  // [units][regions] candidates per region
+  uint2* cand;       // [units][regions][CAND_REGION] (order key, index)
+};
+__host__ __device__ inline int cand_regions(int T_cap) {  // regions per unit
+  return (T_cap + CAND_BLOCK_KEYS - 1) / CAND_BLOCK_KEYS * (CAND_BLOCK_KEYS / CAND_REGION);
+}
+size_t cand_ws_bytes(const Shape& s);
+CandWs cand_carve(const Shape& s, void* ws);  // hint at offset 0
+// fallback == false: keep the keys at or above each unit's hint.
+// fallback == true: keep every key of the units flagged by the first select
+// launch (the other units' blocks return at once).
+hipError_t launch_score_candidates(const Shape& s, const float* q_pred, const void* k, const int32_t* seq_lens,
+                                   const CandWs& cw, bool fallback, hipStream_t st, hipEvent_t done = nullptr);
+// Exact top-C_eff from the candidates (first launch), the rescoring of the
+// flagged units, and their selection (last launch); new hints.
+// adv_newest/adv_len (nullable) advance the query ring by one slot.
+hipError_t launch_select_candidates(const Shape& s, const float* q_pred, const void* k, const int32_t* seq_lens,
+                                    const CandWs& cw, int32_t* idx, int32_t* n_sel, int32_t* adv_newest,
+                                    int32_t* adv_len, hipStream_t st, hipEvent_t done = nullptr);
 // Per unit, the number of indices that two ascending selections share
 // (s.C <= overlap_max_c()).
 int overlap_max_c();
@@ -88,6 +121,11 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+// Number of set bits of m below this lane.
+__device__ __forceinline__ uint32_t lanes_below(unsigned long long m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
 
 // Cross-lane moves inside a 16-lane DPP row.
 template <int CTRL>

@@ -3,38 +3,46 @@
 
 namespace asp {
 
-template <int D, int G, bool HIST>
+template <int D, int G, bool HIST, int OUT>
 __global__ void __launch_bounds__(SCORE_THREADS) score_mfma_kernel(const float* __restrict__ q_pred,
                                                                    const uint16_t* __restrict__ k,
                                                                    const int32_t* __restrict__ seq_lens,
                                                                    float* __restrict__ scores,
-                                                                   uint32_t* __restrict__ hist, int Hq, int Hkv,
-                                                                   int T_cap) {
-  __shared__ __align__(16) unsigned char smem[score_mfma_lds_bytes<D, HIST>()];
-  score_mfma_block<D, G, HIST>(q_pred, k, seq_lens, scores, hist, Hq, Hkv, T_cap, blockIdx.x, blockIdx.y, smem);
+                                                                   uint32_t* __restrict__ hist, CandWs cw, int Hq,
+                                                                   int Hkv, int T_cap) {
+  __shared__ __align__(16) unsigned char smem[score_mfma_lds_bytes<D, HIST, OUT>()];
+  // The rescoring launch follows every selection and usually finds no unit
+  // flagged: its workgroups then leave before touching anything else.
+  if constexpr (OUT == OUT_ALL_FLAGGED) {
+    if (cw.flag[blockIdx.y] == 0u) return;
+  }
+  score_mfma_block<D, G, HIST, OUT>(q_pred, k, seq_lens, scores, hist, cw, Hq, Hkv, T_cap, blockIdx.x, blockIdx.y, smem);
 }
 
-template <int D, int G, bool HIST>
+template <int D, int G, bool HIST, int OUT>
 __global__ void __launch_bounds__(SCORE_THREADS) score_valu_kernel(const float* __restrict__ q_pred,
                                                                    const float* __restrict__ k,
                                                                    const int32_t* __restrict__ seq_lens,
                                                                    float* __restrict__ scores,
-                                                                   uint32_t* __restrict__ hist, int Hq, int Hkv,
-                                                                   int T_cap) {
-  __shared__ __align__(16) unsigned char smem[score_valu_lds_bytes<HIST>()];
-  score_valu_block<D, G, HIST>(q_pred, k, seq_lens, scores, hist, Hq, Hkv, T_cap, blockIdx.x, blockIdx.y, smem);
+                                                                   uint32_t* __restrict__ hist, CandWs cw, int Hq,
+                                                                   int Hkv, int T_cap) {
+  __shared__ __align__(16) unsigned char smem[score_valu_lds_bytes<HIST, OUT>()];
+  if constexpr (OUT == OUT_ALL_FLAGGED) {
+    if (cw.flag[blockIdx.y] == 0u) return;
+  }
+  score_valu_block<D, G, HIST, OUT>(q_pred, k, seq_lens, scores, hist, cw, Hq, Hkv, T_cap, blockIdx.x, blockIdx.y, smem);
 }
 
-template <int D, bool HIST>
+template <int D, bool HIST, int OUT>
 static hipError_t launch_score_dh(const Shape& s, const float* q_pred, const void* k, const int32_t* seq_lens,
-                                  float* scores, uint32_t* hist, hipStream_t st, hipEvent_t done) {
+                                  float* scores, uint32_t* hist, const CandWs& cw, hipStream_t st, hipEvent_t done) {
   const dim3 grid((s.T_cap + SCORE_KEYS_PER_BLOCK - 1) / SCORE_KEYS_PER_BLOCK, s.B * s.Hkv);
   const dim3 block(SCORE_THREADS);
-#define ASP_SCORE_LAUNCH(GG)                                                                                    \
-  (s.kv == 0 ? launch_recording(score_mfma_kernel<D, GG, HIST>, grid, block, st, done, q_pred,                   \
-                                static_cast<const uint16_t*>(k), seq_lens, scores, hist, s.Hq, s.Hkv, s.T_cap)   \
-             : launch_recording(score_valu_kernel<D, GG, HIST>, grid, block, st, done, q_pred,                   \
-                                static_cast<const float*>(k), seq_lens, scores, hist, s.Hq, s.Hkv, s.T_cap))
+#define ASP_SCORE_LAUNCH(GG)                                                                                      \
+  (s.kv == 0 ? launch_recording(score_mfma_kernel<D, GG, HIST, OUT>, grid, block, st, done, q_pred,                \
+                                static_cast<const uint16_t*>(k), seq_lens, scores, hist, cw, s.Hq, s.Hkv, s.T_cap) \
+             : launch_recording(score_valu_kernel<D, GG, HIST, OUT>, grid, block, st, done, q_pred,                \
+                                static_cast<const float*>(k), seq_lens, scores, hist, cw, s.Hq, s.Hkv, s.T_cap))
   hipError_t e;
   switch (s.G) {
     case 1: e = ASP_SCORE_LAUNCH(1); break;
@@ -61,11 +69,49 @@ hipError_t launch_clear_u32(uint32_t* p, size_t n, hipStream_t st) {
 hipError_t launch_score(const Shape& s, const float* q_pred, const void* k, const int32_t* seq_lens, float* scores,
                         uint32_t* hist, hipStream_t st, hipEvent_t done) {
   if (s.B == 0) return done ? hipEventRecord(done, st) : hipSuccess;
+  const CandWs none{};
   if (hist != nullptr)
-    return s.D == 64 ? launch_score_dh<64, true>(s, q_pred, k, seq_lens, scores, hist, st, done)
-                     : launch_score_dh<128, true>(s, q_pred, k, seq_lens, scores, hist, st, done);
-  return s.D == 64 ? launch_score_dh<64, false>(s, q_pred, k, seq_lens, scores, nullptr, st, done)
-                   : launch_score_dh<128, false>(s, q_pred, k, seq_lens, scores, nullptr, st, done);
+    return s.D == 64 ? launch_score_dh<64, true, OUT_SCORES>(s, q_pred, k, seq_lens, scores, hist, none, st, done)
+                     : launch_score_dh<128, true, OUT_SCORES>(s, q_pred, k, seq_lens, scores, hist, none, st, done);
+  return s.D == 64 ? launch_score_dh<64, false, OUT_SCORES>(s, q_pred, k, seq_lens, scores, nullptr, none, st, done)
+                   : launch_score_dh<128, false, OUT_SCORES>(s, q_pred, k, seq_lens, scores, nullptr, none, st, done);
+}
+
+hipError_t launch_score_candidates(const Shape& s, const float* q_pred, const void* k, const int32_t* seq_lens,
+                                   const CandWs& cw, bool fallback, hipStream_t st, hipEvent_t done) {
+  if (s.B == 0) return done ? hipEventRecord(done, st) : hipSuccess;
+  if (fallback)
+    return s.D == 64 ? launch_score_dh<64, false, OUT_ALL_FLAGGED>(s, q_pred, k, seq_lens, nullptr, nullptr, cw, st,
+                                                                    done)
+                     : launch_score_dh<128, false, OUT_ALL_FLAGGED>(s, q_pred, k, seq_lens, nullptr, nullptr, cw, st,
+                                                                     done);
+  return s.D == 64
+             ? launch_score_dh<64, false, OUT_ABOVE_HINT>(s, q_pred, k, seq_lens, nullptr, nullptr, cw, st, done)
+             : launch_score_dh<128, false, OUT_ABOVE_HINT>(s, q_pred, k, seq_lens, nullptr, nullptr, cw, st, done);
+}
+
+namespace {
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+}  // namespace
+
+size_t cand_ws_bytes(const Shape& s) {
+  const size_t units = (size_t)s.B * s.Hkv, nr = (size_t)cand_regions(s.T_cap);
+  return align256(units * 4) + align256(units * 4) + align256(units * nr * 4) +
+         align256(units * nr * CAND_REGION * sizeof(uint2));
+}
+
+CandWs cand_carve(const Shape& s, void* ws) {
+  const size_t units = (size_t)s.B * s.Hkv, nr = (size_t)cand_regions(s.T_cap);
+  unsigned char* p = static_cast<unsigned char*>(ws);
+  CandWs w;
+  w.hint = reinterpret_cast<uint32_t*>(p);
+  p += align256(units * 4);
+  w.flag = reinterpret_cast<uint32_t*>(p);
+  p += align256(units * 4);
+  w.rcount = reinterpret_cast<uint32_t*>(p);
+  p += align256(units * nr * 4);
+  w.cand = reinterpret_cast<uint2*>(p);
+  return w;
 }
 
 }  // namespace asp

@@ -29,9 +29,14 @@
 // error <= 2^-18 per term) and accumulates in fp32.
 // fp32 keys: a VALU dot product (LPK lanes per key, DPP reduction).
 //
-// Optionally each workgroup also bins its scores by the top 11 bits of the
-// order-preserving key (LDS histogram, then one global atomic per non-empty
-// bin): the first radix pass of the top-C select, done while the keys stream.
+// A block writes either every score (optionally also binning them by the top
+// 11 bits of the order-preserving key: an LDS histogram, then one global
+// atomic per non-empty bin, the first radix pass of the top-C select done
+// while the keys stream), or candidates: the (order key, index) pairs of the
+// keys at or above the unit's threshold hint, compacted per wave (ballot,
+// LDS staging) into the wave's region of CAND_REGION slots.  Writing only the
+// candidates spares the DRAM writes of the score rows, which otherwise cut into
+// the read stream.
 #pragma once
 
 #include "asp_internal.h"
@@ -54,18 +59,48 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
 constexpr int SCORE_MFMA_U = 4;     // 16-key tiles loaded per wave and iteration
 constexpr int SCORE_MFMA_SLOTS = 2;  // LDS transpose slots per wave (double buffer)
 
-// LDS of one bf16 score block: the per-wave transpose slots, then the histogram.
-template <int D, bool HIST>
+// Every wave of a block sees SCORE_KEYS_PER_BLOCK / SCORE_WAVES keys (whole
+// iterations of its loop): its candidate region.
+static_assert(SCORE_KEYS_PER_BLOCK % (SCORE_WAVES * 16 * SCORE_MFMA_U) == 0, "whole mfma iterations per wave");
+static_assert(SCORE_KEYS_PER_BLOCK / SCORE_WAVES == CAND_REGION, "one candidate region per wave");
+static_assert(SCORE_KEYS_PER_BLOCK == CAND_BLOCK_KEYS, "candidate regions follow the score blocks");
+
+// What a score block writes.
+enum ScoreOut : int {
+  OUT_SCORES = 0,       // every score (HIST: and the coarse histogram)
+  OUT_ABOVE_HINT = 1,   // candidates: the keys at or above the unit's hint
+  OUT_ALL_FLAGGED = 2,  // candidates: every key, for units flagged for rescoring
+};
+
+constexpr size_t CAND_STAGE_BYTES = (size_t)SCORE_WAVES * CAND_REGION * sizeof(uint2);
+
+// LDS of one bf16 score block: the per-wave transpose slots, then the
+// histogram or the candidate staging.
+template <int D, bool HIST, int OUT>
 constexpr size_t score_mfma_lds_bytes() {
-  return (size_t)SCORE_WAVES * SCORE_MFMA_SLOTS * 16 * (D * 2 / 16) * 16 + (HIST ? HIST_BINS * 4 : 0);
+  return (size_t)SCORE_WAVES * SCORE_MFMA_SLOTS * 16 * (D * 2 / 16) * 16 + (HIST ? HIST_BINS * 4 : 0) +
+         (OUT != OUT_SCORES ? CAND_STAGE_BYTES : 0);
 }
 
-// Score block (bx, unit) for bf16 keys; smem holds score_mfma_lds_bytes<D, HIST>().
-template <int D, int G, bool HIST>
+// Candidate region `region`: the wave's staged (key, index) pairs, then their count.
+__device__ __forceinline__ void flush_candidates(const CandWs& cw, size_t region, const uint2* stage, uint32_t kept,
+                                                 int lane) {
+  // the staging writes of every lane of the wave are visible to all of them
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  uint2* dst = cw.cand + region * CAND_REGION;
+  for (uint32_t i = (uint32_t)lane; i < kept; i += 64) dst[i] = stage[i];
+  if (lane == 0) cw.rcount[region] = kept;
+}
+
+// Score block (bx, unit) for bf16 keys; smem holds score_mfma_lds_bytes<D, HIST, OUT>().
+template <int D, int G, bool HIST, int OUT>
 __device__ __forceinline__ void score_mfma_block(const float* __restrict__ q_pred, const uint16_t* __restrict__ k,
                                                  const int32_t* __restrict__ seq_lens, float* __restrict__ scores,
-                                                 uint32_t* __restrict__ hist, int Hq, int Hkv, int T_cap, int bx,
-                                                 int unit, unsigned char* smem) {
+                                                 uint32_t* __restrict__ hist, const CandWs& cw, int Hq, int Hkv,
+                                                 int T_cap, int bx, int unit, unsigned char* smem) {
+  static_assert(!(HIST && OUT != OUT_SCORES), "the histogram goes with the score rows");
   constexpr int S = D / 32;          // MFMA steps over the coordinates
   constexpr int CH = D * 2 / 16;     // 16-byte chunks per key row
   constexpr int RPI = 64 / CH;       // key rows per wave-wide load
@@ -79,8 +114,11 @@ __device__ __forceinline__ void score_mfma_block(const float* __restrict__ q_pre
   const int T = clampi(seq_lens[b], 0, T_cap);
   const int k0 = bx * SCORE_KEYS_PER_BLOCK;
   if (k0 >= T) return;
+  const uint32_t hint = OUT == OUT_ABOVE_HINT ? cw.hint[unit] : 0u;
   const int k1 = min(k0 + SCORE_KEYS_PER_BLOCK, T);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint2* stage = reinterpret_cast<uint2*>(smem + (size_t)SCORE_WAVES * TB * 16 * CH * 16) + wave * CAND_REGION;
+  uint32_t kept = 0u;  // candidates staged by this wave (uniform)
   const int j = lane & 15, c = lane >> 4;          // MFMA roles: key column j, coordinate group c
   const int lrow = lane / CH, lchunk = lane % CH;  // load roles: row in the load, 16-byte chunk
 
@@ -156,15 +194,27 @@ __device__ __forceinline__ void score_mfma_block(const float* __restrict__ q_pre
       if constexpr (G >= 4) m = fmaxf(fmaxf(m, acc[2]), acc[3]);
       if constexpr (G == 8) m = fmaxf(m, __shfl_xor(m, 16));
       const int key = base + u * 16 + j;
-      if (c == 0 && key < k1) {
-        sb[key] = m;  // a plain store: the select launches read the row back soon after
-        if constexpr (HIST) atomicAdd(&lhist[order_key(m) >> HIST_SHIFT], 1u);
+      if constexpr (OUT == OUT_SCORES) {
+        if (c == 0 && key < k1) {
+          sb[key] = m;  // a plain store: the select launches read the row back soon after
+          if constexpr (HIST) atomicAdd(&lhist[order_key(m) >> HIST_SHIFT], 1u);
+        }
+      } else {
+        const uint32_t ok = order_key(m);
+        const bool take = c == 0 && key < k1 && ok >= hint;
+        const unsigned long long bal = __ballot(take);
+        if (take) stage[kept + lanes_below(bal)] = make_uint2(ok, (uint32_t)key);
+        kept += (uint32_t)__popcll(bal);
       }
       // Slot u % TB is written again two tiles later (or next iteration).
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
+  }
+  if constexpr (OUT != OUT_SCORES) {
+    const int nreg = cand_regions(T_cap);
+    flush_candidates(cw, (size_t)unit * nreg + (size_t)bx * SCORE_WAVES + wave, stage, kept, lane);
   }
   if constexpr (HIST) {
     __syncthreads();
@@ -176,31 +226,36 @@ __device__ __forceinline__ void score_mfma_block(const float* __restrict__ q_pre
   }
 }
 
-// LDS of one fp32 score block: the histogram.
-template <bool HIST>
+// LDS of one fp32 score block: the histogram or the candidate staging.
+template <bool HIST, int OUT>
 constexpr size_t score_valu_lds_bytes() {
-  return HIST ? HIST_BINS * 4 : 4;
+  return HIST ? HIST_BINS * 4 : (OUT != OUT_SCORES ? CAND_STAGE_BYTES : 4);
 }
 
-// Score block (bx, unit) for fp32 keys; smem holds score_valu_lds_bytes<HIST>().
-template <int D, int G, bool HIST>
+// Score block (bx, unit) for fp32 keys; smem holds score_valu_lds_bytes<HIST, OUT>().
+template <int D, int G, bool HIST, int OUT>
 __device__ __forceinline__ void score_valu_block(const float* __restrict__ q_pred, const float* __restrict__ k,
                                                  const int32_t* __restrict__ seq_lens, float* __restrict__ scores,
-                                                 uint32_t* __restrict__ hist, int Hq, int Hkv, int T_cap, int bx,
-                                                 int unit, unsigned char* smem) {
+                                                 uint32_t* __restrict__ hist, const CandWs& cw, int Hq, int Hkv,
+                                                 int T_cap, int bx, int unit, unsigned char* smem) {
+  static_assert(!(HIST && OUT != OUT_SCORES), "the histogram goes with the score rows");
   constexpr int EPL = 4;           // fp32 elements per 16-byte load
   constexpr int LPK = D / EPL;     // lanes per key row
   constexpr int KPW = 64 / LPK;    // keys per wave-wide load
   constexpr int U = 4;             // loads in flight per lane
+  static_assert(SCORE_KEYS_PER_BLOCK % (SCORE_WAVES * KPW * U) == 0, "whole iterations per wave");
   uint32_t* lhist = reinterpret_cast<uint32_t*>(smem);
 
   const int b = unit / Hkv, g = unit % Hkv;
   const int T = clampi(seq_lens[b], 0, T_cap);
   const int k0 = bx * SCORE_KEYS_PER_BLOCK;
   if (k0 >= T) return;
+  const uint32_t hint = OUT == OUT_ABOVE_HINT ? cw.hint[unit] : 0u;
   const int k1 = min(k0 + SCORE_KEYS_PER_BLOCK, T);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane % LPK, kl = lane / LPK;
+  uint2* stage = reinterpret_cast<uint2*>(smem) + wave * CAND_REGION;
+  uint32_t kept = 0u;  // candidates staged by this wave (uniform)
   if constexpr (HIST) {
     for (int i = threadIdx.x; i < HIST_BINS; i += SCORE_THREADS) lhist[i] = 0u;
     __syncthreads();
@@ -236,11 +291,23 @@ __device__ __forceinline__ void score_valu_block(const float* __restrict__ q_pre
         best = h == 0 ? acc : fmaxf(best, acc);
       }
       const int key = base + u * KPW + kl;
-      if (sub == 0 && key < k1) {
-        sb[key] = best;
-        if constexpr (HIST) atomicAdd(&lhist[order_key(best) >> HIST_SHIFT], 1u);
+      if constexpr (OUT == OUT_SCORES) {
+        if (sub == 0 && key < k1) {
+          sb[key] = best;
+          if constexpr (HIST) atomicAdd(&lhist[order_key(best) >> HIST_SHIFT], 1u);
+        }
+      } else {
+        const uint32_t ok = order_key(best);
+        const bool take = sub == 0 && key < k1 && ok >= hint;
+        const unsigned long long bal = __ballot(take);
+        if (take) stage[kept + lanes_below(bal)] = make_uint2(ok, (uint32_t)key);
+        kept += (uint32_t)__popcll(bal);
       }
     }
+  }
+  if constexpr (OUT != OUT_SCORES) {
+    const int nreg = cand_regions(T_cap);
+    flush_candidates(cw, (size_t)unit * nreg + (size_t)bx * SCORE_WAVES + wave, stage, kept, lane);
   }
   if constexpr (HIST) {
     __syncthreads();

@@ -35,6 +35,9 @@ constexpr int NBINS = HIST_BINS;
 constexpr int CAND_CAP = 8192;              // candidates staged in LDS by the finish
 constexpr int MAX_REGIONS = (1 << 22) / REGION;  // t_cap <= 2^22
 constexpr int BM_CHUNK = SEL_THREADS;       // bitmap words compacted per round
+constexpr int CAND_BATCH = 8;               // 16-byte candidate loads in flight per thread
+constexpr int CAND_STAGE_CAP = 16384;       // candidates staged in LDS by the candidate select
+static_assert(CAND_REGION % (2 * CAND_BATCH) == 0, "batches stay inside a candidate region");
 
 int select_regions(int T_cap) { return (T_cap + REGION - 1) / REGION; }
 
@@ -110,10 +113,6 @@ __device__ __forceinline__ uint32_t block_excl(uint32_t v, uint32_t* scratch, ui
   __syncthreads();
   *total = tot;
   return before + incl - v;
-}
-
-__device__ __forceinline__ uint32_t lanes_below(unsigned long long m) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 // Boundary bin of a coarse histogram, by one wave: lane l sums bins
@@ -397,6 +396,257 @@ __global__ void __launch_bounds__(SEL_THREADS) select_finish_kernel(const int32_
     }
     written += tot;
   }
+}
+
+// Selection from candidates (the rows' keys at or above a threshold hint, in
+// per-wave regions of CAND_REGION keys, written by the score launch): one
+// workgroup per unit.  The first launch takes every unit: it advances the
+// ring, flags a unit whose candidates are fewer than C_eff (its keys are then
+// all kept by a rescoring launch) and selects the others; the second launch
+// selects the flagged units.  The C_eff-th key comes from three radix digits
+// (11, 11, 10 bits) over the candidates; the output is compacted in index
+// order through two LDS bitmaps per chunk of the row, one for the keys above
+// the C_eff-th key and one for those equal to it, of which the lowest indices
+// are taken.  The next hint is the lower edge of the fine bin (top 22 bits of
+// the key, two digits) that holds the 2 C_eff-th candidate key; when fewer
+// than 2 C_eff keys were kept, the current hint moves down by the shortfall at
+// the density of the kept keys in its coarse bin (at most two coarse bins).
+__global__ void __launch_bounds__(SEL_THREADS) select_cand_kernel(const int32_t* __restrict__ seq_lens, CandWs cw,
+                                                                  int32_t* __restrict__ idx,
+                                                                  int32_t* __restrict__ n_sel,
+                                                                  int32_t* __restrict__ adv_newest,
+                                                                  int32_t* __restrict__ adv_len, int Hkv, int T_cap,
+                                                                  int C, int W, int first) {
+  __shared__ uint32_t ckey[CAND_STAGE_CAP];
+  __shared__ uint32_t cidx[CAND_STAGE_CAP];
+  __shared__ uint32_t hist[NBINS];
+  __shared__ uint32_t bm_gt[BM_CHUNK];
+  __shared__ uint32_t bm_eq[BM_CHUNK];
+  __shared__ uint32_t scratch[SEL_WAVES];
+  __shared__ uint32_t sh[4];
+
+  const int unit = blockIdx.x, b = unit / Hkv, tid = threadIdx.x;
+  const int T = clampi(seq_lens[b], 0, T_cap);
+  const int c_eff = C < T ? C : T;
+  int32_t* out = idx + (size_t)unit * C;
+
+  if (first) {
+    if (adv_newest != nullptr && unit % Hkv == 0 && tid == 0) ring_advance(adv_newest, adv_len, b, W);
+  } else if (cw.flag[unit] == 0u) {
+    return;  // selected by the first launch (uniform over the workgroup)
+  }
+  if (c_eff == T) {  // everything is selected (includes the empty row)
+    for (int j = c_eff + tid; j < C; j += SEL_THREADS) out[j] = -1;
+    for (int j = tid; j < T; j += SEL_THREADS) out[j] = j;
+    if (tid == 0) {
+      n_sel[unit] = c_eff;
+      cw.flag[unit] = 0u;
+      cw.hint[unit] = 0u;
+    }
+    return;
+  }
+  const uint32_t hint_cur = cw.hint[unit];
+
+  // Candidate count; thread t owns the regions [t*m, t*m + m) of the row.
+  const int nr = cand_regions(T);
+  const size_t rbase = (size_t)unit * cand_regions(T_cap);
+  const int m = (nr + SEL_THREADS - 1) / SEL_THREADS;
+  const int r0 = min(tid * m, nr), r1 = min(r0 + m, nr);
+  uint32_t local = 0u;
+  for (int r = r0; r < r1; ++r) local += min(cw.rcount[rbase + r], (uint32_t)CAND_REGION);
+  uint32_t n;
+  const uint32_t before = block_excl(local, scratch, &n);
+  if (first) {
+    const bool short_row = n < (uint32_t)c_eff;
+    if (tid == 0) cw.flag[unit] = short_row ? 1u : 0u;
+    if (short_row) return;  // rescored with every key kept, then selected by the second launch
+  }
+  for (int j = c_eff + tid; j < C; j += SEL_THREADS) out[j] = -1;
+  if (tid == 0) {
+    n_sel[unit] = c_eff;
+    sh[0] = 0u;
+    sh[1] = 0u;
+    sh[2] = 0xffffffffu;
+    sh[3] = 0u;
+  }
+
+  // f(key, index) for the candidates of this thread's regions, read with
+  // batches of independent 16-byte loads (two slots each) so that a region's
+  // slots arrive in a few round trips rather than one per slot.
+  auto for_own = [&](auto&& f) {
+    for (int r = r0; r < r1; ++r) {
+      const uint32_t c = min(cw.rcount[rbase + r], (uint32_t)CAND_REGION);
+      const uint4* e = reinterpret_cast<const uint4*>(cw.cand + (rbase + r) * CAND_REGION);
+      for (uint32_t i0 = 0; i0 < c; i0 += 2 * CAND_BATCH) {
+        uint4 x[CAND_BATCH];
+#pragma unroll
+        for (int j = 0; j < CAND_BATCH; ++j)
+          x[j] = i0 + 2 * j < c ? e[i0 / 2 + j] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int j = 0; j < CAND_BATCH; ++j) {
+          if (i0 + 2 * j < c) f(x[j].x, x[j].y);
+          if (i0 + 2 * j + 1 < c) f(x[j].z, x[j].w);
+        }
+      }
+    }
+  };
+  const bool staged = n <= (uint32_t)CAND_STAGE_CAP;
+  if (staged) {
+    uint32_t at = before;
+    for_own([&](uint32_t key, uint32_t pos) {
+      ckey[at] = key;
+      cidx[at] = pos;
+      ++at;
+    });
+  }
+  // f(key, index) for every candidate, each visited by one thread.
+  auto for_each = [&](auto&& f) {
+    if (staged) {
+      for (uint32_t p = tid; p < n; p += SEL_THREADS) f(ckey[p], cidx[p]);
+    } else {
+      for_own(f);
+    }
+  };
+
+  // The C_eff-th key, digit by digit: after the loop the keys above `prefix`
+  // (under pmask) are taken, with `need` more of those equal to it.
+  uint32_t prefix = 0u, pmask = 0u, need = (uint32_t)c_eff;
+  const uint32_t need2 = 2u * (uint32_t)c_eff;
+  uint32_t hint_next = 0u;
+  bool refine_hint = false;  // the 2 C_eff-th key's coarse bin is known: refine it by one digit
+  const int shifts[3] = {HIST_SHIFT, 10, 0};
+  const uint32_t dmasks[3] = {0x7ffu, 0x7ffu, 0x3ffu};
+  bool done = false;
+  for (int pass = 0; pass < 3 && !done; ++pass) {
+    for (int j = tid; j < NBINS; j += SEL_THREADS) hist[j] = 0u;
+    __syncthreads();
+    const int sft = shifts[pass];
+    const uint32_t dm = dmasks[pass];
+    for_each([&](uint32_t key, uint32_t) {
+      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sft) & dm], 1u);
+    });
+    __syncthreads();
+    // Digit d with (#keys above d) < need <= (#keys at or above d): thread t
+    // owns bins 2047-2t and 2046-2t, so a prefix over threads is a suffix over bins.
+    const int hb = NBINS - 1 - 2 * tid, lb = hb - 1;
+    const uint32_t chi = hist[hb], clo = hist[lb];
+    uint32_t tot;
+    const uint32_t ex = block_excl(chi + clo, scratch, &tot);
+    if (ex < need && need <= ex + chi) {
+      sh[0] = (uint32_t)hb;
+      sh[1] = ex;
+    } else if (ex + chi < need && need <= ex + chi + clo) {
+      sh[0] = (uint32_t)lb;
+      sh[1] = ex + chi;
+    }
+    if (pass == 0) {  // the coarse bin of the 2 C_eff-th candidate key, and the keys above it
+      if (ex < need2 && need2 <= ex + chi) {
+        sh[2] = (uint32_t)hb;
+        sh[3] = ex;
+      } else if (ex + chi < need2 && need2 <= ex + chi + clo) {
+        sh[2] = (uint32_t)lb;
+        sh[3] = ex + chi;
+      }
+    }
+    __syncthreads();
+    const uint32_t d = sh[0] & dm;
+    need -= sh[1];
+    prefix |= d << sft;
+    pmask |= dm << sft;
+    if (pass == 0) {
+      if (sh[2] != 0xffffffffu) {
+        hint_next = (sh[2] & 0x7ffu) << HIST_SHIFT;
+        refine_hint = true;
+      } else if (first) {
+        // Fewer than 2 C_eff keys kept: move the hint down by the key range
+        // that the shortfall (plus a quarter) would take at the density of
+        // the kept keys in the hint's own coarse bin; at most two coarse bins.
+        const uint32_t hb_cur = hint_cur >> HIST_SHIFT;
+        const uint64_t span = ((uint64_t)(hb_cur + 1u) << HIST_SHIFT) - hint_cur;  // kept part of that bin
+        const uint64_t c_lo = hist[hb_cur];
+        const uint64_t cap = 2ull << HIST_SHIFT;
+        const uint64_t down = c_lo ? min(span * (uint64_t)(need2 - n) * 5u / (4u * c_lo) + 1u, cap) : cap;
+        hint_next = (uint32_t)((uint64_t)hint_cur > down ? (uint64_t)hint_cur - down : 0u) & ~0x3ffu;
+      }  // else every key was kept and fewer than 2 C_eff exist: keep them all
+    }
+    done = hist[d] == need;
+    __syncthreads();
+  }
+
+  // The hint's second digit: bits 20..10 of the 2 C_eff-th candidate key, from
+  // the keys of its coarse bin (one more histogram pass over the candidates).
+  if (refine_hint) {
+    const uint32_t above = sh[3], need_h = need2 - above;
+    for (int j = tid; j < NBINS; j += SEL_THREADS) hist[j] = 0u;
+    __syncthreads();
+    for_each([&](uint32_t key, uint32_t) {
+      if ((key >> HIST_SHIFT) == (hint_next >> HIST_SHIFT)) atomicAdd(&hist[(key >> 10) & 0x7ffu], 1u);
+    });
+    __syncthreads();
+    const int hb = NBINS - 1 - 2 * tid, lb = hb - 1;
+    const uint32_t chi = hist[hb], clo = hist[lb];
+    uint32_t tot;
+    const uint32_t ex = block_excl(chi + clo, scratch, &tot);
+    if (ex < need_h && need_h <= ex + chi) sh[0] = (uint32_t)hb;
+    else if (ex + chi < need_h && need_h <= ex + chi + clo) sh[0] = (uint32_t)lb;
+    __syncthreads();
+    hint_next |= (sh[0] & 0x7ffu) << 10;
+    __syncthreads();
+  }
+
+  // Output in ascending index order, BM_CHUNK words (32 keys each) per round.
+  const int nwords = (T + 31) / 32;
+  uint32_t written = 0u, eq_seen = 0u;
+  for (int w0 = 0; w0 < nwords; w0 += BM_CHUNK) {
+    bm_gt[tid] = 0u;
+    bm_eq[tid] = 0u;
+    __syncthreads();
+    for_each([&](uint32_t key, uint32_t pos) {
+      const int wd = (int)(pos >> 5) - w0;
+      if (wd < 0 || wd >= BM_CHUNK) return;
+      const uint32_t mk = key & pmask, bit = 1u << (pos & 31u);
+      if (mk > prefix) atomicOr(&bm_gt[wd], bit);
+      else if (mk == prefix) atomicOr(&bm_eq[wd], bit);
+    });
+    __syncthreads();
+    uint32_t eqw = bm_eq[tid];
+    const uint32_t gtw = bm_gt[tid];
+    uint32_t eq_tot;
+    const uint32_t eb = eq_seen + block_excl((uint32_t)__popc(eqw), scratch, &eq_tot);
+    uint32_t take = 0u;  // the lowest set bits of eqw while fewer than `need` ties are taken
+    for (uint32_t k = eb; eqw != 0u && k < need; ++k) {
+      const uint32_t low = eqw & (0u - eqw);
+      take |= low;
+      eqw ^= low;
+    }
+    eq_seen += eq_tot;
+    uint32_t wv = gtw | take;
+    uint32_t tot;
+    uint32_t at = written + block_excl((uint32_t)__popc(wv), scratch, &tot);
+    while (wv != 0u) {
+      const int bit = __ffs((int)wv) - 1;
+      wv &= wv - 1u;
+      if (at < (uint32_t)c_eff) out[at] = (w0 + tid) * 32 + bit;
+      ++at;
+    }
+    written += tot;
+  }
+  if (tid == 0) cw.hint[unit] = hint_next;
+}
+
+hipError_t launch_select_candidates(const Shape& s, const float* q_pred, const void* k, const int32_t* seq_lens,
+                                    const CandWs& cw, int32_t* idx, int32_t* n_sel, int32_t* adv_newest,
+                                    int32_t* adv_len, hipStream_t st, hipEvent_t done) {
+  if (s.B == 0) return done ? hipEventRecord(done, st) : hipSuccess;
+  const int units = s.B * s.Hkv, W = s.W > 0 ? s.W : 1;
+  hipLaunchKernelGGL(select_cand_kernel, dim3(units), dim3(SEL_THREADS), 0, st, seq_lens, cw, idx, n_sel, adv_newest,
+                     adv_len, s.Hkv, s.T_cap, s.C, W, 1);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_score_candidates(s, q_pred, k, seq_lens, cw, true, st);
+  if (e != hipSuccess) return e;
+  return launch_recording(select_cand_kernel, dim3(units), dim3(SEL_THREADS), st, done, seq_lens, cw, idx, n_sel,
+                          adv_newest, adv_len, s.Hkv, s.T_cap, s.C, W, 0);
 }
 
 hipError_t launch_select(const Shape& s, const float* scores, const uint32_t* hist, const int32_t* seq_lens,

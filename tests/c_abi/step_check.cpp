@@ -106,9 +106,10 @@ int main() {
 
   // History, then the bootstrap step, identical for both copies.
   for (auto& l : L) {
-    for (int t = 0; t < W - 1; ++t) {
-      CHECK_HIP(hipMemcpy(l.q, qs.data() + (size_t)t * q_n, q_n * 4, hipMemcpyHostToDevice));
+    for (int t = 0; t < W - 1; ++t) {  // the copy and the push in one stream's order
+      CHECK_HIP(hipMemcpyAsync(l.q, qs.data() + (size_t)t * q_n, q_n * 4, hipMemcpyHostToDevice, attn));
       CHECK_ASP(asp_push_query(&d, &c, l.q, l.q_hist, l.newest, l.len, attn));
+      CHECK_HIP(hipStreamSynchronize(attn));
     }
     CHECK_HIP(hipMemcpyAsync(l.q, qs.data() + (size_t)(W - 1) * q_n, q_n * 4, hipMemcpyHostToDevice, attn));
     CHECK_ASP(asp_step(&d, &c, l.q, l.q_hist, l.newest, l.len, k, v, lens, nullptr, nullptr, l.idx[0], l.nsel[0],
@@ -119,6 +120,23 @@ int main() {
   std::vector<float> o0(q_n), o1(q_n);
   std::vector<int32_t> i0((size_t)B * Hkv * C), i1((size_t)B * Hkv * C), n0(B * Hkv), n1(B * Hkv);
   std::vector<float> h0((size_t)B * Hq * W * D), h1((size_t)B * Hq * W * D);
+  {  // the bootstrap steps agree too
+    CHECK_HIP(hipMemcpy(o0.data(), L[0].out, q_n * 4, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(o1.data(), L[1].out, q_n * 4, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(i0.data(), L[0].idx[0], i0.size() * 4, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(i1.data(), L[1].idx[0], i1.size() * 4, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(n0.data(), L[0].nsel[0], n0.size() * 4, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(n1.data(), L[1].nsel[0], n1.size() * 4, hipMemcpyDeviceToHost));
+    const bool same_out = std::memcmp(o0.data(), o1.data(), q_n * 4) == 0;
+    const bool same_idx = std::memcmp(i0.data(), i1.data(), i0.size() * 4) == 0;
+    const bool same_n = std::memcmp(n0.data(), n1.data(), n0.size() * 4) == 0;
+    std::printf("bootstrap: %s\n", same_out && same_idx && same_n ? "agree" : "DIFFER");
+    if (!(same_out && same_idx && same_n)) {
+      std::printf("  out %s, idx %s, n_sel %s\n", same_out ? "same" : "differs", same_idx ? "same" : "differs",
+                  same_n ? "same" : "differs");
+      return 1;
+    }
+  }
   for (int s = 0; s < steps; ++s) {
     const int cur = s % 2, nxt = 1 - cur;
     const float* qsrc = qs.data() + (size_t)(W + s) * q_n;
@@ -141,14 +159,24 @@ int main() {
     CHECK_HIP(hipMemcpy(n1.data(), L[1].nsel[nxt], n1.size() * 4, hipMemcpyDeviceToHost));
     CHECK_HIP(hipMemcpy(h0.data(), L[0].q_hist, h0.size() * 4, hipMemcpyDeviceToHost));
     CHECK_HIP(hipMemcpy(h1.data(), L[1].q_hist, h1.size() * 4, hipMemcpyDeviceToHost));
-    const bool same = std::memcmp(o0.data(), o1.data(), q_n * 4) == 0 &&
-                      std::memcmp(i0.data(), i1.data(), i0.size() * 4) == 0 &&
-                      std::memcmp(n0.data(), n1.data(), n0.size() * 4) == 0 &&
-                      std::memcmp(h0.data(), h1.data(), h0.size() * 4) == 0;
+    const bool same_out = std::memcmp(o0.data(), o1.data(), q_n * 4) == 0;
+    const bool same_idx = std::memcmp(i0.data(), i1.data(), i0.size() * 4) == 0;
+    const bool same_n = std::memcmp(n0.data(), n1.data(), n0.size() * 4) == 0;
+    const bool same_ring = std::memcmp(h0.data(), h1.data(), h0.size() * 4) == 0;
+    const bool same = same_out && same_idx && same_n && same_ring;
     int sel_total = 0;
     for (int x : n0) sel_total += x;
     std::printf("step %d: one stream and two streams %s (selected %d tokens)\n", s, same ? "agree" : "DIFFER",
                 sel_total);
+    if (!same) {
+      std::printf("  out %s, idx %s, n_sel %s, ring %s\n", same_out ? "same" : "differs",
+                  same_idx ? "same" : "differs", same_n ? "same" : "differs", same_ring ? "same" : "differs");
+      for (size_t i = 0; i < i0.size(); ++i)
+        if (i0[i] != i1[i]) {
+          std::printf("  first idx difference at unit %zu slot %zu: %d vs %d\n", i / C, i % C, i0[i], i1[i]);
+          break;
+        }
+    }
     if (!same) return 1;
   }
   CHECK_ASP(asp_release_streams());

@@ -29,7 +29,8 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "asp_workspace_size", "asp_status_string", "asp_push_query", "asp_predict_query", "asp_score_keys",
-        "asp_select_topc", "asp_sparse_decode", "asp_step", "asp_selection_overlap", "asp_release_streams"])
+        "asp_select_topc", "asp_score_candidates", "asp_select_candidates", "asp_sparse_decode", "asp_step",
+        "asp_selection_overlap", "asp_release_streams"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -65,9 +66,16 @@ def test_workspace_sizes(lib):
     dec = A.asp_workspace_size(d, c, A.OP_DECODE)
     step = A.asp_workspace_size(d, c, A.OP_STEP)
     assert dec > 0 and dec % 256 == 0
-    # the step holds the predicted queries, the score rows and the attention partials
-    assert step >= 8 * 32 * 128 * 4 + 8 * 8 * 32768 * 4 + dec
+    cand = A.asp_workspace_size(d, c, A.OP_CANDIDATES)
+    # hints and flags per unit, a count per 128-key region, an 8-byte slot per key
+    assert cand % 256 == 0 and cand >= 8 * 8 * (4 + 4 + (32768 // 128) * 4 + 32768 * 8)
+    # the step holds the candidate workspace, the predicted queries and the attention partials
+    assert step >= cand + 8 * 32 * 128 * 4 + dec
     assert A.asp_workspace_size(_dims(head_dim=96), c, A.OP_STEP) == 0
+    assert A.asp_workspace_size(_dims(head_dim=96), c, A.OP_CANDIDATES) == 0
+    # a ragged t_cap rounds up to whole 512-key score blocks
+    c7 = A.Cfg(16, 64, 1e-2)
+    assert A.asp_workspace_size(_dims(t_cap=700), c7, A.OP_CANDIDATES) >= 8 * 8 * (1024 // 128) * (4 + 128 * 8)
 
 
 BAD_DIMS = [
@@ -132,6 +140,21 @@ def test_null_pointers_and_short_workspace_rejected(lib):
     assert _call_select(lib, d, c, ctypes.c_void_p(256), need_sel - 1) == 3
     assert _call_decode(lib, d, c, ctypes.c_void_p(256), need - 1) == 3
     assert lib.asp_score_keys(None, None, None, None, None, None, None) == 1
+    # candidate route: missing, short or misaligned workspace; null outputs
+    need_c = A.asp_workspace_size(d, c, A.OP_CANDIDATES)
+    for ws, nb in ((None, 0), (ctypes.c_void_p(256), need_c - 1), (ctypes.c_void_p(264), need_c)):
+        assert lib.asp_score_candidates(ctypes.byref(d), ctypes.byref(c), ctypes.c_void_p(16), ctypes.c_void_p(16),
+                                        ctypes.c_void_p(16), ws, nb, None) == 3
+        assert lib.asp_select_candidates(ctypes.byref(d), ctypes.byref(c), ctypes.c_void_p(16), ctypes.c_void_p(16),
+                                         ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16), ws, nb,
+                                         None) == 3
+    assert lib.asp_score_candidates(ctypes.byref(d), ctypes.byref(c), None, ctypes.c_void_p(16), ctypes.c_void_p(16),
+                                    ctypes.c_void_p(256), need_c, None) == 1
+    assert lib.asp_select_candidates(ctypes.byref(d), ctypes.byref(c), ctypes.c_void_p(16), ctypes.c_void_p(16),
+                                     ctypes.c_void_p(16), None, ctypes.c_void_p(16), ctypes.c_void_p(256), need_c,
+                                     None) == 1
+    assert lib.asp_score_candidates(ctypes.byref(d), ctypes.byref(A.Cfg(6, 64, 1e-2)), ctypes.c_void_p(16),
+                                    ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(256), need_c, None) == 1
     one = ctypes.c_void_p(16)
     # asp_step: idx_cur without n_sel_cur; missing workspace
     args = [ctypes.byref(d), ctypes.byref(c)] + [one] * 7  # q_cur .. seq_lens

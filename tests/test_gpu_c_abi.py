@@ -21,4 +21,5 @@ def test_c_abi_pipelined_steps_agree_across_stream_modes():
     print(r.stdout, r.stderr, flush=True)
     assert r.returncode == 0, r.stderr
     assert "c-abi step check: ok" in r.stdout
-    assert r.stdout.count("agree") == 6
+    assert r.stdout.count("one stream and two streams agree") == 6
+    assert "bootstrap: agree" in r.stdout

@@ -68,12 +68,14 @@ def _full_shape_check(p: Problem, units):
     q_ready = A.HipEvent()
     attn, sel = torch.cuda.Stream(), torch.cuda.Stream()
     attn.wait_stream(torch.cuda.current_stream())
-    A.asp_step(d, c, q0.to(DEV), p.q_hist, p.newest, p.length, p.k, p.v, p.seq_lens, None, None, idx[0], nsel[0],
+    q0d, q1d = q0.to(DEV), q1.to(DEV)  # held until the streams are done with them
+    attn.wait_stream(torch.cuda.current_stream())
+    A.asp_step(d, c, q0d, p.q_hist, p.newest, p.length, p.k, p.v, p.seq_lens, None, None, idx[0], nsel[0],
                p.out, ws, attn_stream=attn, idx_next_ready=ev[0])
     torch.cuda.synchronize()
     got0 = _snap(p, idx[0], nsel[0])
     assert np.array_equal(np_(p.q_hist), np_(ring1[0]))
-    A.asp_step(d, c, q1.to(DEV), p.q_hist, p.newest, p.length, p.k, p.v, p.seq_lens, idx[0], nsel[0], idx[1],
+    A.asp_step(d, c, q1d, p.q_hist, p.newest, p.length, p.k, p.v, p.seq_lens, idx[0], nsel[0], idx[1],
                nsel[1], p.out, ws, attn_stream=attn, sel_stream=sel, q_ready=q_ready, idx_cur_ready=ev[0],
                idx_next_ready=ev[1])
     torch.cuda.synchronize()

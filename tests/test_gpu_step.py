@@ -129,10 +129,11 @@ def test_qwen3_8b_layer_full_shape_staged():
     _staged_check(p, p.queries[wl.history_steps])
 
 
-def _step_run(p: Problem, mode: str, n_steps: int, release_after=None):
+def _step_run(p: Problem, mode: str, n_steps: int, release_after=None, hints=None):
     """Run n_steps decode steps with asp_step in `mode`; return per-step outputs.
     release_after: step after which the library's streams are released (the
-    next two-stream step creates them again)."""
+    next two-stream step creates them again).  hints: {step: value} written
+    over the workspace's per-unit threshold hints after that step."""
     wl, d, c = p.wl, p.dims, p.cfg
     B, Hkv, C = wl.batch, wl.n_kv_heads, wl.top_c
     ws = torch.empty(A.asp_workspace_size(d, c, A.OP_STEP), dtype=torch.uint8, device=DEV)
@@ -161,6 +162,9 @@ def _step_run(p: Problem, mode: str, n_steps: int, release_after=None):
                         np_(p.newest).copy(), np_(p.length).copy()))
         if s == release_after:
             A.asp_release_streams()
+        if hints and s in hints:
+            ws[:4 * B * Hkv].view(torch.int32).fill_(hints[s])
+            torch.cuda.synchronize()
     return results
 
 
@@ -214,7 +218,8 @@ def test_step_modes_bit_identical_to_entry_points(wl_name):
     wl = wk.CONFIGS.get(wl_name) or SMALL_STEP_CASES[wl_name]
     n = 5
     runs = {}
-    for mode in ("manual", "one_stream", "two_streams", "two_streams_release"):
+    modes = ("one_stream", "two_streams", "two_streams_release", "two_streams_hints", "one_stream_hints")
+    for mode in ("manual",) + modes:
         p = Problem(wl, kv_device=DEV if wl.batch > 1 else "cpu", n_steps=n, lens=STEP_LENS.get(wl_name))
         p.fill_history()
         torch.cuda.synchronize()
@@ -222,9 +227,11 @@ def test_step_modes_bit_identical_to_entry_points(wl_name):
             runs[mode] = _manual_run(p, n)
         elif mode == "two_streams_release":  # the library's streams released mid-run and created again
             runs[mode] = _step_run(p, "two_streams", n, release_after=2)
+        elif mode.endswith("_hints"):  # hints that keep nothing (every unit rescored), then every key
+            runs[mode] = _step_run(p, mode[:-len("_hints")], n, hints={0: -1, 1: 0, 3: -1})
         else:
             runs[mode] = _step_run(p, mode, n)
-    for mode in ("one_stream", "two_streams", "two_streams_release"):
+    for mode in modes:
         for s in range(n):
             for a, b in zip(runs["manual"][s], runs[mode][s]):
                 np.testing.assert_array_equal(a, b, err_msg="%s step %d" % (mode, s))
@@ -258,9 +265,14 @@ def test_two_stream_layer_rotation_matches_entry_points(wl_name, L, n):
     attn, sel = torch.cuda.Stream(), torch.cuda.Stream()
     attn.wait_stream(torch.cuda.current_stream())
     got = [[] for _ in range(L)]
+    # every step's query stays allocated until the end: the streams read it
+    # long after the host has moved on (a freed block could be refilled by the
+    # next upload on the default stream while a step still reads it)
+    alive = []
     for s in range(n):
         for l, p in enumerate(probs):  # one step of every layer, in layer order, nothing synchronised
             q = p.queries[base.history_steps + s].to(DEV)
+            alive.append(q)
             cur, nxt = s % 2, (s + 1) % 2
             attn.wait_stream(torch.cuda.current_stream())
             if s == 0:
