@@ -12,10 +12,16 @@ __global__ void __launch_bounds__(SCORE_THREADS) score_mfma_kernel(const float* 
                                                                    int Hkv, int T_cap) {
   __shared__ __align__(16) unsigned char smem[score_mfma_lds_bytes<D, HIST, OUT>()];
   // The rescoring launch follows every selection and usually finds no unit
-  // flagged: its workgroups then leave before touching anything else.
+  // flagged: its workgroups (a few per unit) then leave at once; those of a
+  // flagged unit loop over its key blocks.
   if constexpr (OUT == OUT_ALL_FLAGGED) {
     if (cw.flag[blockIdx.y] == 0u) return;
+    const int nblk = (T_cap + SCORE_KEYS_PER_BLOCK - 1) / SCORE_KEYS_PER_BLOCK;
+    for (int bx = blockIdx.x; bx < nblk; bx += gridDim.x)
+      score_mfma_block<D, G, HIST, OUT>(q_pred, k, seq_lens, scores, hist, cw, Hq, Hkv, T_cap, bx, blockIdx.y, smem);
+    return;
   }
+  // Otherwise one key block per workgroup: a loop here slows the launch inside the step.
   score_mfma_block<D, G, HIST, OUT>(q_pred, k, seq_lens, scores, hist, cw, Hq, Hkv, T_cap, blockIdx.x, blockIdx.y, smem);
 }
 
@@ -29,14 +35,23 @@ __global__ void __launch_bounds__(SCORE_THREADS) score_valu_kernel(const float* 
   __shared__ __align__(16) unsigned char smem[score_valu_lds_bytes<HIST, OUT>()];
   if constexpr (OUT == OUT_ALL_FLAGGED) {
     if (cw.flag[blockIdx.y] == 0u) return;
+    const int nblk = (T_cap + SCORE_KEYS_PER_BLOCK - 1) / SCORE_KEYS_PER_BLOCK;
+    for (int bx = blockIdx.x; bx < nblk; bx += gridDim.x)
+      score_valu_block<D, G, HIST, OUT>(q_pred, k, seq_lens, scores, hist, cw, Hq, Hkv, T_cap, bx, blockIdx.y, smem);
+    return;
   }
   score_valu_block<D, G, HIST, OUT>(q_pred, k, seq_lens, scores, hist, cw, Hq, Hkv, T_cap, blockIdx.x, blockIdx.y, smem);
 }
 
+// Workgroups per unit of the rescoring launch.
+constexpr int RESCORE_BLOCKS_PER_UNIT = 4;
+
 template <int D, bool HIST, int OUT>
 static hipError_t launch_score_dh(const Shape& s, const float* q_pred, const void* k, const int32_t* seq_lens,
                                   float* scores, uint32_t* hist, const CandWs& cw, hipStream_t st, hipEvent_t done) {
-  const dim3 grid((s.T_cap + SCORE_KEYS_PER_BLOCK - 1) / SCORE_KEYS_PER_BLOCK, s.B * s.Hkv);
+  const int nblk = (s.T_cap + SCORE_KEYS_PER_BLOCK - 1) / SCORE_KEYS_PER_BLOCK;
+  const int gx = OUT == OUT_ALL_FLAGGED && nblk > RESCORE_BLOCKS_PER_UNIT ? RESCORE_BLOCKS_PER_UNIT : nblk;
+  const dim3 grid(gx, s.B * s.Hkv);
   const dim3 block(SCORE_THREADS);
 #define ASP_SCORE_LAUNCH(GG)                                                                                      \
   (s.kv == 0 ? launch_recording(score_mfma_kernel<D, GG, HIST, OUT>, grid, block, st, done, q_pred,                \

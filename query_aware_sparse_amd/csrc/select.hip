@@ -36,7 +36,6 @@ constexpr int CAND_CAP = 8192;              // candidates staged in LDS by the f
 constexpr int MAX_REGIONS = (1 << 22) / REGION;  // t_cap <= 2^22
 constexpr int BM_CHUNK = SEL_THREADS;       // bitmap words compacted per round
 constexpr int CAND_BATCH = 8;               // 16-byte candidate loads in flight per thread
-constexpr int CAND_STAGE_CAP = 16384;       // candidates staged in LDS by the candidate select
 static_assert(CAND_REGION % (2 * CAND_BATCH) == 0, "batches stay inside a candidate region");
 
 int select_regions(int T_cap) { return (T_cap + REGION - 1) / REGION; }
@@ -398,11 +397,64 @@ __global__ void __launch_bounds__(SEL_THREADS) select_finish_kernel(const int32_
   }
 }
 
+// Exclusive scan over a workgroup of NT threads; *total receives the sum.  Two barriers.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_n(uint32_t v, uint32_t* scratch, uint32_t* total) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_scan(v);
+  if (lane == 63) scratch[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0u, tot = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t x = scratch[w];
+    before += w < wave ? x : 0u;
+    tot += x;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + incl - v;
+}
+
+// Digit of a 2048-bin histogram that holds the need-th key from the top, by NT
+// threads: thread t owns the bins [2048 - PB(t+1), 2048 - PB t) (PB = 2048 / NT)
+// and walks them from the highest.  For rank need_a, sh[0] = digit and sh[1] =
+// the keys in higher bins; for need_b (0: none), sh[2] and sh[3].  A rank past
+// the histogram's total leaves its slots as they were.  Barriers: those of
+// block_excl_n.
+template <int NT>
+__device__ __forceinline__ void pick_digits(const uint32_t* hist, uint32_t need_a, uint32_t need_b,
+                                            uint32_t* scratch, uint32_t* sh) {
+  constexpr int PB = NBINS / NT;
+  const int top = NBINS - 1 - PB * (int)threadIdx.x;
+  uint32_t c[PB], sum = 0u;
+#pragma unroll
+  for (int j = 0; j < PB; ++j) {
+    c[j] = hist[top - j];
+    sum += c[j];
+  }
+  uint32_t tot;
+  uint32_t acc = block_excl_n<NT>(sum, scratch, &tot);
+#pragma unroll
+  for (int j = 0; j < PB; ++j) {
+    if (acc < need_a && need_a <= acc + c[j]) {
+      sh[0] = (uint32_t)(top - j);
+      sh[1] = acc;
+    }
+    if (acc < need_b && need_b <= acc + c[j]) {
+      sh[2] = (uint32_t)(top - j);
+      sh[3] = acc;
+    }
+    acc += c[j];
+  }
+}
+
 // Selection from candidates (the rows' keys at or above a threshold hint, in
 // per-wave regions of CAND_REGION keys, written by the score launch): one
-// workgroup per unit.  The first launch takes every unit: it advances the
-// ring, flags a unit whose candidates are fewer than C_eff (its keys are then
-// all kept by a rescoring launch) and selects the others; the second launch
+// workgroup of CAND_SEL_THREADS per unit.  The first launch takes every unit: it advances the ring,
+// flags a unit whose candidates are fewer than C_eff (its keys are then all
+// kept by a rescoring launch) and selects the others; the second launch
 // selects the flagged units.  The C_eff-th key comes from three radix digits
 // (11, 11, 10 bits) over the candidates; the output is compacted in index
 // order through two LDS bitmaps per chunk of the row, one for the keys above
@@ -411,18 +463,26 @@ __global__ void __launch_bounds__(SEL_THREADS) select_finish_kernel(const int32_
 // the key, two digits) that holds the 2 C_eff-th candidate key; when fewer
 // than 2 C_eff keys were kept, the current hint moves down by the shortfall at
 // the density of the kept keys in its coarse bin (at most two coarse bins).
-__global__ void __launch_bounds__(SEL_THREADS) select_cand_kernel(const int32_t* __restrict__ seq_lens, CandWs cw,
-                                                                  int32_t* __restrict__ idx,
-                                                                  int32_t* __restrict__ n_sel,
-                                                                  int32_t* __restrict__ adv_newest,
-                                                                  int32_t* __restrict__ adv_len, int Hkv, int T_cap,
-                                                                  int C, int W, int first) {
-  __shared__ uint32_t ckey[CAND_STAGE_CAP];
-  __shared__ uint32_t cidx[CAND_STAGE_CAP];
+// CAP: candidates staged in LDS (0: none, every pass reads them from memory).
+// The LDS a workgroup holds is taken from the concurrent score launches, so
+// the first launch sizes CAP to the budget and the second one, which usually
+// finds no unit flagged, stages nothing.
+constexpr int CAND_SEL_THREADS = 1024;
+template <int CAP>
+__global__ void __launch_bounds__(CAND_SEL_THREADS) select_cand_kernel(const int32_t* __restrict__ seq_lens,
+                                                                       CandWs cw, int32_t* __restrict__ idx,
+                                                                       int32_t* __restrict__ n_sel,
+                                                                       int32_t* __restrict__ adv_newest,
+                                                                       int32_t* __restrict__ adv_len, int Hkv,
+                                                                       int T_cap, int C, int W, int first) {
+  constexpr int NT = CAND_SEL_THREADS;
+  constexpr int CHUNK = NT;  // bitmap words (32 keys each) compacted per round
+  __shared__ uint32_t ckey[CAP > 0 ? CAP : 1];
+  __shared__ uint32_t cidx[CAP > 0 ? CAP : 1];
   __shared__ uint32_t hist[NBINS];
-  __shared__ uint32_t bm_gt[BM_CHUNK];
-  __shared__ uint32_t bm_eq[BM_CHUNK];
-  __shared__ uint32_t scratch[SEL_WAVES];
+  __shared__ uint32_t bm_gt[CHUNK];
+  __shared__ uint32_t bm_eq[CHUNK];
+  __shared__ uint32_t scratch[NT / 64];
   __shared__ uint32_t sh[4];
 
   const int unit = blockIdx.x, b = unit / Hkv, tid = threadIdx.x;
@@ -436,8 +496,8 @@ __global__ void __launch_bounds__(SEL_THREADS) select_cand_kernel(const int32_t*
     return;  // selected by the first launch (uniform over the workgroup)
   }
   if (c_eff == T) {  // everything is selected (includes the empty row)
-    for (int j = c_eff + tid; j < C; j += SEL_THREADS) out[j] = -1;
-    for (int j = tid; j < T; j += SEL_THREADS) out[j] = j;
+    for (int j = c_eff + tid; j < C; j += NT) out[j] = -1;
+    for (int j = tid; j < T; j += NT) out[j] = j;
     if (tid == 0) {
       n_sel[unit] = c_eff;
       cw.flag[unit] = 0u;
@@ -450,18 +510,18 @@ __global__ void __launch_bounds__(SEL_THREADS) select_cand_kernel(const int32_t*
   // Candidate count; thread t owns the regions [t*m, t*m + m) of the row.
   const int nr = cand_regions(T);
   const size_t rbase = (size_t)unit * cand_regions(T_cap);
-  const int m = (nr + SEL_THREADS - 1) / SEL_THREADS;
+  const int m = (nr + NT - 1) / NT;
   const int r0 = min(tid * m, nr), r1 = min(r0 + m, nr);
   uint32_t local = 0u;
   for (int r = r0; r < r1; ++r) local += min(cw.rcount[rbase + r], (uint32_t)CAND_REGION);
   uint32_t n;
-  const uint32_t before = block_excl(local, scratch, &n);
+  const uint32_t before = block_excl_n<NT>(local, scratch, &n);
   if (first) {
     const bool short_row = n < (uint32_t)c_eff;
     if (tid == 0) cw.flag[unit] = short_row ? 1u : 0u;
     if (short_row) return;  // rescored with every key kept, then selected by the second launch
   }
-  for (int j = c_eff + tid; j < C; j += SEL_THREADS) out[j] = -1;
+  for (int j = c_eff + tid; j < C; j += NT) out[j] = -1;
   if (tid == 0) {
     n_sel[unit] = c_eff;
     sh[0] = 0u;
@@ -490,7 +550,7 @@ __global__ void __launch_bounds__(SEL_THREADS) select_cand_kernel(const int32_t*
       }
     }
   };
-  const bool staged = n <= (uint32_t)CAND_STAGE_CAP;
+  const bool staged = CAP > 0 && n <= (uint32_t)CAP;
   if (staged) {
     uint32_t at = before;
     for_own([&](uint32_t key, uint32_t pos) {
@@ -502,7 +562,7 @@ __global__ void __launch_bounds__(SEL_THREADS) select_cand_kernel(const int32_t*
   // f(key, index) for every candidate, each visited by one thread.
   auto for_each = [&](auto&& f) {
     if (staged) {
-      for (uint32_t p = tid; p < n; p += SEL_THREADS) f(ckey[p], cidx[p]);
+      for (uint32_t p = tid; p < n; p += NT) f(ckey[p], cidx[p]);
     } else {
       for_own(f);
     }
@@ -518,7 +578,7 @@ __global__ void __launch_bounds__(SEL_THREADS) select_cand_kernel(const int32_t*
   const uint32_t dmasks[3] = {0x7ffu, 0x7ffu, 0x3ffu};
   bool done = false;
   for (int pass = 0; pass < 3 && !done; ++pass) {
-    for (int j = tid; j < NBINS; j += SEL_THREADS) hist[j] = 0u;
+    for (int j = tid; j < NBINS; j += NT) hist[j] = 0u;
     __syncthreads();
     const int sft = shifts[pass];
     const uint32_t dm = dmasks[pass];
@@ -526,28 +586,8 @@ __global__ void __launch_bounds__(SEL_THREADS) select_cand_kernel(const int32_t*
       if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sft) & dm], 1u);
     });
     __syncthreads();
-    // Digit d with (#keys above d) < need <= (#keys at or above d): thread t
-    // owns bins 2047-2t and 2046-2t, so a prefix over threads is a suffix over bins.
-    const int hb = NBINS - 1 - 2 * tid, lb = hb - 1;
-    const uint32_t chi = hist[hb], clo = hist[lb];
-    uint32_t tot;
-    const uint32_t ex = block_excl(chi + clo, scratch, &tot);
-    if (ex < need && need <= ex + chi) {
-      sh[0] = (uint32_t)hb;
-      sh[1] = ex;
-    } else if (ex + chi < need && need <= ex + chi + clo) {
-      sh[0] = (uint32_t)lb;
-      sh[1] = ex + chi;
-    }
-    if (pass == 0) {  // the coarse bin of the 2 C_eff-th candidate key, and the keys above it
-      if (ex < need2 && need2 <= ex + chi) {
-        sh[2] = (uint32_t)hb;
-        sh[3] = ex;
-      } else if (ex + chi < need2 && need2 <= ex + chi + clo) {
-        sh[2] = (uint32_t)lb;
-        sh[3] = ex + chi;
-      }
-    }
+    // pass 0 also locates the coarse bin of the 2 C_eff-th candidate key
+    pick_digits<NT>(hist, need, pass == 0 ? need2 : 0u, scratch, sh);
     __syncthreads();
     const uint32_t d = sh[0] & dm;
     need -= sh[1];
@@ -576,34 +616,29 @@ __global__ void __launch_bounds__(SEL_THREADS) select_cand_kernel(const int32_t*
   // The hint's second digit: bits 20..10 of the 2 C_eff-th candidate key, from
   // the keys of its coarse bin (one more histogram pass over the candidates).
   if (refine_hint) {
-    const uint32_t above = sh[3], need_h = need2 - above;
-    for (int j = tid; j < NBINS; j += SEL_THREADS) hist[j] = 0u;
+    const uint32_t need_h = need2 - sh[3];
+    for (int j = tid; j < NBINS; j += NT) hist[j] = 0u;
     __syncthreads();
     for_each([&](uint32_t key, uint32_t) {
       if ((key >> HIST_SHIFT) == (hint_next >> HIST_SHIFT)) atomicAdd(&hist[(key >> 10) & 0x7ffu], 1u);
     });
     __syncthreads();
-    const int hb = NBINS - 1 - 2 * tid, lb = hb - 1;
-    const uint32_t chi = hist[hb], clo = hist[lb];
-    uint32_t tot;
-    const uint32_t ex = block_excl(chi + clo, scratch, &tot);
-    if (ex < need_h && need_h <= ex + chi) sh[0] = (uint32_t)hb;
-    else if (ex + chi < need_h && need_h <= ex + chi + clo) sh[0] = (uint32_t)lb;
+    pick_digits<NT>(hist, need_h, 0u, scratch, sh);
     __syncthreads();
     hint_next |= (sh[0] & 0x7ffu) << 10;
     __syncthreads();
   }
 
-  // Output in ascending index order, BM_CHUNK words (32 keys each) per round.
+  // Output in ascending index order, CHUNK words (32 keys each) per round.
   const int nwords = (T + 31) / 32;
   uint32_t written = 0u, eq_seen = 0u;
-  for (int w0 = 0; w0 < nwords; w0 += BM_CHUNK) {
+  for (int w0 = 0; w0 < nwords; w0 += CHUNK) {
     bm_gt[tid] = 0u;
     bm_eq[tid] = 0u;
     __syncthreads();
     for_each([&](uint32_t key, uint32_t pos) {
       const int wd = (int)(pos >> 5) - w0;
-      if (wd < 0 || wd >= BM_CHUNK) return;
+      if (wd < 0 || wd >= CHUNK) return;
       const uint32_t mk = key & pmask, bit = 1u << (pos & 31u);
       if (mk > prefix) atomicOr(&bm_gt[wd], bit);
       else if (mk == prefix) atomicOr(&bm_eq[wd], bit);
@@ -612,7 +647,7 @@ __global__ void __launch_bounds__(SEL_THREADS) select_cand_kernel(const int32_t*
     uint32_t eqw = bm_eq[tid];
     const uint32_t gtw = bm_gt[tid];
     uint32_t eq_tot;
-    const uint32_t eb = eq_seen + block_excl((uint32_t)__popc(eqw), scratch, &eq_tot);
+    const uint32_t eb = eq_seen + block_excl_n<NT>((uint32_t)__popc(eqw), scratch, &eq_tot);
     uint32_t take = 0u;  // the lowest set bits of eqw while fewer than `need` ties are taken
     for (uint32_t k = eb; eqw != 0u && k < need; ++k) {
       const uint32_t low = eqw & (0u - eqw);
@@ -622,7 +657,7 @@ __global__ void __launch_bounds__(SEL_THREADS) select_cand_kernel(const int32_t*
     eq_seen += eq_tot;
     uint32_t wv = gtw | take;
     uint32_t tot;
-    uint32_t at = written + block_excl((uint32_t)__popc(wv), scratch, &tot);
+    uint32_t at = written + block_excl_n<NT>((uint32_t)__popc(wv), scratch, &tot);
     while (wv != 0u) {
       const int bit = __ffs((int)wv) - 1;
       wv &= wv - 1u;
@@ -634,19 +669,53 @@ __global__ void __launch_bounds__(SEL_THREADS) select_cand_kernel(const int32_t*
   if (tid == 0) cw.hint[unit] = hint_next;
 }
 
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    cached[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+  }
+  return cached[dev];
+}
+
 hipError_t launch_select_candidates(const Shape& s, const float* q_pred, const void* k, const int32_t* seq_lens,
                                     const CandWs& cw, int32_t* idx, int32_t* n_sel, int32_t* adv_newest,
                                     int32_t* adv_len, hipStream_t st, hipEvent_t done) {
   if (s.B == 0) return done ? hipEventRecord(done, st) : hipSuccess;
   const int units = s.B * s.Hkv, W = s.W > 0 ? s.W : 1;
-  hipLaunchKernelGGL(select_cand_kernel, dim3(units), dim3(SEL_THREADS), 0, st, seq_lens, cw, idx, n_sel, adv_newest,
-                     adv_len, s.Hkv, s.T_cap, s.C, W, 1);
+  // LDS of the first launch.  With few units (at most one workgroup per two
+  // CUs) each workgroup takes a CU's whole LDS, which keeps the concurrent
+  // score blocks off that CU: measured faster than sharing the CU with them
+  // (64 units: 101.6 against 103.3 us per step; 128 units: 209.5 against
+  // 210.3 us).  With more units that would take every CU from the score
+  // launch (256 units: 240 against 228 us), so the stage is sized for about
+  // 3 C candidates (a selection keeps some 2 C, the rest is room for the drift
+  // of the scores between steps).
+  const int want = 2 * units <= device_cus() ? 16384 : 3 * s.C;
+#define ASP_SEL_FIRST(CAPV)                                                                                 \
+  hipLaunchKernelGGL(select_cand_kernel<CAPV>, dim3(units), dim3(CAND_SEL_THREADS), 0, st, seq_lens, cw, idx, \
+                     n_sel, adv_newest, adv_len, s.Hkv, s.T_cap, s.C, W, 1)
+  switch ((want + 2047) / 2048) {  // LDS in steps of 2048 candidates (16 KiB), at most 16384
+    case 0:
+    case 1: ASP_SEL_FIRST(2048); break;
+    case 2: ASP_SEL_FIRST(4096); break;
+    case 3: ASP_SEL_FIRST(6144); break;
+    case 4: ASP_SEL_FIRST(8192); break;
+    case 5: ASP_SEL_FIRST(10240); break;
+    case 6: ASP_SEL_FIRST(12288); break;
+    case 7: ASP_SEL_FIRST(14336); break;
+    default: ASP_SEL_FIRST(16384); break;
+  }
+#undef ASP_SEL_FIRST
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = launch_score_candidates(s, q_pred, k, seq_lens, cw, true, st);
   if (e != hipSuccess) return e;
-  return launch_recording(select_cand_kernel, dim3(units), dim3(SEL_THREADS), st, done, seq_lens, cw, idx, n_sel,
-                          adv_newest, adv_len, s.Hkv, s.T_cap, s.C, W, 0);
+  return launch_recording(select_cand_kernel<0>, dim3(units), dim3(CAND_SEL_THREADS), st, done, seq_lens, cw, idx,
+                          n_sel, adv_newest, adv_len, s.Hkv, s.T_cap, s.C, W, 0);
 }
 
 hipError_t launch_select(const Shape& s, const float* scores, const uint32_t* hist, const int32_t* seq_lens,
