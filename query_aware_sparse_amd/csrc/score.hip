@@ -4,13 +4,10 @@
 namespace asp {
 
 template <int D, int G, bool HIST, int OUT>
-__global__ void __launch_bounds__(SCORE_THREADS) score_mfma_kernel(const float* __restrict__ q_pred,
-                                                                   const uint16_t* __restrict__ k,
-                                                                   const int32_t* __restrict__ seq_lens,
-                                                                   float* __restrict__ scores,
-                                                                   uint32_t* __restrict__ hist, CandWs cw, int Hq,
-                                                                   int Hkv, int T_cap) {
-  __shared__ __align__(16) unsigned char smem[score_mfma_lds_bytes<D, HIST, OUT>()];
+__device__ __forceinline__ void score_mfma_grid(const float* __restrict__ q_pred, const uint16_t* __restrict__ k,
+                                                const int32_t* __restrict__ seq_lens, float* __restrict__ scores,
+                                                uint32_t* __restrict__ hist, const CandWs& cw, int Hq, int Hkv,
+                                                int T_cap, unsigned char* smem) {
   // The rescoring launch follows every selection and usually finds no unit
   // flagged: its workgroups (a few per unit) then leave at once; those of a
   // flagged unit loop over its key blocks.
@@ -23,6 +20,46 @@ __global__ void __launch_bounds__(SCORE_THREADS) score_mfma_kernel(const float* 
   }
   // Otherwise one key block per workgroup: a loop here slows the launch inside the step.
   score_mfma_block<D, G, HIST, OUT>(q_pred, k, seq_lens, scores, hist, cw, Hq, Hkv, T_cap, blockIdx.x, blockIdx.y, smem);
+}
+
+// Streaming launches (G >= 2, score rows or kept keys) are held to 128
+// registers per lane, four waves per SIMD: with fewer waves resident the
+// launch loses more to the kernels that share its CUs inside a step than it
+// gains alone.  The rescoring launch and G = 1 would spill under that cap and
+// run without it.
+template <int D, int G, bool HIST, int OUT>
+constexpr bool score_regs_capped() {
+  return G >= 2 && OUT != OUT_ALL_FLAGGED;
+}
+
+template <int D, int G, bool HIST, int OUT>
+__global__ void __launch_bounds__(SCORE_THREADS) __attribute__((amdgpu_waves_per_eu(4, 8)))
+score_mfma_kernel(const float* __restrict__ q_pred, const uint16_t* __restrict__ k,
+                  const int32_t* __restrict__ seq_lens, float* __restrict__ scores, uint32_t* __restrict__ hist,
+                  CandWs cw, int Hq, int Hkv, int T_cap) {
+  __shared__ __align__(16) unsigned char smem[score_mfma_lds_bytes<D, HIST, OUT>()];
+  score_mfma_grid<D, G, HIST, OUT>(q_pred, k, seq_lens, scores, hist, cw, Hq, Hkv, T_cap, smem);
+}
+
+template <int D, int G, bool HIST, int OUT>
+__global__ void __launch_bounds__(SCORE_THREADS)
+score_mfma_kernel_uncapped(const float* __restrict__ q_pred, const uint16_t* __restrict__ k,
+                           const int32_t* __restrict__ seq_lens, float* __restrict__ scores,
+                           uint32_t* __restrict__ hist, CandWs cw, int Hq, int Hkv, int T_cap) {
+  __shared__ __align__(16) unsigned char smem[score_mfma_lds_bytes<D, HIST, OUT>()];
+  score_mfma_grid<D, G, HIST, OUT>(q_pred, k, seq_lens, scores, hist, cw, Hq, Hkv, T_cap, smem);
+}
+
+template <int D, int G, bool HIST, int OUT>
+static hipError_t launch_mfma(dim3 grid, dim3 block, hipStream_t st, hipEvent_t done, const float* q_pred,
+                              const uint16_t* k, const int32_t* seq_lens, float* scores, uint32_t* hist,
+                              const CandWs& cw, int Hq, int Hkv, int T_cap) {
+  if constexpr (score_regs_capped<D, G, HIST, OUT>())
+    return launch_recording(score_mfma_kernel<D, G, HIST, OUT>, grid, block, st, done, q_pred, k, seq_lens, scores,
+                            hist, cw, Hq, Hkv, T_cap);
+  else
+    return launch_recording(score_mfma_kernel_uncapped<D, G, HIST, OUT>, grid, block, st, done, q_pred, k, seq_lens,
+                            scores, hist, cw, Hq, Hkv, T_cap);
 }
 
 template <int D, int G, bool HIST, int OUT>
@@ -54,8 +91,8 @@ static hipError_t launch_score_dh(const Shape& s, const float* q_pred, const voi
   const dim3 grid(gx, s.B * s.Hkv);
   const dim3 block(SCORE_THREADS);
 #define ASP_SCORE_LAUNCH(GG)                                                                                      \
-  (s.kv == 0 ? launch_recording(score_mfma_kernel<D, GG, HIST, OUT>, grid, block, st, done, q_pred,                \
-                                static_cast<const uint16_t*>(k), seq_lens, scores, hist, cw, s.Hq, s.Hkv, s.T_cap) \
+  (s.kv == 0 ? launch_mfma<D, GG, HIST, OUT>(grid, block, st, done, q_pred, static_cast<const uint16_t*>(k),      \
+                                             seq_lens, scores, hist, cw, s.Hq, s.Hkv, s.T_cap)                    \
              : launch_recording(score_valu_kernel<D, GG, HIST, OUT>, grid, block, st, done, q_pred,                \
                                 static_cast<const float*>(k), seq_lens, scores, hist, cw, s.Hq, s.Hkv, s.T_cap))
   hipError_t e;

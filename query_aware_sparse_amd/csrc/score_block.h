@@ -152,6 +152,22 @@ __device__ __forceinline__ void score_mfma_block(const float* __restrict__ q_pre
   const u32x4* kb = reinterpret_cast<const u32x4*>(k + (size_t)unit * T_cap * D);
   float* sb = scores + (size_t)unit * T_cap;
 
+  // Candidate route: the kept-key bookkeeping of an iteration's tiles (ballot,
+  // LDS staging) runs after the next iteration's loads are issued, so that it
+  // never delays them.
+  float pend[U];
+  int pend_base = -1;
+  auto keep_pending = [&]() {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int key = pend_base + u * 16 + j;
+      const uint32_t ok = order_key(pend[u]);
+      const bool take = c == 0 && key < k1 && ok >= hint;
+      const unsigned long long bal = __ballot(take);
+      if (take) stage[kept + lanes_below(bal)] = make_uint2(ok, (uint32_t)key);
+      kept += (uint32_t)__popcll(bal);
+    }
+  };
   for (int base = k0 + wave * 16 * U; base < k1; base += SCORE_WAVES * 16 * U) {
     // Coalesced non-temporal loads: each wave-wide load is RPI whole key rows.
     u32x4 gld[U][NI];
@@ -162,6 +178,9 @@ __device__ __forceinline__ void score_mfma_block(const float* __restrict__ q_pre
         const int key = base + u * 16 + RPI * i + lrow;
         gld[u][i] = key < k1 ? __builtin_nontemporal_load(kb + (size_t)key * CH + lchunk) : u32x4{0u, 0u, 0u, 0u};
       }
+    }
+    if constexpr (OUT != OUT_SCORES) {
+      if (pend_base >= 0) keep_pending();
     }
     // Transpose through LDS, one 16-key tile at a time through two slots:
     // tile u+1 is written while the MFMAs read tile u.  Chunk q of tile row r
@@ -200,19 +219,17 @@ __device__ __forceinline__ void score_mfma_block(const float* __restrict__ q_pre
           if constexpr (HIST) atomicAdd(&lhist[order_key(m) >> HIST_SHIFT], 1u);
         }
       } else {
-        const uint32_t ok = order_key(m);
-        const bool take = c == 0 && key < k1 && ok >= hint;
-        const unsigned long long bal = __ballot(take);
-        if (take) stage[kept + lanes_below(bal)] = make_uint2(ok, (uint32_t)key);
-        kept += (uint32_t)__popcll(bal);
+        pend[u] = m;
       }
       // Slot u % TB is written again two tiles later (or next iteration).
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
+    pend_base = base;
   }
   if constexpr (OUT != OUT_SCORES) {
+    if (pend_base >= 0) keep_pending();
     const int nreg = cand_regions(T_cap);
     flush_candidates(cw, (size_t)unit * nreg + (size_t)bx * SCORE_WAVES + wave, stage, kept, lane);
   }
