@@ -192,3 +192,16 @@ def test_candidates_any_workspace_contents():
         case.ws.copy_(torch.randint(0, 256, tuple(case.ws.shape), generator=g, device=DEV, dtype=torch.int32)
                       .to(torch.uint8))
         case.check(case.q, "random workspace %d" % fill)
+
+
+def test_candidates_empty_batch_is_a_no_op():
+    # batch 0: validated, nothing enqueued, nothing dereferenced (placeholder pointers)
+    import ctypes
+    lib = A.load()
+    dims = A.Dims(0, 8, 2, 128, 1000, A.KV_BF16)
+    cfg = A.Cfg(8, 100, 1e-2)
+    p = ctypes.c_void_p(256)
+    nbytes = A.asp_workspace_size(dims, cfg, A.OP_CANDIDATES)
+    assert lib.asp_score_candidates(ctypes.byref(dims), ctypes.byref(cfg), p, p, p, p, nbytes, None) == 0
+    assert lib.asp_select_candidates(ctypes.byref(dims), ctypes.byref(cfg), p, p, p, p, p, p, nbytes, None) == 0
+    torch.cuda.synchronize()
