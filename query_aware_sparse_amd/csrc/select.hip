@@ -6,10 +6,14 @@
 // Readings for cases the pages never mention: NaN ranks as -infinity, -0 ties
 // with +0, and the lower index wins a tie.
 //
-// Scores become order-preserving 32-bit keys (order_key).  The first 11 bits
-// of the C_eff-th largest key (the boundary bin) come from a coarse histogram
-// of the row: the score launch bins every key while it streams, or, for a
-// standalone call, one workgroup per row builds it here.  Two launches follow.
+// Scores become order-preserving 32-bit keys (order_key).  Two routes:
+//  - from score rows (asp_select_topc), described here;
+//  - from the keys a score launch kept above a threshold hint (the step and
+//    asp_select_candidates): select_cand_kernel, further below.
+// Score-row route.  The first 11 bits of the C_eff-th largest key (the boundary
+// bin) come from a coarse histogram of the row: the score launch bins every key
+// while it streams, or, for a standalone call, one workgroup per row builds it
+// here.  Two launches follow.
 //  * Classify: 8192 keys per 1024-thread workgroup, so a batch of long rows
 //    fills every CU.  Each wave owns a region of 512 consecutive keys (eight
 //    coalesced loads of 64 keys); a ballot per load gives 64 bits of the
