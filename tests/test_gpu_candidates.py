@@ -120,6 +120,11 @@ def _walk(case: Case, seed):
     for t in range(3):                       # AR(1)-like drift, the hints of the previous step
         q = (0.9 * q + 0.3 * wk.randn(tuple(q.shape), seed=seed + 100 + t).to(DEV)).contiguous()
         case.check(q, "drift step %d" % t)
+    # a sudden change of scale: the hints of the previous scores keep too few
+    # keys (every unit rescored), then far too many
+    case.check((q * 0.01).contiguous(), "scale 1/100")
+    case.check(q, "scale back")
+    case.check(q, "same scores again")
 
 
 @pytest.mark.parametrize("kind", ["normal", "integer", "special"])
