@@ -210,3 +210,12 @@ def test_candidates_empty_batch_is_a_no_op():
     assert lib.asp_score_candidates(ctypes.byref(dims), ctypes.byref(cfg), p, p, p, p, nbytes, None) == 0
     assert lib.asp_select_candidates(ctypes.byref(dims), ctypes.byref(cfg), p, p, p, p, p, p, nbytes, None) == 0
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("C", [1, 2, 998, 999])
+@pytest.mark.parametrize("kind", ["normal", "integer"])
+def test_candidates_extreme_budgets(C, kind):
+    # C = 1 and C = T - 1 on rows of 1000 keys, beside rows of 999 and 2 keys
+    # (C_eff = T there for the larger budgets), with every kind of hint
+    lens = [1000, 999, 2]
+    _walk(Case(3, 8, 2, 128, 1000, lens, C, "bf16", kind, seed=20 + C), seed=20 + C)
