@@ -173,11 +173,11 @@ asp_status asp_select_topc(const asp_dims* dims, const asp_cfg* cfg, const float
  * first rescored with every key kept.  idx and n_sel therefore equal, bit for
  * bit, those of asp_score_keys followed by asp_select_topc, whatever the hints
  * hold.  Each selection stores the unit's next hint: the lower edge of the bin
- * of the top 22 bits of the order key that holds the 2*C_eff-th kept key, or,
+ * of the top 22 bits of the order key that holds the (3*C_eff/2)-th kept key, or,
  * when fewer keys were kept, the current hint moved down by the key range the
  * shortfall would take at the density of the kept keys just above it.  Scores
  * close to those of the previous step thus cost one pass over the keys plus
- * about 2*C_eff candidate writes per unit.
+ * about 1.5*C_eff candidate writes per unit.
  * ws/ws_bytes: asp_workspace_size(ASP_OP_CANDIDATES) bytes, 16-byte aligned
  * (about 8 bytes per key slot).  Its first 4*batch*n_kv_heads bytes are the
  * hints ([B][Hkv] uint32), carried from one selection to the next; any value

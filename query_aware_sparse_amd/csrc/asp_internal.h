@@ -56,7 +56,7 @@ hipError_t launch_select(const Shape& s, const float* scores, const uint32_t* hi
 // no score rows.  The select launches pick the exact top C_eff from the
 // candidates; a unit left with fewer than C_eff candidates is rescored with
 // every key kept, so the result never depends on the hint.  Each selection
-// stores the next hint: a bin edge of the key that keeps about 2 C_eff
+// stores the next hint: a bin edge of the key that keeps about 1.5 C_eff
 // candidates of the scores it saw.
 constexpr int CAND_REGION = 128;       // keys of one wave of a score block
 constexpr int CAND_BLOCK_KEYS = 512;   // keys of one score block (four waves)

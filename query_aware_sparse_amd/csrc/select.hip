@@ -464,9 +464,9 @@ __device__ __forceinline__ void pick_digits(const uint32_t* hist, uint32_t need_
 // order through two LDS bitmaps per chunk of the row, one for the keys above
 // the C_eff-th key and one for those equal to it, of which the lowest indices
 // are taken.  The next hint is the lower edge of the fine bin (top 22 bits of
-// the key, two digits) that holds the 2 C_eff-th candidate key; when fewer
-// than 2 C_eff keys were kept, the current hint moves down by the shortfall at
-// the density of the kept keys in its coarse bin (at most two coarse bins).
+// the key, two digits) that holds the 1.5 C_eff-th candidate key; when fewer
+// than 1.5 C_eff keys were kept, the current hint moves down by the shortfall
+// at the density of the kept keys in its coarse bin (at most two coarse bins).
 // CAP: candidates staged in LDS (0: none, every pass reads them from memory).
 // The LDS a workgroup holds is taken from the concurrent score launches, so
 // the first launch sizes CAP to the budget and the second one, which usually
@@ -575,9 +575,9 @@ __global__ void __launch_bounds__(CAND_SEL_THREADS) select_cand_kernel(const int
   // The C_eff-th key, digit by digit: after the loop the keys above `prefix`
   // (under pmask) are taken, with `need` more of those equal to it.
   uint32_t prefix = 0u, pmask = 0u, need = (uint32_t)c_eff;
-  const uint32_t need2 = 2u * (uint32_t)c_eff;
+  const uint32_t need2 = 3u * (uint32_t)c_eff / 2u;  // the hint's target: 1.5 C_eff kept keys
   uint32_t hint_next = 0u;
-  bool refine_hint = false;  // the 2 C_eff-th key's coarse bin is known: refine it by one digit
+  bool refine_hint = false;  // the need2-th key's coarse bin is known: refine it by one digit
   const int shifts[3] = {HIST_SHIFT, 10, 0};
   const uint32_t dmasks[3] = {0x7ffu, 0x7ffu, 0x3ffu};
   bool done = false;
@@ -590,7 +590,7 @@ __global__ void __launch_bounds__(CAND_SEL_THREADS) select_cand_kernel(const int
       if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sft) & dm], 1u);
     });
     __syncthreads();
-    // pass 0 also locates the coarse bin of the 2 C_eff-th candidate key
+    // pass 0 also locates the coarse bin of the need2-th candidate key
     pick_digits<NT>(hist, need, pass == 0 ? need2 : 0u, scratch, sh);
     __syncthreads();
     const uint32_t d = sh[0] & dm;
@@ -602,7 +602,7 @@ __global__ void __launch_bounds__(CAND_SEL_THREADS) select_cand_kernel(const int
         hint_next = (sh[2] & 0x7ffu) << HIST_SHIFT;
         refine_hint = true;
       } else if (first) {
-        // Fewer than 2 C_eff keys kept: move the hint down by the key range
+        // Fewer than need2 keys kept: move the hint down by the key range
         // that the shortfall (plus a quarter) would take at the density of
         // the kept keys in the hint's own coarse bin; at most two coarse bins.
         const uint32_t hb_cur = hint_cur >> HIST_SHIFT;
@@ -611,13 +611,13 @@ __global__ void __launch_bounds__(CAND_SEL_THREADS) select_cand_kernel(const int
         const uint64_t cap = 2ull << HIST_SHIFT;
         const uint64_t down = c_lo ? min(span * (uint64_t)(need2 - n) * 5u / (4u * c_lo) + 1u, cap) : cap;
         hint_next = (uint32_t)((uint64_t)hint_cur > down ? (uint64_t)hint_cur - down : 0u) & ~0x3ffu;
-      }  // else every key was kept and fewer than 2 C_eff exist: keep them all
+      }  // else every key was kept and fewer than need2 exist: keep them all
     }
     done = hist[d] == need;
     __syncthreads();
   }
 
-  // The hint's second digit: bits 20..10 of the 2 C_eff-th candidate key, from
+  // The hint's second digit: bits 20..10 of the need2-th candidate key, from
   // the keys of its coarse bin (one more histogram pass over the candidates).
   if (refine_hint) {
     const uint32_t need_h = need2 - sh[3];
