@@ -174,7 +174,7 @@ hipError_t step_fork(StepFork** out) {
 asp_status run_selection(const Shape& s, const float* q_cur, float* q_hist, int32_t* newest, int32_t* len,
                          const void* k, const int32_t* seq_lens, int32_t* idx, int32_t* n_sel, float* q_pred,
                          const asp::CandWs& cw, hipStream_t st, hipEvent_t done) {
-  ASP_TRY_HIP(asp::launch_predict(s, q_hist, newest, len, q_cur, q_pred, nullptr, st));
+  ASP_TRY_HIP(asp::launch_predict(s, q_hist, newest, len, q_cur, q_pred, st));
   ASP_TRY_HIP(asp::launch_score_candidates(s, q_pred, k, seq_lens, cw, false, st));
   ASP_TRY_HIP(asp::launch_select_candidates(s, q_pred, k, seq_lens, cw, idx, n_sel, newest, len, st, done));
   return ASP_OK;
@@ -225,7 +225,7 @@ asp_status asp_predict_query(const asp_dims* dims, const asp_cfg* cfg, const flo
   if (st != ASP_OK) return st;
   if (!q_hist || !hist_newest || !hist_len || !q_pred) return ASP_ERR_INVALID_ARG;
   if (!aligned16(q_hist) || !aligned4(q_pred)) return ASP_ERR_INVALID_ARG;
-  return hip_status(asp::launch_predict(s, const_cast<float*>(q_hist), hist_newest, hist_len, nullptr, q_pred, nullptr,
+  return hip_status(asp::launch_predict(s, const_cast<float*>(q_hist), hist_newest, hist_len, nullptr, q_pred,
                                         stream));
 }
 
@@ -374,7 +374,7 @@ asp_status asp_step(const asp_dims* dims, const asp_cfg* cfg, const float* q_cur
   ASP_TRY_HIP(hipEventRecord(f->in, attn_stream));
   ASP_TRY_HIP(hipStreamWaitEvent(f->pred, f->in, 0));
   ASP_TRY_HIP(hipStreamWaitEvent(f->pred, idx_cur_ready, 0));
-  ASP_TRY_HIP(asp::launch_predict(s, q_hist, hist_newest, hist_len, q_cur, q_pred, nullptr, f->pred, q_ready));
+  ASP_TRY_HIP(asp::launch_predict(s, q_hist, hist_newest, hist_len, q_cur, q_pred, f->pred, q_ready));
   ASP_TRY_HIP(hipStreamWaitEvent(f->score, q_ready, 0));
   ASP_TRY_HIP(asp::launch_score_candidates(s, q_pred, k, seq_lens, cw, false, f->score, f->scored));
   ASP_TRY_HIP(hipStreamWaitEvent(sel_stream, f->scored, 0));

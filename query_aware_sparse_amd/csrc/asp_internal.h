@@ -31,10 +31,9 @@ hipError_t launch_push(const Shape& s, const float* q_cur, float* q_hist, int32_
 // next ring slot, but leaves newest/len unchanged: a later launch of the same
 // step advances them (ring_advance, in the last select launch), once every
 // predictor workgroup has read them.
-// hist_zero, when not null, is cleared ([B*Hkv][HIST_BINS]).
 // `done` (nullable) is recorded when the launch completes.
 hipError_t launch_predict(const Shape& s, float* q_hist, const int32_t* newest, const int32_t* len,
-                          const float* q_cur, float* q_pred, uint32_t* hist_zero, hipStream_t st,
+                          const float* q_cur, float* q_pred, hipStream_t st,
                           hipEvent_t done = nullptr);
 // Scores; hist (nullable) accumulates the coarse histogram of every unit and
 // must be zero on entry.  `done` (nullable) is recorded when the launch completes.

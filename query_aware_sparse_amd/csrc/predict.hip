@@ -246,7 +246,7 @@ __global__ void __launch_bounds__(PRED_THREADS) predict_kernel(float* __restrict
                                                                const int32_t* __restrict__ len,
                                                                const float* __restrict__ q_cur,
                                                                float* __restrict__ q_pred,
-                                                               uint32_t* __restrict__ hist_zero, int Hq, int Hkv,
+                                                               int Hq,
                                                                int W, int D, double lambda) {
   constexpr int NR = ((PB + 1 + 15) / 16) * 16;  // lag rows staged (whole 16-row MFMA tiles)
   __shared__ float X[NR * XS];
@@ -258,13 +258,6 @@ __global__ void __launch_bounds__(PRED_THREADS) predict_kernel(float* __restrict
   const int b = bh / Hq;
   float* ring = q_hist + (size_t)bh * W * D;
   float* out = q_pred + (size_t)bh * D;
-
-  if (hist_zero != nullptr) {  // the G heads of a KV head clear its histogram row together
-    const int G = Hq / Hkv, h = bh % Hq;
-    uint32_t* row = hist_zero + ((size_t)b * Hkv + h / G) * HIST_BINS;
-    const int per = HIST_BINS / G, j0 = (h % G) * per;
-    for (int j = j0 + t; j < j0 + per; j += PRED_THREADS) row[j] = 0u;
-  }
 
   int on = newest[b] % W;
   if (on < 0) on += W;
@@ -357,13 +350,13 @@ __global__ void __launch_bounds__(PRED_THREADS) predict_kernel(float* __restrict
 }
 
 hipError_t launch_predict(const Shape& s, float* q_hist, const int32_t* newest, const int32_t* len,
-                          const float* q_cur, float* q_pred, uint32_t* hist_zero, hipStream_t st, hipEvent_t done) {
+                          const float* q_cur, float* q_pred, hipStream_t st, hipEvent_t done) {
   if (s.B == 0) return done ? hipEventRecord(done, st) : hipSuccess;
   const dim3 grid(s.B * s.Hq), block(PRED_THREADS);
   const int P = s.W - 1;
 #define ASP_PRED_LAUNCH(PB)                                                                                    \
-  launch_recording(predict_kernel<PB>, grid, block, st, done, q_hist, newest, len, q_cur, q_pred, hist_zero, s.Hq, \
-                   s.Hkv, s.W, s.D, s.lambda)
+  launch_recording(predict_kernel<PB>, grid, block, st, done, q_hist, newest, len, q_cur, q_pred, s.Hq,  \
+                   s.W, s.D, s.lambda)
   hipError_t e;
   if (P <= 3) e = ASP_PRED_LAUNCH(3);
   else if (P <= 7) e = ASP_PRED_LAUNCH(7);
