@@ -240,14 +240,16 @@ __device__ __forceinline__ double pooled_weights(double* M, double lambda, int P
 }
 
 // PB: a bound on P = (largest window) - 1; PB + 1 is a multiple of 4 and at most 64.
-template <int PB>
+// DD: head_dim (64 or 128), a compile-time bound so that the Gram loop unrolls.
+template <int PB, int DD>
 __global__ void __launch_bounds__(PRED_THREADS) predict_kernel(float* __restrict__ q_hist,
                                                                const int32_t* __restrict__ newest,
                                                                const int32_t* __restrict__ len,
                                                                const float* __restrict__ q_cur,
                                                                float* __restrict__ q_pred,
                                                                int Hq,
-                                                               int W, int D, double lambda) {
+                                                               int W, double lambda) {
+  constexpr int D = DD;
   constexpr int NR = ((PB + 1 + 15) / 16) * 16;  // lag rows staged (whole 16-row MFMA tiles)
   __shared__ float X[NR * XS];
   __shared__ double M[NR * NR];  // Gram of lags 0..P; later reused for L
@@ -298,10 +300,7 @@ __global__ void __launch_bounds__(PRED_THREADS) predict_kernel(float* __restrict
   const int NT = (P + 1 + 15) / 16;
 
   // 1. Stage lags 0..P (rows up to the tile boundary are zero).
-  if (D == 128)
-    stage_lags<128>(X, ring, qc, P, NT, on, shift, W, t);
-  else
-    stage_lags<64>(X, ring, qc, P, NT, on, shift, W, t);
+  stage_lags<DD>(X, ring, qc, P, NT, on, shift, W, t);
   __syncthreads();
 
   // 2. Gram matrix M[a][c] = <lag a, lag c>, fp64 MFMA over 16x16 tiles.  The
@@ -316,6 +315,7 @@ __global__ void __launch_bounds__(PRED_THREADS) predict_kernel(float* __restrict
       for (int q = 0; q < 4; ++q) acc[q] = f64x4{0.0, 0.0, 0.0, 0.0};
       const float* xa = X + (ti * 16 + lr) * XS + lk;
       const float* xb = X + (tj * 16 + lr) * XS + lk;
+#pragma unroll
       for (int m = 0; m < D / 16; ++m) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
@@ -354,9 +354,11 @@ hipError_t launch_predict(const Shape& s, float* q_hist, const int32_t* newest, 
   if (s.B == 0) return done ? hipEventRecord(done, st) : hipSuccess;
   const dim3 grid(s.B * s.Hq), block(PRED_THREADS);
   const int P = s.W - 1;
-#define ASP_PRED_LAUNCH(PB)                                                                                    \
-  launch_recording(predict_kernel<PB>, grid, block, st, done, q_hist, newest, len, q_cur, q_pred, s.Hq,  \
-                   s.W, s.D, s.lambda)
+#define ASP_PRED_LAUNCH(PB)                                                                                  \
+  (s.D == 64 ? launch_recording(predict_kernel<PB, 64>, grid, block, st, done, q_hist, newest, len, q_cur, q_pred,  \
+                                s.Hq, s.W, s.lambda)                                                            \
+             : launch_recording(predict_kernel<PB, 128>, grid, block, st, done, q_hist, newest, len, q_cur, q_pred, \
+                                s.Hq, s.W, s.lambda))
   hipError_t e;
   if (P <= 3) e = ASP_PRED_LAUNCH(3);
   else if (P <= 7) e = ASP_PRED_LAUNCH(7);
