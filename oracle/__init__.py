@@ -6,9 +6,10 @@ code with the HIP library in ``query_aware_sparse_amd`` and never calls it.
 
 The arithmetic lives in ``asp_oracle.c`` (compiled with gcc, no fast-math);
 this module only builds it, marshals numpy arrays through ctypes, shapes the
-results, and lists the tokens of the optional newest-token window
-(``attend_with_recent``) before handing them to the C attention.  Each wrapper names the definition it follows; the C file states
-the readings adopted where the pages are silent.
+results, lists the tokens of the optional newest-token window
+(``attend_with_recent``) before handing them to the C attention, and lists the
+tokens of selected pages (``page_tokens``).  Each wrapper names the definition
+it follows; the C file states the readings adopted where the pages are silent.
 """
 from __future__ import annotations
 
@@ -63,6 +64,10 @@ def _load():
     lib.oracle_attend.restype = I
     lib.oracle_overlap.argtypes = [I, I, I, P, P, P, P, P]
     lib.oracle_overlap.restype = None
+    lib.oracle_page_summary.argtypes = [I, I, I, I, I, I, P, P, P, P]
+    lib.oracle_page_summary.restype = None
+    lib.oracle_page_score.argtypes = [I, I, I, I, I, P, P, P, P, P]
+    lib.oracle_page_score.restype = None
     _lib = lib
     return lib
 
@@ -219,3 +224,73 @@ def overlap(idx_a, n_a, idx_b, n_b, T_cap: int):
     out = np.empty(idx_a.shape[:-1], np.int32)
     _load().oracle_overlap(units, C, int(T_cap), _ptr(idx_a), _ptr(n_a), _ptr(idx_b), _ptr(n_b), _ptr(out))
     return out
+
+
+def page_counts(seq_lens, T_cap: int, P: int) -> np.ndarray:
+    """Pages holding at least one token: ceil(T_b / P), T_b clamped to [0, T_cap]."""
+    T = np.clip(np.asarray(seq_lens, np.int64), 0, T_cap)
+    return ((T + P - 1) // P).astype(np.int32)
+
+
+def page_summary(k, seq_lens, P: int):
+    """Quest page summaries (per page of P tokens, the element-wise min and max
+    of its keys; asp_oracle.c states the source and the readings):
+    K[B][Hkv][T_cap][D] -> (kmin, kmax) [B][Hkv][NP][D] fp64, NaN for pages
+    with no token."""
+    k, kvd = _kv(k)
+    B, Hkv, T_cap, D = k.shape
+    NP = (T_cap + P - 1) // P
+    seq_lens = _c(seq_lens, np.int32)
+    kmin = np.empty((B, Hkv, NP, D), np.float64)
+    kmax = np.empty((B, Hkv, NP, D), np.float64)
+    _load().oracle_page_summary(B, Hkv, D, T_cap, kvd, int(P), _ptr(k), _ptr(seq_lens), _ptr(kmin), _ptr(kmax))
+    return kmin, kmax
+
+
+def page_scores(q, kmin, kmax, n_pages):
+    """Quest page scores: max over the KV head's query heads of
+    sum_d max(q_d * min_d, q_d * max_d); q[B][Hq][D] fp32, kmin/kmax
+    [B][Hkv][NP][D] (widened to fp64), n_pages[B] -> [B][Hkv][NP] fp64, NaN
+    past each sequence's pages."""
+    q = _c(q, np.float32)
+    kmin = _c(kmin, np.float64)
+    kmax = _c(kmax, np.float64)
+    B, Hkv, NP, D = kmin.shape
+    Hq = q.shape[1]
+    n_pages = _c(n_pages, np.int32)
+    out = np.empty((B, Hkv, NP), np.float64)
+    _load().oracle_page_score(B, Hq, Hkv, D, NP, _ptr(q), _ptr(kmin), _ptr(kmax), _ptr(n_pages), _ptr(out))
+    return out
+
+
+def page_tokens(page_idx, n_pages_sel, seq_lens, P: int, C: int, T_cap: int):
+    """Token list of a page selection: the tokens of the selected pages in
+    ascending order, each page p contributing [p*P, min(p*P + P, T_b)); padded
+    with -1 to C.  Returns (idx[B][Hkv][C], n_sel[B][Hkv])."""
+    page_idx = np.asarray(page_idx, np.int32)
+    n_pages_sel = np.asarray(n_pages_sel, np.int32)
+    B, Hkv = n_pages_sel.shape
+    T = np.clip(np.asarray(seq_lens, np.int64), 0, T_cap)
+    idx = np.full((B, Hkv, C), -1, np.int32)
+    n_sel = np.zeros((B, Hkv), np.int32)
+    for b in range(B):
+        for g in range(Hkv):
+            toks = []
+            for p in sorted(int(x) for x in page_idx[b, g, : n_pages_sel[b, g]]):
+                toks.extend(range(p * P, min(p * P + P, int(T[b]))))
+            idx[b, g, : len(toks)] = toks
+            n_sel[b, g] = len(toks)
+    return idx, n_sel
+
+
+def page_select(q, kmin, kmax, seq_lens, P: int, C: int):
+    """Quest selection with a budget of C tokens: the top C / P pages of each
+    unit by page score (score descending, lower page first on ties), as the
+    token list of page_tokens.  Returns (idx, n_sel, page_idx, n_pages_sel)."""
+    B, Hkv, NP, D = np.shape(kmin)
+    T_cap = NP * P
+    n_pages = page_counts(seq_lens, T_cap, P)
+    scores = page_scores(q, kmin, kmax, n_pages)
+    page_idx, n_pages_sel = select(scores, n_pages, C // P)
+    idx, n_sel = page_tokens(page_idx, n_pages_sel, seq_lens, P, C, T_cap)
+    return idx, n_sel, page_idx, n_pages_sel

@@ -385,3 +385,89 @@ void oracle_overlap(int units, int C, int T_cap, const int* idx_a, const int* n_
     free(mark);
   }
 }
+
+/* ------------------------------------------------------------------------- */
+/* Page-level selection, the baseline the pages compare against.  [summary]   */
+/* "Problem" and "Baselines", [abstract]: Quest selects whole pages of the KV  */
+/* cache with the current query.  The pages do not define how a page is        */
+/* scored; the definition used is the one Quest publishes (Tang et al.,        */
+/* "Quest: Query-Aware Sparsity for Efficient Long-Context LLM Inference",     */
+/* ICML 2024, the criticality estimate of its method section): each page keeps */
+/* the element-wise minimum and maximum of its keys, and a query q scores the  */
+/* page by sum_d max(q_d * min_d, q_d * max_d), the largest value q . k can    */
+/* take over the box [min, max], hence an upper bound on q . k for every key   */
+/* of the page.  Readings for what Quest leaves open here:                     */
+/*  - pages are runs of P consecutive tokens from token 0; a sequence's last   */
+/*    page may be partial and then summarises only its valid tokens;          */
+/*  - grouped-query attention: as for token scores, a KV head's page score is  */
+/*    the largest bound over the query heads that share it;                    */
+/*  - the token budget C buys C / P pages, ranked like tokens (score           */
+/*    descending, lower page index first on ties).                             */
+/* ------------------------------------------------------------------------- */
+
+/* Page summaries.  K[B][Hkv][T_cap][D] -> kmin, kmax [B][Hkv][NP][D] (fp64,   */
+/* exact copies of key elements), NP = ceil(T_cap / P); page p of sequence b   */
+/* covers tokens [p*P, min(p*P + P, T_b)); pages with no token are NaN.        */
+void oracle_page_summary(int B, int Hkv, int D, int T_cap, int kv_dtype, int P, const void* k, const int* seq_lens,
+                         double* kmin, double* kmax) {
+  const int NP = (T_cap + P - 1) / P;
+#pragma omp parallel for schedule(dynamic)
+  for (long u = 0; u < (long)B * Hkv; ++u) {
+    const int b = (int)(u / Hkv);
+    int T = seq_lens[b];
+    if (T < 0) T = 0;
+    if (T > T_cap) T = T_cap;
+    for (int p = 0; p < NP; ++p) {
+      double* mn = kmin + ((size_t)u * NP + p) * D;
+      double* mx = kmax + ((size_t)u * NP + p) * D;
+      const int first = p * P;
+      int last = first + P;
+      if (last > T) last = T;
+      for (int d = 0; d < D; ++d) {
+        mn[d] = NAN;
+        mx[d] = NAN;
+      }
+      for (int i = first; i < last; ++i) {
+        for (int d = 0; d < D; ++d) {
+          const double x = kv_at(k, kv_dtype, ((size_t)u * T_cap + i) * D + d);
+          if (i == first || x < mn[d]) mn[d] = x;
+          if (i == first || x > mx[d]) mx[d] = x;
+        }
+      }
+    }
+  }
+}
+
+/* Page scores.  q[B][Hq][D] fp32, kmin/kmax [B][Hkv][NP][D] fp64,            */
+/* n_pages[B] (pages with at least one token) -> scores[B][Hkv][NP]:           */
+/*   scores[b][g][p] = max over h of g of sum_d max(q[h][d] * kmin[p][d],      */
+/*                                                   q[h][d] * kmax[p][d])     */
+/* for p < n_pages[b], NaN beyond.                                             */
+void oracle_page_score(int B, int Hq, int Hkv, int D, int NP, const float* q, const double* kmin, const double* kmax,
+                       const int* n_pages, double* scores) {
+  const int G = Hq / Hkv;
+#pragma omp parallel for schedule(dynamic)
+  for (long u = 0; u < (long)B * Hkv; ++u) {
+    const int b = (int)(u / Hkv), g = (int)(u % Hkv);
+    int n = n_pages[b];
+    if (n < 0) n = 0;
+    if (n > NP) n = NP;
+    for (int p = 0; p < NP; ++p) {
+      double best = NAN;
+      if (p < n) {
+        const double* mn = kmin + ((size_t)u * NP + p) * D;
+        const double* mx = kmax + ((size_t)u * NP + p) * D;
+        for (int hh = 0; hh < G; ++hh) {
+          const float* qh = q + ((size_t)b * Hq + (size_t)g * G + hh) * D;
+          double s = 0.0;
+          for (int d = 0; d < D; ++d) {
+            const double lo = (double)qh[d] * mn[d], hi = (double)qh[d] * mx[d];
+            s += lo > hi ? lo : hi;
+          }
+          if (hh == 0 || s > best) best = s;
+        }
+      }
+      scores[(size_t)u * NP + p] = best;
+    }
+  }
+}
