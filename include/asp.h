@@ -224,6 +224,49 @@ asp_status asp_sparse_decode(const asp_dims* dims, const asp_cfg* cfg, const flo
                              const int32_t* seq_lens, const int32_t* idx, const int32_t* n_sel, float* out, void* ws,
                              size_t ws_bytes, hipStream_t stream);
 
+/* Page-level selection, the baseline the pages compare against ([summary]
+ * "Problem" and "Baselines"; [abstract]: Quest, which selects pages of the KV
+ * cache with the current query, on the decode critical path).  The pages do
+ * not define how a page is scored; the score is the criticality estimate that
+ * Quest publishes (Tang et al., ICML 2024, method section):
+ *   pages: runs of P = page_size consecutive tokens from token 0,
+ *     NP = ceil(t_cap / P) page rows per unit; page p of sequence b holds the
+ *     tokens [p*P, min(p*P + P, T)), T = seq_lens[b] clamped to [0, t_cap], so
+ *     the sequence has ceil(T / P) pages and only its last may be partial;
+ *   summary: kmin[b][g][p][d] and kmax[b][g][p][d], the minimum and maximum
+ *     over the page's tokens of K[b][g][i][d] (exact elements, in
+ *     dims->kv_dtype);
+ *   score: max over the G query heads h of g of
+ *     sum_d max(q[b][h][d] * kmin[b][g][p][d], q[b][h][d] * kmax[b][g][p][d]),
+ *     the largest value of q[h] . k over the page's min/max box (an upper
+ *     bound on the dot product of every key of the page), accumulated in fp32;
+ *   selection: with a budget of C = cfg->top_c tokens, the K = C / P pages
+ *     that come first by score descending, then page index ascending (the
+ *     order of asp_select_topc); their tokens are written in ascending order
+ *     to idx[b][g][0..n), n = n_sel[b][g] (at most C; fewer when the
+ *     sequence has fewer than K pages or its partial last page is chosen),
+ *     and idx[b][g][n..C) = -1, ready for asp_sparse_decode.
+ * Keys must be finite (a NaN key gives unspecified summaries).
+ * 1 <= page_size <= t_cap, else ASP_ERR_INVALID_ARG; asp_page_select also
+ * needs top_c % page_size == 0.
+ * kmin, kmax: [B][Hkv][NP][D] in dims->kv_dtype, 16-byte aligned,
+ * asp_page_summary_size() bytes each (0 when dims or page_size are invalid);
+ * rows of pages without tokens are not written.  q[B][Hq][D] fp32,
+ * k[B][Hkv][t_cap][D], seq_lens[B] int32, scores[B][Hkv][NP] fp32 (rows past
+ * a sequence's pages not written), idx[B][Hkv][C] and n_sel[B][Hkv] int32.
+ * asp_page_select: ws/ws_bytes: asp_page_select_workspace_size() bytes,
+ * 16-byte aligned (0 when the arguments are invalid); contents need no
+ * initialisation and are not kept. */
+size_t asp_page_summary_size(const asp_dims* dims, int32_t page_size);
+asp_status asp_page_summary(const asp_dims* dims, int32_t page_size, const void* k, const int32_t* seq_lens,
+                            void* kmin, void* kmax, hipStream_t stream);
+asp_status asp_page_scores(const asp_dims* dims, int32_t page_size, const float* q, const void* kmin,
+                           const void* kmax, const int32_t* seq_lens, float* scores, hipStream_t stream);
+size_t asp_page_select_workspace_size(const asp_dims* dims, const asp_cfg* cfg, int32_t page_size);
+asp_status asp_page_select(const asp_dims* dims, const asp_cfg* cfg, int32_t page_size, const float* q,
+                           const void* kmin, const void* kmax, const int32_t* seq_lens, int32_t* idx,
+                           int32_t* n_sel, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* One decode step of one layer ([abstract], second component; [summary]
  * "Approach": selection for the next step is taken off the decode critical
  * path and overlapped with the current step's attention).

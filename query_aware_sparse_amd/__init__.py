@@ -22,6 +22,8 @@ __all__ = [
     "asp_workspace_size", "asp_status_string", "asp_push_query", "asp_predict_query", "asp_score_keys",
     "asp_select_topc", "asp_score_candidates", "asp_select_candidates", "asp_sparse_decode", "asp_step",
     "asp_selection_overlap", "asp_release_streams",
+    "asp_page_summary_size", "asp_page_summary", "asp_page_scores", "asp_page_select_workspace_size",
+    "asp_page_select", "page_count",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -88,6 +90,14 @@ def load():
     lib.asp_step.argtypes = [D, C, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P, P, P, P, P]
     lib.asp_selection_overlap.argtypes = [D, C, P, P, P, P, P, P]
     lib.asp_release_streams.argtypes = []
+    I32 = ctypes.c_int32
+    lib.asp_page_summary_size.argtypes = [D, I32]
+    lib.asp_page_summary_size.restype = SZ
+    lib.asp_page_summary.argtypes = [D, I32, P, P, P, P, P]
+    lib.asp_page_scores.argtypes = [D, I32, P, P, P, P, P, P]
+    lib.asp_page_select_workspace_size.argtypes = [D, C, I32]
+    lib.asp_page_select_workspace_size.restype = SZ
+    lib.asp_page_select.argtypes = [D, C, I32, P, P, P, P, P, P, P, SZ, P]
     for name in ("asp_push_query", "asp_predict_query", "asp_score_keys", "asp_select_topc",
                  "asp_score_candidates", "asp_select_candidates", "asp_sparse_decode", "asp_step",
                  "asp_selection_overlap", "asp_release_streams"):
@@ -326,6 +336,66 @@ def asp_step(dims: Dims, cfg: Cfg, q_cur, q_hist, hist_newest, hist_len, k, v, s
                                        _ptr(hist_newest), _ptr(hist_len), _ptr(k), _ptr(v), _ptr(seq_lens),
                                        _ptr(idx_cur), _ptr(n_sel_cur), _ptr(idx_next), _ptr(n_sel_next), _ptr(out),
                                        wp, wb, attn, sel, _ev(q_ready), _ev(idx_cur_ready), _ev(idx_next_ready)))
+
+
+def page_count(t_cap: int, page_size: int) -> int:
+    """Page rows per unit of the page summaries and page scores: ceil(t_cap / page_size)."""
+    return (int(t_cap) + int(page_size) - 1) // int(page_size)
+
+
+def asp_page_summary_size(dims: Dims, page_size: int) -> int:
+    return int(load().asp_page_summary_size(ctypes.byref(dims), int(page_size)))
+
+
+def _check_summaries(dims: Dims, page_size: int, kmin, kmax):
+    B, Hkv, D = dims.batch, dims.n_kv_heads, dims.head_dim
+    shape = (B, Hkv, page_count(dims.t_cap, page_size), D)
+    _check(kmin, "kmin", shape, _kv_dtype(dims))
+    _check(kmax, "kmax", shape, _kv_dtype(dims))
+
+
+def asp_page_summary(dims: Dims, page_size: int, k, seq_lens, kmin, kmax, stream=None) -> None:
+    """Per page of page_size tokens, the element-wise min and max of its keys."""
+    B, Hkv, D, T = dims.batch, dims.n_kv_heads, dims.head_dim, dims.t_cap
+    _check(k, "k", (B, Hkv, T, D), _kv_dtype(dims))
+    _check(seq_lens, "seq_lens", (B,), torch.int32)
+    _check_summaries(dims, page_size, kmin, kmax)
+    _raise("asp_page_summary", load().asp_page_summary(ctypes.byref(dims), int(page_size), _ptr(k), _ptr(seq_lens),
+                                                       _ptr(kmin), _ptr(kmax), _stream_handle(stream)))
+
+
+def asp_page_scores(dims: Dims, page_size: int, q, kmin, kmax, seq_lens, scores, stream=None) -> None:
+    """Page scores [B][Hkv][NP] fp32 from the page summaries and the query q."""
+    B, Hq, Hkv, D = dims.batch, dims.n_q_heads, dims.n_kv_heads, dims.head_dim
+    _check(q, "q", (B, Hq, D), torch.float32)
+    _check_summaries(dims, page_size, kmin, kmax)
+    _check(seq_lens, "seq_lens", (B,), torch.int32)
+    _check(scores, "scores", (B, Hkv, page_count(dims.t_cap, page_size)), torch.float32)
+    _raise("asp_page_scores", load().asp_page_scores(ctypes.byref(dims), int(page_size), _ptr(q), _ptr(kmin),
+                                                     _ptr(kmax), _ptr(seq_lens), _ptr(scores),
+                                                     _stream_handle(stream)))
+
+
+def asp_page_select_workspace_size(dims: Dims, cfg: Cfg, page_size: int) -> int:
+    return int(load().asp_page_select_workspace_size(ctypes.byref(dims), ctypes.byref(cfg), int(page_size)))
+
+
+def asp_page_select(dims: Dims, cfg: Cfg, page_size: int, q, kmin, kmax, seq_lens, idx, n_sel, ws=None,
+                    stream=None) -> None:
+    """The top top_c / page_size pages per unit, written as their tokens."""
+    B, Hq, Hkv, D, C = dims.batch, dims.n_q_heads, dims.n_kv_heads, dims.head_dim, cfg.top_c
+    _check(q, "q", (B, Hq, D), torch.float32)
+    _check_summaries(dims, page_size, kmin, kmax)
+    _check(seq_lens, "seq_lens", (B,), torch.int32)
+    _check(idx, "idx", (B, Hkv, C), torch.int32)
+    _check(n_sel, "n_sel", (B, Hkv), torch.int32)
+    if ws is None:
+        ws = torch.empty(max(asp_page_select_workspace_size(dims, cfg, page_size), 1), dtype=torch.uint8,
+                         device=q.device)
+    wp, wb = _ws(ws)
+    _raise("asp_page_select", load().asp_page_select(ctypes.byref(dims), ctypes.byref(cfg), int(page_size), _ptr(q),
+                                                     _ptr(kmin), _ptr(kmax), _ptr(seq_lens), _ptr(idx), _ptr(n_sel),
+                                                     wp, wb, _stream_handle(stream)))
 
 
 def asp_release_streams() -> None:

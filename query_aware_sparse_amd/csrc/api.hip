@@ -308,6 +308,57 @@ asp_status asp_sparse_decode(const asp_dims* dims, const asp_cfg* cfg, const flo
   return hip_status(asp::launch_attend(s, q, k, v, seq_lens, idx, n_sel, out, ws, stream));
 }
 
+size_t asp_page_summary_size(const asp_dims* dims, int32_t page_size) {
+  Shape s;
+  if (check_dims(dims, &s) != ASP_OK || page_size < 1 || page_size > s.T_cap) return 0;
+  return (size_t)s.B * s.Hkv * asp::page_count(s.T_cap, page_size) * s.D * (s.kv == 0 ? 2 : 4);
+}
+
+asp_status asp_page_summary(const asp_dims* dims, int32_t page_size, const void* k, const int32_t* seq_lens,
+                            void* kmin, void* kmax, hipStream_t stream) {
+  Shape s;
+  asp_status st = check_dims(dims, &s);
+  if (st != ASP_OK) return st;
+  if (page_size < 1 || page_size > s.T_cap) return ASP_ERR_INVALID_ARG;
+  if (!k || !seq_lens || !kmin || !kmax) return ASP_ERR_INVALID_ARG;
+  if (!aligned16(k) || !aligned16(kmin) || !aligned16(kmax) || !aligned4(seq_lens)) return ASP_ERR_INVALID_ARG;
+  return hip_status(asp::launch_page_summary(s, page_size, k, seq_lens, kmin, kmax, stream));
+}
+
+asp_status asp_page_scores(const asp_dims* dims, int32_t page_size, const float* q, const void* kmin,
+                           const void* kmax, const int32_t* seq_lens, float* scores, hipStream_t stream) {
+  Shape s;
+  asp_status st = check_dims(dims, &s);
+  if (st != ASP_OK) return st;
+  if (page_size < 1 || page_size > s.T_cap) return ASP_ERR_INVALID_ARG;
+  if (!q || !kmin || !kmax || !seq_lens || !scores) return ASP_ERR_INVALID_ARG;
+  if (!aligned4(q) || !aligned16(kmin) || !aligned16(kmax) || !aligned4(seq_lens) || !aligned4(scores))
+    return ASP_ERR_INVALID_ARG;
+  return hip_status(asp::launch_page_scores(s, page_size, q, kmin, kmax, seq_lens, scores, nullptr, stream));
+}
+
+size_t asp_page_select_workspace_size(const asp_dims* dims, const asp_cfg* cfg, int32_t page_size) {
+  Shape s;
+  if (check_all(dims, cfg, &s) != ASP_OK || page_size < 1 || s.C % page_size != 0) return 0;
+  return align_up(asp::page_select_ws_bytes(s, page_size));
+}
+
+asp_status asp_page_select(const asp_dims* dims, const asp_cfg* cfg, int32_t page_size, const float* q,
+                           const void* kmin, const void* kmax, const int32_t* seq_lens, int32_t* idx,
+                           int32_t* n_sel, void* ws, size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  asp_status st = check_all(dims, cfg, &s);
+  if (st != ASP_OK) return st;
+  if (page_size < 1 || s.C % page_size != 0) return ASP_ERR_INVALID_ARG;
+  if (!q || !kmin || !kmax || !seq_lens || !idx || !n_sel) return ASP_ERR_INVALID_ARG;
+  if (!aligned4(q) || !aligned16(kmin) || !aligned16(kmax) || !aligned4(seq_lens) || !aligned4(idx) ||
+      !aligned4(n_sel))
+    return ASP_ERR_INVALID_ARG;
+  const size_t need = align_up(asp::page_select_ws_bytes(s, page_size));
+  if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return ASP_ERR_WORKSPACE;
+  return hip_status(asp::launch_page_select(s, page_size, q, kmin, kmax, seq_lens, idx, n_sel, ws, stream));
+}
+
 asp_status asp_step(const asp_dims* dims, const asp_cfg* cfg, const float* q_cur, float* q_hist,
                     int32_t* hist_newest, int32_t* hist_len, const void* k, const void* v,
                     const int32_t* seq_lens, const int32_t* idx_cur, const int32_t* n_sel_cur,

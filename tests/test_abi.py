@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "asp_workspace_size", "asp_status_string", "asp_push_query", "asp_predict_query", "asp_score_keys",
         "asp_select_topc", "asp_score_candidates", "asp_select_candidates", "asp_sparse_decode", "asp_step",
-        "asp_selection_overlap", "asp_release_streams"])
+        "asp_selection_overlap", "asp_release_streams", "asp_page_summary_size", "asp_page_summary",
+        "asp_page_scores", "asp_page_select_workspace_size", "asp_page_select"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -166,3 +167,31 @@ def test_null_pointers_and_short_workspace_rejected(lib):
                         None, None, None) == 1
     assert lib.asp_step(*args, one, one, one, one, one, one, 1 << 40, ctypes.c_void_p(1), ctypes.c_void_p(2),
                         ctypes.c_void_p(3), None, None) == 1
+
+
+def test_page_sizes_and_argument_checks(lib):
+    d, c = _dims(), A.Cfg(16, 2048, 1e-2)
+    # summaries: B * Hkv * ceil(t_cap / P) * D * 2 bytes (bf16) each
+    assert A.asp_page_summary_size(d, 16) == 8 * 8 * 2048 * 128 * 2
+    assert A.asp_page_summary_size(_dims(t_cap=33, kv_dtype=A.KV_F32), 16) == 8 * 8 * 3 * 128 * 4
+    assert A.asp_page_summary_size(d, 0) == 0
+    assert A.asp_page_summary_size(d, 32769) == 0
+    assert A.asp_page_summary_size(_dims(head_dim=96), 16) == 0
+    ws = A.asp_page_select_workspace_size(d, c, 16)
+    assert ws >= 64 * 2048 * 4 + 64 * 128 * 4  # page scores and selected pages
+    assert ws % 256 == 0
+    assert A.asp_page_select_workspace_size(d, c, 24) == 0  # 2048 is not a multiple of 24
+    assert A.asp_page_select_workspace_size(d, A.Cfg(6, 2048, 1e-2), 16) == 0
+    one, P = ctypes.c_void_p(16), 16
+    dr, cr = ctypes.byref(d), ctypes.byref(c)
+    assert lib.asp_page_summary(dr, 0, one, one, one, one, None) == 1
+    assert lib.asp_page_summary(dr, P, None, one, one, one, None) == 1
+    assert lib.asp_page_summary(dr, P, one, one, ctypes.c_void_p(20), one, None) == 1  # kmin misaligned
+    assert lib.asp_page_summary(ctypes.byref(_dims(head_dim=96)), P, one, one, one, one, None) == 2
+    assert lib.asp_page_scores(dr, P, one, one, one, one, None, None) == 1
+    assert lib.asp_page_scores(dr, P, one, one, ctypes.c_void_p(24), one, one, None) == 1
+    assert lib.asp_page_select(dr, cr, 24, one, one, one, one, one, one, one, 1 << 40, None) == 1
+    assert lib.asp_page_select(dr, cr, P, one, one, one, one, None, one, one, 1 << 40, None) == 1
+    assert lib.asp_page_select(dr, cr, P, one, one, one, one, one, one, None, 1 << 40, None) == 3
+    assert lib.asp_page_select(dr, cr, P, one, one, one, one, one, one, one, ws - 1, None) == 3
+    assert lib.asp_page_select(dr, cr, P, one, one, one, one, one, one, ctypes.c_void_p(8), ws, None) == 3
