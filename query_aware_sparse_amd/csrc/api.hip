@@ -7,6 +7,7 @@
 
 #include "../../include/asp.h"
 #include "asp_internal.h"
+#include "page.h"
 
 using asp::Shape;
 

@@ -81,19 +81,6 @@ hipError_t launch_score_candidates(const Shape& s, const float* q_pred, const vo
 hipError_t launch_select_candidates(const Shape& s, const float* q_pred, const void* k, const int32_t* seq_lens,
                                     const CandWs& cw, int32_t* idx, int32_t* n_sel, int32_t* adv_newest,
                                     int32_t* adv_len, hipStream_t st, hipEvent_t done = nullptr);
-// Page-level selection (the Quest baseline): pages are runs of P tokens from
-// token 0, NP = page_count(T_cap, P) rows per unit.  Summaries kmin/kmax are
-// [units][NP][D] in the KV dtype; scores [units][NP] f32; counts (nullable)
-// receives each sequence's page count.  The selection keeps s.C / P pages and
-// writes their tokens (ascending) to idx, -1 after them.
-int page_count(int T_cap, int P);
-hipError_t launch_page_summary(const Shape& s, int P, const void* k, const int32_t* seq_lens, void* kmin, void* kmax,
-                               hipStream_t st);
-hipError_t launch_page_scores(const Shape& s, int P, const float* q, const void* kmin, const void* kmax,
-                              const int32_t* seq_lens, float* scores, int32_t* counts, hipStream_t st);
-size_t page_select_ws_bytes(const Shape& s, int P);
-hipError_t launch_page_select(const Shape& s, int P, const float* q, const void* kmin, const void* kmax,
-                              const int32_t* seq_lens, int32_t* idx, int32_t* n_sel, void* ws, hipStream_t st);
 // Per unit, the number of indices that two ascending selections share
 // (s.C <= overlap_max_c()).
 int overlap_max_c();

@@ -21,7 +21,7 @@
 // as 16-byte chunks, TPP = D * esize / 16 consecutive lanes per row (8, 16 or
 // 32), so a wave reads whole rows and the row-sum of the score is a reduction
 // inside a DPP row or a half-wave.
-#include "asp_internal.h"
+#include "page.h"
 
 namespace asp {
 namespace {
