@@ -15,6 +15,10 @@ layer, the Qwen3-32B layer or the ragged long-CoT batch; --top-c and --window
 override C and W); the roofline's measured traffic is then null, since the
 committed counter summary is of the Qwen3-8B layer.
 
+Beside the step, the page-level (Quest) baseline is timed on the same layers
+("page_baseline"): page scoring with the current query, top C / P pages and
+attention over their tokens, all on one stream (--page-size, 0 skips it).
+
 Prints one JSON line on stdout.  Everything else goes to stderr.
 """
 from __future__ import annotations
@@ -134,6 +138,57 @@ def cpu_baseline(wl, layer, q_t) -> dict:
                       "%.3f s each" % (wl.batch * wl.n_kv_heads, reps, el, per_step)}
 
 
+def page_baseline(A, dims, cfg, wl, layers, P, time_entry, out, ws_dec, attn, n) -> dict:
+    """The page-level (Quest) baseline on the same layers: its per-page min/max
+    summaries are built once per KV cache; each of its decode steps scores the
+    pages with the current query, keeps the top C / P pages and attends over
+    their tokens, all on the decode critical path (one stream)."""
+    import torch
+    B, Hq, Hkv, D, C = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.top_c
+    NP = A.page_count(wl.t_cap, P)
+    dev = layers[0]["k"].device
+    summ = []
+    for lay in layers:
+        kmin = torch.empty((B, Hkv, NP, D), dtype=lay["k"].dtype, device=dev)
+        kmax = torch.empty_like(kmin)
+        A.asp_page_summary(dims, P, lay["k"], lay["seq_lens"], kmin, kmax, stream=attn)
+        summ.append((kmin, kmax))
+    L = len(layers)
+    ws = torch.empty(A.asp_page_select_workspace_size(dims, cfg, P), dtype=torch.uint8, device=dev)
+    pscores = torch.empty((B, Hkv, NP), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, Hkv, C), dtype=torch.int32, device=dev)
+    nsel = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+
+    def q_of(i):
+        lay = layers[i % L]
+        return lay["qs"][lay["t"]]
+
+    def page_step(i):
+        lay, (kmin, kmax) = layers[i % L], summ[i % L]
+        A.asp_page_select(dims, cfg, P, q_of(i), kmin, kmax, lay["seq_lens"], idx, nsel, ws, stream=attn)
+        A.asp_sparse_decode(dims, cfg, q_of(i), lay["k"], lay["v"], lay["seq_lens"], idx, nsel, out, ws_dec,
+                            stream=attn)
+
+    t = {
+        "summary_us": time_entry(lambda i: A.asp_page_summary(dims, P, layers[i % L]["k"], layers[i % L]["seq_lens"],
+                                                              summ[i % L][0], summ[i % L][1], stream=attn), 20),
+        "page_scores_us": time_entry(lambda i: A.asp_page_scores(dims, P, q_of(i), summ[i % L][0], summ[i % L][1],
+                                                                 layers[i % L]["seq_lens"], pscores, stream=attn), n),
+        "page_select_us": time_entry(lambda i: A.asp_page_select(dims, cfg, P, q_of(i), summ[i % L][0],
+                                                                 summ[i % L][1], layers[i % L]["seq_lens"], idx, nsel,
+                                                                 ws, stream=attn), n),
+        "step_us": time_entry(page_step, n),
+    }
+    lens = [int(x) for x in layers[0]["seq_lens"].tolist()]
+    esize = 2 if wl.kv_dtype == "bf16" else 4
+    scan = sum(Hkv * ((T + P - 1) // P) * D * esize * 2 for T in lens)  # kmin + kmax rows read
+    res = {k_: round(v_, 2) for k_, v_ in t.items()}
+    res.update({"page_size": P, "pages_kept": C // P, "summary_bytes_read_per_step": scan,
+                "page_scores_GBps": round(scan / (t["page_scores_us"] * 1e-6) / 1e9, 1),
+                "steps_per_s": round(1e6 / t["step_us"], 1)})
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -148,6 +203,8 @@ def main() -> int:
     ap.add_argument("--window", type=int, default=None, help="override the workload's ridge window W")
     ap.add_argument("--recent", type=int, default=0, help="newest tokens attended beside the selection")
     ap.add_argument("--kernel-launches", type=int, default=200)
+    ap.add_argument("--page-size", type=int, default=16,
+                    help="page size of the page-level (Quest) baseline timed beside the step (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (rocprofv3 counter calibration)")
@@ -308,6 +365,11 @@ def main() -> int:
                 "algorithmic_bytes_per_launch": sk_bytes, "avg_launch_us": round(kern["score_us"], 2)}
     log("per-kernel us: %s" % json.dumps({k_: round(v_, 2) for k_, v_ in kern.items()}))
 
+    page = None
+    if args.page_size > 0 and C % args.page_size == 0:
+        page = page_baseline(A, dims, cfg, wl, layers, args.page_size, time_entry, out, ws_dec, attn, n)
+        log("page baseline: %s" % json.dumps(page))
+
     cpu = None
     if not args.no_cpu_baseline:
         lay = layers[0]
@@ -328,6 +390,7 @@ def main() -> int:
         "bytes_per_step": nbytes,
         "kernels_us": {k_: round(v_, 2) for k_, v_ in kern.items()},
         "roofline": roofline,
+        "page_baseline": page,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -8,19 +8,21 @@
 // grouped-query attention a KV head takes the largest bound of its query heads,
 // as its token scores take the largest dot product.
 //
-// Three launches:
+// Launches:
 //  - page_summary_kernel: one pass over K writing kmin/kmax rows in the KV
-//    dtype (exact copies of key elements);
+//    dtype (exact copies of key elements), once per cache;
 //  - page_score_kernel: one pass over the summaries, a page score row per unit
-//    (f32), plus the page count of every sequence for the selection;
-//  - the token-level top-C selection (select.hip) run on the page rows with a
-//    budget of C / P pages, then page_tokens_kernel, which lists the selected
-//    pages' tokens in ascending order as asp_sparse_decode reads them.
+//    (f32), plus the page count of every sequence;
+//  - page_topk_kernel: one workgroup per unit keeps the top C / P pages and
+//    writes their tokens in ascending order, as asp_sparse_decode reads them;
+//    rows of more than PAGE_TOPK_MAX pages take the token-level selection
+//    (select.hip) on the page rows instead, then page_tokens_kernel.
 //
 // Thread layout of the two streaming kernels: a page row of D elements is read
 // as 16-byte chunks, TPP = D * esize / 16 consecutive lanes per row (8, 16 or
 // 32), so a wave reads whole rows and the row-sum of the score is a reduction
 // inside a DPP row or a half-wave.
+#include "block_scan.h"
 #include "page.h"
 
 namespace asp {
@@ -28,6 +30,9 @@ namespace {
 
 constexpr int PAGE_THREADS = 256;
 constexpr int PAGE_SCORE_ROUNDS = 8;  // page rows per lane group of a score block
+constexpr int PAGE_SCORE_BATCH = 2;   // of which loaded before any is reduced
+constexpr int PAGE_TOPK_THREADS = 1024;
+constexpr int PAGE_TOPK_MAX = 16384;  // pages per unit whose keys one workgroup holds in LDS
 
 template <int D, int KV>
 struct RowChunks {
@@ -150,22 +155,136 @@ __global__ __launch_bounds__(PAGE_THREADS) void page_score_kernel(const float* _
   }
   const int p_end = min(n_pages, p0 + RC::ppb * PAGE_SCORE_ROUNDS);
   const size_t base = (size_t)u * NP * RC::row_bytes + (size_t)c * 16;
-  for (int p = p0; p < p_end; p += RC::ppb) {
-    const size_t off = base + (size_t)p * RC::row_bytes;
-    float lo[RC::ept], hi[RC::ept];
-    widen16<KV>(*reinterpret_cast<const uint4*>(kmin + off), lo);
-    widen16<KV>(*reinterpret_cast<const uint4*>(kmax + off), hi);
-    float best = 0.0f;
+  for (int r0 = 0; r0 < PAGE_SCORE_ROUNDS; r0 += PAGE_SCORE_BATCH) {
+    uint4 wlo[PAGE_SCORE_BATCH], whi[PAGE_SCORE_BATCH];  // a batch of rows in flight
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float acc = 0.0f;
-#pragma unroll
-      for (int e = 0; e < RC::ept; ++e) acc += fmaxf(qv[h][e] * lo[e], qv[h][e] * hi[e]);
-      acc = group_sum<RC::tpp>(acc);
-      best = h == 0 ? acc : fmaxf(best, acc);
+    for (int j = 0; j < PAGE_SCORE_BATCH; ++j) {
+      const int p = p0 + (r0 + j) * RC::ppb;
+      wlo[j] = whi[j] = make_uint4(0u, 0u, 0u, 0u);
+      if (p < p_end) {
+        const size_t off = base + (size_t)p * RC::row_bytes;
+        wlo[j] = *reinterpret_cast<const uint4*>(kmin + off);
+        whi[j] = *reinterpret_cast<const uint4*>(kmax + off);
+      }
     }
-    if (c == 0) scores[(size_t)u * NP + p] = best;
+#pragma unroll
+    for (int j = 0; j < PAGE_SCORE_BATCH; ++j) {
+      const int p = p0 + (r0 + j) * RC::ppb;
+      if (p >= p_end) break;  // the same for the whole lane group
+      float lo[RC::ept], hi[RC::ept];
+      widen16<KV>(wlo[j], lo);
+      widen16<KV>(whi[j], hi);
+      float best = 0.0f;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int e = 0; e < RC::ept; ++e) acc += fmaxf(qv[h][e] * lo[e], qv[h][e] * hi[e]);
+        acc = group_sum<RC::tpp>(acc);
+        best = h == 0 ? acc : fmaxf(best, acc);
+      }
+      if (c == 0) scores[(size_t)u * NP + p] = best;
+    }
   }
+}
+
+// One workgroup per unit (n pages <= PAGE_TOPK_MAX): the top K pages of the
+// unit's score row, as their tokens in ascending order.  The pages' order keys
+// sit in LDS; the K-th key comes from three radix digits (11, 11, 10 bits),
+// then two bitmaps (keys above it, keys equal to it) are compacted in page
+// order, ties taking the lowest pages.  Each chosen page writes its P tokens
+// at its rank; the partial last page, if chosen, is the last one written.
+template <int NT>
+__global__ __launch_bounds__(NT) void page_topk_kernel(const float* __restrict__ scores,
+                                                       const int32_t* __restrict__ seq_lens,
+                                                       int32_t* __restrict__ idx, int32_t* __restrict__ n_sel,
+                                                       int Hkv, int T_cap, int P, int NP, int K, int C) {
+  __shared__ uint32_t key[PAGE_TOPK_MAX];
+  __shared__ uint32_t hist[HIST_BINS];
+  __shared__ uint32_t bm_gt[PAGE_TOPK_MAX / 32], bm_eq[PAGE_TOPK_MAX / 32];
+  __shared__ uint32_t scratch[NT / 64];
+  __shared__ uint32_t sh[4];
+  __shared__ int last_taken;
+  const int u = blockIdx.x, b = u / Hkv, tid = threadIdx.x;
+  const int T = clampi(seq_lens[b], 0, T_cap);
+  const int n = min((T + P - 1) / P, NP);
+  const int k_eff = min(K, n);
+  int32_t* out = idx + (size_t)u * C;
+  if (k_eff == n) {  // every page: the tokens [0, T), T <= K * P = C
+    for (int j = tid; j < C; j += NT) out[j] = j < T ? j : -1;
+    if (tid == 0) n_sel[u] = T;
+    return;
+  }
+  const float* row = scores + (size_t)u * NP;
+  for (int i = tid; i < n; i += NT) key[i] = order_key(row[i]);
+  uint32_t prefix = 0u, pmask = 0u, need = (uint32_t)k_eff;
+  const int shifts[3] = {HIST_SHIFT, 10, 0};
+  const uint32_t dmasks[3] = {0x7ffu, 0x7ffu, 0x3ffu};
+  for (int pass = 0; pass < 3; ++pass) {
+    for (int j = tid; j < HIST_BINS; j += NT) hist[j] = 0u;
+    __syncthreads();
+    const int sft = shifts[pass];
+    const uint32_t dm = dmasks[pass];
+    for (int i = tid; i < n; i += NT) {
+      const uint32_t k = key[i];
+      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> sft) & dm], 1u);
+    }
+    __syncthreads();
+    pick_digits<NT>(hist, need, 0u, scratch, sh);
+    __syncthreads();
+    const uint32_t d = sh[0] & dm;
+    need -= sh[1];
+    prefix |= d << sft;
+    pmask |= dm << sft;
+    const bool done = hist[d] == need;  // every remaining key of this digit is taken
+    __syncthreads();
+    if (done) break;
+  }
+  const int nwords = (n + 31) / 32;
+  for (int j = tid; j < nwords; j += NT) {
+    bm_gt[j] = 0u;
+    bm_eq[j] = 0u;
+  }
+  if (tid == 0) last_taken = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += NT) {
+    const uint32_t mk = key[i] & pmask, bit = 1u << (i & 31);
+    if (mk > prefix) atomicOr(&bm_gt[i >> 5], bit);
+    else if (mk == prefix) atomicOr(&bm_eq[i >> 5], bit);
+  }
+  __syncthreads();
+  // NT bitmap words per round, in page order
+  uint32_t written = 0u, eq_seen = 0u;
+  for (int w0 = 0; w0 < nwords; w0 += NT) {
+    const int wi = w0 + tid;
+    uint32_t eqw = wi < nwords ? bm_eq[wi] : 0u;
+    const uint32_t gtw = wi < nwords ? bm_gt[wi] : 0u;
+    uint32_t eq_tot;
+    const uint32_t eb = eq_seen + block_excl_n<NT>((uint32_t)__popc(eqw), scratch, &eq_tot);
+    uint32_t take = 0u;  // the lowest set bits of eqw while fewer than `need` ties are taken
+    for (uint32_t k = eb; eqw != 0u && k < need; ++k) {
+      const uint32_t low = eqw & (0u - eqw);
+      take |= low;
+      eqw ^= low;
+    }
+    eq_seen += eq_tot;
+    uint32_t wv = gtw | take, tot;
+    uint32_t at = written + block_excl_n<NT>((uint32_t)__popc(wv), scratch, &tot);
+    if (wi == (n - 1) >> 5 && ((wv >> ((n - 1) & 31)) & 1u)) last_taken = 1;
+    while (wv != 0u) {
+      const int p = wi * 32 + __ffs((int)wv) - 1;
+      wv &= wv - 1u;
+      const int first = p * P, cnt = min(P, T - first);
+      int32_t* o = out + (size_t)at * P;
+      for (int r = 0; r < cnt; ++r) o[r] = first + r;
+      ++at;
+    }
+    written += tot;
+  }
+  __syncthreads();
+  const int total = k_eff * P - (last_taken ? n * P - T : 0);
+  for (int j = total + tid; j < C; j += NT) out[j] = -1;
+  if (tid == 0) n_sel[u] = total;
 }
 
 // One block per unit: the tokens of the n selected pages (ascending page
@@ -293,8 +412,15 @@ hipError_t launch_page_select(const Shape& s, int P, const float* q, const void*
                               const int32_t* seq_lens, int32_t* idx, int32_t* n_sel, void* ws, hipStream_t st) {
   if (s.B == 0) return hipSuccess;
   const PageWs w = page_carve(s, P, ws);
+  const int NP = page_count(s.T_cap, P);
   hipError_t e = launch_page_scores(s, P, q, kmin, kmax, seq_lens, w.scores, w.counts, st);
   if (e != hipSuccess) return e;
+  if (NP <= PAGE_TOPK_MAX) {
+    hipLaunchKernelGGL(page_topk_kernel<PAGE_TOPK_THREADS>, dim3(s.B * s.Hkv), dim3(PAGE_TOPK_THREADS), 0, st,
+                       w.scores, seq_lens, idx, n_sel, s.Hkv, s.T_cap, P, NP, s.C / P, s.C);
+    return hipGetLastError();
+  }
+  // Longer rows: the token-level selection on the page rows, then the token lists.
   e = launch_select(page_shape(s, P), w.scores, nullptr, w.counts, w.pidx, w.pn, nullptr, nullptr, w.sel, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(page_tokens_kernel, dim3(s.B * s.Hkv), dim3(PAGE_THREADS), 0, st, w.pidx, w.pn, seq_lens, idx,

@@ -116,6 +116,8 @@ CASES = [
     (3, 4, 2, 128, 1500, "f32", [1500, 777, 1], 16, 256),
     (2, 4, 4, 64, 1030, "f32", [1030, 1029], 1, 96),
     (2, 16, 2, 128, 2048, "bf16", [2048, 0], 32, 32),
+    # more pages than one workgroup holds: the row-selection route
+    (2, 4, 2, 64, 17000, "bf16", [17000, 16500], 1, 256),
 ]
 
 
@@ -200,6 +202,37 @@ def test_one_token_pages_match_the_token_selection():
     s_orc = oracle.score(np_(q), kv_np(k), lens)
     assert_selection_within_gap(np_(idx), np_(n_sel), s_orc, lens, C)
     assert_selection_within_gap(np_(idx_t), np_(n_t), s_orc, lens, C)
+
+
+@pytest.mark.parametrize("P", [16, 7])
+def test_partial_last_page_chosen(P):
+    # The last page of each sequence holds a few tokens whose keys stand out,
+    # so it is chosen; it must be listed last and only with its valid tokens.
+    B, Hq, Hkv, D, T_cap = 2, 8, 2, 128, 1000
+    lens = [995, 990]
+    C = 10 * P
+    k, q, lens_t = _inputs(B, Hq, Hkv, D, T_cap, "bf16", lens, seed=11 + P)
+    q = q.abs()
+    for b, T in enumerate(lens):
+        last = (T - 1) // P * P
+        k[b, :, last:T] = 4.0
+    dims = dims_for(A, B, Hq, Hkv, D, T_cap, "bf16")
+    cfg = A.Cfg(16, C, 1e-2)
+    kmin, kmax = _summaries(dims, P, k, lens_t)
+    idx = torch.empty((B, Hkv, C), dtype=torch.int32, device=DEV)
+    n_sel = torch.empty((B, Hkv), dtype=torch.int32, device=DEV)
+    A.asp_page_select(dims, cfg, P, q, kmin, kmax, lens_t, idx, n_sel)
+    torch.cuda.synchronize()
+    o_min, o_max = oracle.page_summary(kv_np(k), lens, P)
+    n_pages = oracle.page_counts(lens, T_cap, P)
+    s_orc = oracle.page_scores(np_(q), o_min, o_max, n_pages)
+    _check_selection(np_(idx), np_(n_sel), s_orc, n_pages, lens, P, C)
+    for b, T in enumerate(lens):
+        part = T - (T - 1) // P * P
+        for g in range(Hkv):
+            n = int(np_(n_sel)[b, g])
+            assert n == C - P + part
+            np.testing.assert_array_equal(np_(idx)[b, g, n - part:n], np.arange(T - part, T))
 
 
 def test_page_step_attention_matches_the_oracle():
