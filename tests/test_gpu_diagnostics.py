@@ -89,7 +89,12 @@ def test_diagnostics_counts_match_oracle():
     for t, cnt in res["rec_last"].items():
         a, b = host(res["true"][t - 1]), host(res["true"][t])
         np.testing.assert_array_equal(np_(cnt), oracle.overlap(a[0], a[1], b[0], b[1], T_cap))
+    assert res["page_size"] == 16 and sorted(res["rec_page"]) == sorted(res["rec_pred"])
+    for t, cnt in res["rec_page"].items():
+        a, b = host(res["page"][t]), host(res["true"][t])
+        np.testing.assert_array_equal(np_(cnt), oracle.overlap(a[0], a[1], b[0], b[1], T_cap))
     s = dg.summarize(wl, res)
+    assert 0.0 <= s["recall_page_current_query"] <= 1.0
     rp = [np.mean(np_(res["rec_pred"][t]) / np_(res["true"][t][1])) for t in sorted(res["rec_pred"])]
     assert s["recall_predicted"] == pytest.approx(np.mean(rp), rel=1e-12)
     assert 0.0 <= s["recall_last_query"] <= 1.0 and 0.0 <= s["temporal_overlap_window_mean"] <= 1.0

@@ -90,3 +90,52 @@ def test_captured_entry_point_step_replays_match_eager(wl_name):
         for name, a, b in zip(("out", "idx", "n_sel", "q_hist", "newest", "len"), graph_state.snapshot(0),
                               eager_state.snapshot(0)):
             np.testing.assert_array_equal(a, b, err_msg="replay %d %s" % (rep, name))
+
+
+def test_captured_page_step_replays_match_eager():
+    # The page-level baseline's step (page selection with the current query,
+    # then attention over the chosen pages' tokens) in a graph.
+    require_gpu()
+    B, Hq, Hkv, D, T, P, C = 3, 16, 4, 128, 5000, 16, 1024
+    wl = wk.Q8B_LAYER.replace(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, t_cap=T, seed=21)
+    lens = torch.tensor([5000, 3001, 100], dtype=torch.int32)
+    k, v = wk.make_kv(wl, lens, device=DEV)
+    lens = lens.to(DEV)
+    qs = wk.make_queries(wl, 6, device=DEV)
+    dims = A.Dims(B, Hq, Hkv, D, T, A.KV_BF16)
+    cfg = A.Cfg(16, C, 1e-2)
+    NP = A.page_count(T, P)
+    kmin = torch.empty((B, Hkv, NP, D), dtype=torch.bfloat16, device=DEV)
+    kmax = torch.empty_like(kmin)
+    A.asp_page_summary(dims, P, k, lens, kmin, kmax)
+
+    def buffers():
+        return dict(idx=torch.full((B, Hkv, C), -5, dtype=torch.int32, device=DEV),
+                    n=torch.zeros((B, Hkv), dtype=torch.int32, device=DEV),
+                    out=torch.zeros((B, Hq, D), device=DEV),
+                    ws=torch.empty(A.asp_page_select_workspace_size(dims, cfg, P), dtype=torch.uint8, device=DEV),
+                    wsd=torch.empty(A.asp_workspace_size(dims, cfg, A.OP_DECODE), dtype=torch.uint8, device=DEV))
+
+    def step(bf, q, stream=None):
+        A.asp_page_select(dims, cfg, P, q, kmin, kmax, lens, bf["idx"], bf["n"], bf["ws"], stream=stream)
+        A.asp_sparse_decode(dims, cfg, q, k, v, lens, bf["idx"], bf["n"], bf["out"], bf["wsd"], stream=stream)
+
+    gb, eb = buffers(), buffers()
+    q_buf = qs[0].clone()
+    step(buffers(), q_buf)  # one eager call before the capture
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        step(gb, q_buf, stream=side)
+    torch.cuda.synchronize()
+    for rep in range(1, 6):
+        q_buf.copy_(qs[rep])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        step(eb, qs[rep])
+        torch.cuda.synchronize()
+        for name in ("idx", "n", "out"):
+            np.testing.assert_array_equal(np_(gb[name]), np_(eb[name]), err_msg="replay %d %s" % (rep, name))
