@@ -122,3 +122,37 @@ def test_ragged_long_cot_full_size(ragged_kv, W, C):
     # the shortest, the longest and one mid-length sequence
     order = np.argsort(lens)
     _full_shape_check(p, units=sorted({int(order[0]), int(order[len(order) // 2]), int(order[-1])}))
+
+
+def test_ragged_long_cot_page_baseline_full_size(ragged_kv):
+    # The page-level baseline on the full ragged batch (8192 page rows per
+    # unit, pages of 16, C = 2048): summaries bit-exact and the selection by
+    # the gap rule on the shortest, a mid-length and the longest sequence.
+    import oracle
+    from asp_testutil import kv_np
+    from test_gpu_page import _check_selection, _check_summaries
+    k, _ = ragged_kv
+    wl = wk.RAGGED
+    B, Hq, Hkv, D, T, P, C = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.t_cap, 16, wl.top_c
+    lens_t = wk.make_seq_lens(wl, device=DEV)
+    q = wk.make_queries(wl, 1, device=DEV)[0].contiguous()
+    dims = A.Dims(B, Hq, Hkv, D, T, A.KV_BF16)
+    cfg = A.Cfg(wl.window, C, wl.lam)
+    NP = A.page_count(T, P)
+    kmin = torch.empty((B, Hkv, NP, D), dtype=torch.bfloat16, device=DEV)
+    kmax = torch.empty_like(kmin)
+    A.asp_page_summary(dims, P, k, lens_t, kmin, kmax)
+    idx = torch.empty((B, Hkv, C), dtype=torch.int32, device=DEV)
+    n_sel = torch.empty((B, Hkv), dtype=torch.int32, device=DEV)
+    A.asp_page_select(dims, cfg, P, q, kmin, kmax, lens_t, idx, n_sel)
+    torch.cuda.synchronize()
+    lens = np_(lens_t)
+    order = np.argsort(lens)
+    bs = sorted({int(order[0]), int(order[len(order) // 2]), int(order[-1])})
+    sl = [int(lens[b]) for b in bs]
+    o_min, o_max = oracle.page_summary(kv_np(k[bs]), sl, P)
+    n_pages = oracle.page_counts(sl, T, P)
+    _check_summaries(kmin[bs], kmax[bs], o_min, o_max, n_pages)
+    s_orc = oracle.page_scores(np_(q[bs]), o_min, o_max, n_pages)
+    _check_selection(np_(idx[bs]), np_(n_sel[bs]), s_orc, n_pages, sl, P, C)
+    del kmin, kmax
