@@ -18,6 +18,9 @@
 //    rows of more than PAGE_TOPK_MAX pages take the token-level selection
 //    (select.hip) on the page rows instead, then page_tokens_kernel.
 //
+// The larger of q_d * min_d and q_d * max_d is q_d * max_d when q_d >= 0 and
+// q_d * min_d otherwise, so each term is one select and one fused multiply-add.
+//
 // Thread layout of the two streaming kernels: a page row of D elements is read
 // as 16-byte chunks, TPP = D * esize / 16 consecutive lanes per row (8, 16 or
 // 32), so a wave reads whole rows and the row-sum of the score is a reduction
@@ -145,13 +148,25 @@ __global__ __launch_bounds__(PAGE_THREADS) void page_score_kernel(const float* _
   if (counts != nullptr && g == 0 && blockIdx.x == 0 && threadIdx.x == 0) counts[b] = n_pages;
   const int c = (int)threadIdx.x % RC::tpp;
   const int p0 = blockIdx.x * RC::ppb * PAGE_SCORE_ROUNDS + (int)threadIdx.x / RC::tpp;
+  // With eight query heads the group's queries sit in LDS and each head's chunk
+  // is read there per row (registers for all eight would halve the waves in
+  // flight); fewer heads keep theirs in registers.
+  constexpr bool Q_LDS = G >= 8;
+  __shared__ __align__(16) float q_s[Q_LDS ? G * D : 1];
+  if constexpr (Q_LDS) {
+    const float* qg = q + ((size_t)b * Hq + (size_t)g * G) * D;
+    for (int i = threadIdx.x; i < G * D; i += PAGE_THREADS) q_s[i] = qg[i];
+    __syncthreads();
+  }
   if (p0 >= n_pages) return;
-  float qv[G][RC::ept];
+  float qv[Q_LDS ? 1 : G][RC::ept];
+  if constexpr (!Q_LDS) {
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float* qh = q + ((size_t)b * Hq + (size_t)g * G + h) * D + c * RC::ept;
+    for (int h = 0; h < G; ++h) {
+      const float* qh = q + ((size_t)b * Hq + (size_t)g * G + h) * D + c * RC::ept;
 #pragma unroll
-    for (int e = 0; e < RC::ept; ++e) qv[h][e] = qh[e];
+      for (int e = 0; e < RC::ept; ++e) qv[h][e] = qh[e];
+    }
   }
   const int p_end = min(n_pages, p0 + RC::ppb * PAGE_SCORE_ROUNDS);
   const size_t base = (size_t)u * NP * RC::row_bytes + (size_t)c * 16;
@@ -178,8 +193,23 @@ __global__ __launch_bounds__(PAGE_THREADS) void page_score_kernel(const float* _
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float acc = 0.0f;
+        if constexpr (Q_LDS) {
+          float qh[RC::ept];
+          const float4* src = reinterpret_cast<const float4*>(q_s + h * D + c * RC::ept);
 #pragma unroll
-        for (int e = 0; e < RC::ept; ++e) acc += fmaxf(qv[h][e] * lo[e], qv[h][e] * hi[e]);
+          for (int e4 = 0; e4 < RC::ept / 4; ++e4) {
+            const float4 x = src[e4];
+            qh[4 * e4] = x.x;
+            qh[4 * e4 + 1] = x.y;
+            qh[4 * e4 + 2] = x.z;
+            qh[4 * e4 + 3] = x.w;
+          }
+#pragma unroll
+          for (int e = 0; e < RC::ept; ++e) acc = fmaf(qh[e], qh[e] < 0.0f ? lo[e] : hi[e], acc);
+        } else {
+#pragma unroll
+          for (int e = 0; e < RC::ept; ++e) acc = fmaf(qv[h][e], qv[h][e] < 0.0f ? lo[e] : hi[e], acc);
+        }
         acc = group_sum<RC::tpp>(acc);
         best = h == 0 ? acc : fmaxf(best, acc);
       }
