@@ -5,7 +5,9 @@
  * queries, scores every cached key of each KV head against the prediction,
  * keeps the top-C tokens per (sequence, KV head), and runs decode attention
  * with the actual query over only those tokens.  Selection for the next step
- * can run on a second HIP stream while this step's attention runs.
+ * can run on a second HIP stream while this step's attention runs.  The
+ * page-level selection the pages compare against (asp_page_*) is provided
+ * beside it as a baseline.
  *
  * Sources: [card] the Hugging Face dataset card "Reproduction: AsyncSpade --
  * Efficient Test-Time Scaling with Asynchronous Sparse Decoding"; [summary] the
