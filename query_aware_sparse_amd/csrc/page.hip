@@ -222,8 +222,8 @@ __global__ __launch_bounds__(PAGE_THREADS) void page_score_kernel(const float* _
 // unit's score row, as their tokens in ascending order.  The pages' order keys
 // sit in LDS; the K-th key comes from three radix digits (11, 11, 10 bits),
 // then two bitmaps (keys above it, keys equal to it) are compacted in page
-// order, ties taking the lowest pages.  Each chosen page writes its P tokens
-// at its rank; the partial last page, if chosen, is the last one written.
+// order, ties taking the lowest pages.  The chosen pages are listed in LDS,
+// and the workgroup then writes their tokens in order.
 template <int NT>
 __global__ __launch_bounds__(NT) void page_topk_kernel(const float* __restrict__ scores,
                                                        const int32_t* __restrict__ seq_lens,
@@ -301,19 +301,17 @@ __global__ __launch_bounds__(NT) void page_topk_kernel(const float* __restrict__
     uint32_t wv = gtw | take, tot;
     uint32_t at = written + block_excl_n<NT>((uint32_t)__popc(wv), scratch, &tot);
     if (wi == (n - 1) >> 5 && ((wv >> ((n - 1) & 31)) & 1u)) last_taken = 1;
-    while (wv != 0u) {
-      const int p = wi * 32 + __ffs((int)wv) - 1;
+    while (wv != 0u) {  // the chosen pages in page order, over the keys (no longer read)
+      key[at++] = (uint32_t)(wi * 32 + __ffs((int)wv) - 1);
       wv &= wv - 1u;
-      const int first = p * P, cnt = min(P, T - first);
-      int32_t* o = out + (size_t)at * P;
-      for (int r = 0; r < cnt; ++r) o[r] = first + r;
-      ++at;
     }
     written += tot;
   }
   __syncthreads();
+  // Token lists, written by the whole workgroup in order (the partial last
+  // page, if chosen, is the last listed, so its missing tokens are the tail).
   const int total = k_eff * P - (last_taken ? n * P - T : 0);
-  for (int j = total + tid; j < C; j += NT) out[j] = -1;
+  for (int j = tid; j < C; j += NT) out[j] = j < total ? (int)key[j / P] * P + j % P : -1;
   if (tid == 0) n_sel[u] = total;
 }
 
