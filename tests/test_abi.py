@@ -195,3 +195,22 @@ def test_page_sizes_and_argument_checks(lib):
     assert lib.asp_page_select(dr, cr, P, one, one, one, one, one, one, None, 1 << 40, None) == 3
     assert lib.asp_page_select(dr, cr, P, one, one, one, one, one, one, one, ws - 1, None) == 3
     assert lib.asp_page_select(dr, cr, P, one, one, one, one, one, one, ctypes.c_void_p(8), ws, None) == 3
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    # No fallback: without libasp.so every entry point raises instead of
+    # computing anything elsewhere.  Run in a child process so that this
+    # process's loaded library is untouched.
+    import subprocess
+    import sys
+    code = (
+        "import query_aware_sparse_amd as A\n"
+        "A._LIB_PATH = %r\n"
+        "try:\n"
+        "    A.asp_workspace_size(A.Dims(1, 2, 1, 64, 64, 0), A.Cfg(8, 8, 1e-2), A.OP_SELECT)\n"
+        "except A.AspError as e:\n"
+        "    print('raised:', e)\n"
+        "else:\n"
+        "    print('no error')\n" % str(tmp_path / "libasp.so"))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT, timeout=120)
+    assert "raised: libasp.so is not built" in r.stdout, r.stdout + r.stderr
