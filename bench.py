@@ -135,7 +135,23 @@ def cpu_baseline(wl, layer, q_t) -> dict:
     per_step = el / reps
     return {"value": 1.0 / per_step, "unit": "steps/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": "full step of one layer (all %d units), %d timed repetitions (%.1f s) after 1 warm-up, "
-                      "%.3f s each" % (wl.batch * wl.n_kv_heads, reps, el, per_step)}
+                      "%.3f s each" % (wl.batch * wl.n_kv_heads, reps, el, per_step),
+            "host": host_cpu()}
+
+
+def host_cpu() -> dict:
+    """The host the oracle ran on: its CPU model and the processors the OS reports."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(),
+            "usable": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
 
 
 def page_baseline(A, dims, cfg, wl, layers, P, time_entry, out, ws_dec, attn, n) -> dict:
