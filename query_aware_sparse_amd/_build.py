@@ -49,23 +49,27 @@ def build_library() -> str:
     return LIB
 
 
-C_ABI_CHECK_SRC = os.path.join(ROOT, "tests", "c_abi", "step_check.cpp")
-C_ABI_CHECK_BIN = os.path.join(ROOT, "tests", "c_abi", "step_check")
+C_ABI_DIR = os.path.join(ROOT, "tests", "c_abi")
+C_ABI_CHECKS = ["step_check", "page_check"]
 
 
-def build_c_abi_check() -> str:
-    """The C++ program that drives the C ABI without Python (tests/c_abi); it
-    finds libasp.so through a path relative to itself."""
-    tmp = C_ABI_CHECK_BIN + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "--offload-arch=" + ARCH, "-O2", "-std=c++17", "-Wall",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-I" + os.path.join(ROOT, "include"), C_ABI_CHECK_SRC, "-L" + PKG, "-lasp",
-           "-Wl,-rpath,$ORIGIN/../../query_aware_sparse_amd", "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed for the C ABI check:\n%s\n%s" % (" ".join(cmd), r.stderr))
-    os.replace(tmp, C_ABI_CHECK_BIN)
-    return C_ABI_CHECK_BIN
+def build_c_abi_check() -> list:
+    """The C++ programs that drive the C ABI without Python (tests/c_abi); they
+    find libasp.so through a path relative to themselves."""
+    built = []
+    for name in C_ABI_CHECKS:
+        out = os.path.join(C_ABI_DIR, name)
+        tmp = out + ".tmp%d" % os.getpid()
+        cmd = [HIPCC, "--offload-arch=" + ARCH, "-O2", "-std=c++17", "-Wall",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-I" + os.path.join(ROOT, "include"), os.path.join(C_ABI_DIR, name + ".cpp"), "-L" + PKG, "-lasp",
+               "-Wl,-rpath,$ORIGIN/../../query_aware_sparse_amd", "-o", tmp]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("hipcc failed for the C ABI check:\n%s\n%s" % (" ".join(cmd), r.stderr))
+        os.replace(tmp, out)
+        built.append(out)
+    return built
 
 
 if __name__ == "__main__":

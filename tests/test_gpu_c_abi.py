@@ -1,4 +1,4 @@
-"""The C ABI from C++ alone (GPU required): tests/c_abi/step_check.cpp, built by
+"""The C ABI from C++ alone (GPU required).  tests/c_abi/step_check.cpp, built by
 __graft_entry__.build(), runs a layer's pipelined steps on one stream and on two
 streams through include/asp.h with hipMalloc'd buffers and checks that every
 step's output, selection and query ring agree bit for bit."""
@@ -23,3 +23,18 @@ def test_c_abi_pipelined_steps_agree_across_stream_modes():
     assert "c-abi step check: ok" in r.stdout
     assert r.stdout.count("one stream and two streams agree") == 6
     assert "bootstrap: agree" in r.stdout
+
+
+def test_c_abi_page_baseline():
+    # tests/c_abi/page_check.cpp: one-token pages against the token-level
+    # selection (bit for bit on small-integer inputs), and well-formed page
+    # token lists with pages of 16.
+    require_gpu()
+    page_bin = os.path.join(os.path.dirname(__file__), "c_abi", "page_check")
+    assert os.path.exists(page_bin), "tests/c_abi/page_check is not built; run __graft_entry__.build()"
+    r = subprocess.run([page_bin], capture_output=True, text=True, timeout=120)
+    print(r.stdout, r.stderr, flush=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "one-token pages and the token selection agree" in r.stdout
+    assert "page token lists well-formed" in r.stdout
+    assert "c-abi page check: ok" in r.stdout
