@@ -227,10 +227,11 @@ asp_status asp_sparse_decode(const asp_dims* dims, const asp_cfg* cfg, const flo
                              size_t ws_bytes, hipStream_t stream);
 
 /* Page-level selection, the baseline the pages compare against ([summary]
- * "Problem" and "Baselines"; [abstract]: Quest, which selects pages of the KV
- * cache with the current query, on the decode critical path).  The pages do
- * not define how a page is scored; the score is the criticality estimate that
- * Quest publishes (Tang et al., ICML 2024, method section):
+ * "Problem" and "Experimental setup", its baselines; [abstract]: Quest, which
+ * selects pages of the KV cache with the current query, on the decode critical
+ * path).  The pages do not define how a page is scored; the score is the
+ * criticality estimate that Quest publishes (Tang et al., ICML 2024, method
+ * section):
  *   pages: runs of P = page_size consecutive tokens from token 0,
  *     NP = ceil(t_cap / P) page rows per unit; page p of sequence b holds the
  *     tokens [p*P, min(p*P + P, T)), T = seq_lens[b] clamped to [0, t_cap], so

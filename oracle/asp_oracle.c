@@ -388,10 +388,11 @@ void oracle_overlap(int units, int C, int T_cap, const int* idx_a, const int* n_
 
 /* ------------------------------------------------------------------------- */
 /* Page-level selection, the baseline the pages compare against.  [summary]   */
-/* "Problem" and "Baselines", [abstract]: Quest selects whole pages of the KV  */
-/* cache with the current query.  The pages do not define how a page is        */
-/* scored; the definition used is the one Quest publishes (Tang et al.,        */
-/* "Quest: Query-Aware Sparsity for Efficient Long-Context LLM Inference",     */
+/* "Problem" and "Experimental setup" (its baselines), [abstract]: Quest       */
+/* selects whole pages of the KV cache with the current query.  The pages do   */
+/* not define how a page is scored; the definition used is the one Quest       */
+/* publishes (Tang et al., "Quest: Query-Aware Sparsity for Efficient          */
+/* Long-Context LLM Inference",                                                */
 /* ICML 2024, the criticality estimate of its method section): each page keeps */
 /* the element-wise minimum and maximum of its keys, and a query q scores the  */
 /* page by sum_d max(q_d * min_d, q_d * max_d), the largest value q . k can    */

@@ -1,6 +1,7 @@
 // Page-level selection, the baseline the pages compare AsyncSpade against
-// (research-map summary, "Problem" and "Baselines"; arXiv abstract: Quest,
-// which selects whole pages of the KV cache with the current query).  The page
+// (research-map summary, "Problem" and the baselines of "Experimental setup";
+// arXiv abstract: Quest, which selects whole pages of the KV cache with the
+// current query).  The page
 // score is Quest's published criticality estimate (Tang et al., ICML 2024,
 // method section): every page of P consecutive tokens keeps the element-wise
 // minimum and maximum of its keys, and a query q scores the page with

@@ -1,7 +1,8 @@
 """Parity of the page-level (Quest) selection against the CPU oracle (GPU required).
 
 The baseline the pages compare AsyncSpade with selects whole pages with the
-current query (research-map summary, "Problem" and "Baselines"); the page
+current query (research-map summary, "Problem" and the baselines of
+"Experimental setup"); the page
 score is Quest's published min/max bound.  Checks, on the bytes the GPU used:
   * page summaries: bit-exact (they are copies of key elements);
   * page scores: bit-exact on small-integer inputs, else within 1e-5 of the

@@ -1,6 +1,6 @@
 """Pins for the oracle's page-level selection, the baseline the pages compare
-against (research-map summary, "Problem" and "Baselines"; arXiv abstract:
-Quest's page-level selection with the current query).  The page score is the
+against (research-map summary, "Problem" and the baselines of "Experimental
+setup"; arXiv abstract: Quest's page-level selection with the current query).  The page score is the
 criticality estimate Quest publishes (Tang et al., ICML 2024, method section):
 each page keeps the element-wise min and max of its keys, and a query scores
 the page by the largest value its dot product can take over that box.
