@@ -15,6 +15,11 @@ layer, the Qwen3-32B layer or the ragged long-CoT batch; --top-c and --window
 override C and W); the roofline's measured traffic is then null, since the
 committed counter summary is of the Qwen3-8B layer.
 
+The timed loop is run twice over the same layers: issued from Python through
+the binding's prepared steps (one ctypes call per step; this gives `value`),
+then issued from C++ through the C ABI (bench_driver.cpp; "loops.cpp"), so
+that the host's issue cost can be told from the GPU's time.
+
 Beside the step, the page-level (Quest) baseline is timed on the same layers
 ("page_baseline"): page scoring with the current query, top C / P pages and
 attention over their tokens, all on one stream (--page-size, 0 skips it).
@@ -96,6 +101,25 @@ def measured_traffic(kernel_sources):
     if rec.get("source_sha256_16") != sources_hash(kernel_sources):
         return None
     return rec.get("bytes_per_launch")
+
+
+STEP_SOURCES = [os.path.join(ROOT, "query_aware_sparse_amd", "csrc", f)
+                for f in ("api.hip", "predict.hip", "score.hip", "score_block.h", "select.hip", "attend.hip",
+                          "attend_block.h", "asp_internal.h")]
+
+
+def in_step_score_launch_us():
+    """Average duration of the step's score launch inside the overlapped steps
+    of the default command, from the committed rocprofv3 kernel trace summary,
+    or None when the step's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "sparse_decode_step_qwen3-8b-layer_in_step.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256_16") != sources_hash(STEP_SOURCES):
+        return None
+    return rec.get("score_candidates_avg_us")
 
 
 def cpu_baseline(wl, layer, q_t) -> dict:
@@ -222,6 +246,8 @@ def main() -> int:
     ap.add_argument("--page-size", type=int, default=16,
                     help="page size of the page-level (Quest) baseline timed beside the step (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpp-driver", dest="cpp_driver", action="store_false",
+                    help="skip the second timing of the same loop issued from C++ (bench_driver.so)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (rocprofv3 counter calibration)")
     args = ap.parse_args()
@@ -230,11 +256,6 @@ def main() -> int:
               "(--gpus %d was requested)" % args.gpus, file=sys.stderr)
         return 2
 
-    # The pipelined step keeps four streams busy at once (attention, predictor,
-    # score pass, selection) beside the default stream; each needs a hardware
-    # queue of its own, or streams that share one run in submission order.
-    # HIP reads this at its first call (its default is 4 queues per process).
-    os.environ["GPU_MAX_HW_QUEUES"] = str(max(8, int(os.environ.get("GPU_MAX_HW_QUEUES", "4"))))
     import torch
     import query_aware_sparse_amd as A
     from query_aware_sparse_amd import workload as wk
@@ -263,7 +284,9 @@ def main() -> int:
     cfg = A.Cfg(wl.window, wl.top_c, wl.lam, wl.recent)
     B, Hq, Hkv, D, C = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.top_c
     L = args.kv_buffers
-    n_layer_steps = (args.warmup + args.steps) // L + 2
+    drivers = ["python"] + (["cpp"] if args.cpp_driver else [])
+    # each timing loop takes warmup + steps steps over the L layers in turn
+    n_layer_steps = len(drivers) * ((args.warmup + args.steps) // L + 2)
     attn = torch.cuda.Stream()
     sel = torch.cuda.Stream() if args.mode == "two_streams" else None
     # one step workspace per layer, as a decode loop over layers keeps them
@@ -271,7 +294,7 @@ def main() -> int:
                for _ in range(L)]
     ws_dec = torch.empty(A.asp_workspace_size(dims, cfg, A.OP_DECODE), dtype=torch.uint8, device=dev)
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
-    q_ready = A.HipEvent()
+    ctx = A.AspContext() if sel is not None else None
 
     t0 = time.perf_counter()
     layers = []
@@ -283,7 +306,7 @@ def main() -> int:
         lay = dict(k=k, v=v, seq_lens=lens, qs=qs, q_hist=q_hist, newest=newest, length=length,
                    idx=[torch.empty((B, Hkv, C), dtype=torch.int32, device=dev) for _ in range(2)],
                    nsel=[torch.empty((B, Hkv), dtype=torch.int32, device=dev) for _ in range(2)],
-                   ev=[A.HipEvent(), A.HipEvent()], cur=0, t=wl.history_steps)
+                   ev=[A.HipEvent(), A.HipEvent()], ws=ws_step[l], cur=0, t=wl.history_steps)
         for t in range(wl.history_steps - 1):
             A.asp_push_query(dims, cfg, qs[t], q_hist, newest, length)
         # bootstrap step: selection made from the ring, attended at once
@@ -293,40 +316,89 @@ def main() -> int:
     torch.cuda.synchronize()
     log("setup: %d KV caches of %.2f GiB (K+V) in %.1f s" % (L, 2 * k.numel() * 2 / 2**30, time.perf_counter() - t0))
 
-    def one_step(i):
-        lay = layers[i % L]
-        cur = lay["cur"]
-        nxt = 1 - cur
-        q = lay["qs"][lay["t"]]
-        A.asp_step(dims, cfg, q, lay["q_hist"], lay["newest"], lay["length"], lay["k"], lay["v"], lay["seq_lens"],
-                   lay["idx"][cur], lay["nsel"][cur], lay["idx"][nxt], lay["nsel"][nxt], out, ws_step[i % L],
-                   attn_stream=attn, sel_stream=sel, q_ready=q_ready, idx_cur_ready=lay["ev"][cur],
-                   idx_next_ready=lay["ev"][nxt])
-        lay["cur"] = nxt
-        lay["t"] += 1
+    def prepare(lay, n):
+        """The layer's next n steps (each with its own query and selection
+        buffer order), checked and marshalled ahead: a step is then one
+        ctypes call."""
+        steps = []
+        for j in range(n):
+            cur, t = (lay["cur"] + j) % 2, lay["t"] + j
+            steps.append(A.PreparedStep(dims, cfg, lay["qs"][t], lay["q_hist"], lay["newest"], lay["length"],
+                                        lay["k"], lay["v"], lay["seq_lens"], lay["idx"][cur], lay["nsel"][cur],
+                                        lay["idx"][1 - cur], lay["nsel"][1 - cur], out, lay["ws"], attn_stream=attn,
+                                        sel_stream=sel, ctx=ctx, idx_cur_ready=lay["ev"][cur],
+                                        idx_next_ready=lay["ev"][1 - cur]))
+        return steps
+
+    def time_python_loop():
+        per_layer = (args.warmup + args.steps + L - 1) // L
+        plan = [prepare(lay, per_layer) for lay in layers]
+        order = [plan[i % L][i // L] for i in range(args.warmup + args.steps)]
+        for i in range(args.warmup):
+            order[i]()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        ev0.record(attn)
+        for i in range(args.warmup, args.warmup + args.steps):
+            order[i]()
+        issued = time.perf_counter() - w0
+        if sel is not None:
+            attn.wait_stream(sel)
+        ev1.record(attn)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        for i in range(args.warmup + args.steps):  # the layers' state moves on
+            lay = layers[i % L]
+            lay["cur"], lay["t"] = 1 - lay["cur"], lay["t"] + 1
+        return ev0.elapsed_time(ev1), wall * 1e3, issued * 1e3
+
+    def time_cpp_loop():
+        import ctypes
+        drv = ctypes.CDLL(os.path.join(ROOT, "bench_driver.so"))
+        P = ctypes.c_void_p
+
+        class Layer(ctypes.Structure):
+            _fields_ = [("qs", P), ("q_hist", P), ("newest", P), ("len", P), ("k", P), ("v", P),
+                        ("seq_lens", P), ("idx", P * 2), ("nsel", P * 2), ("ev", P * 2), ("out", P), ("ws", P),
+                        ("ws_bytes", ctypes.c_size_t), ("cur", ctypes.c_int32), ("t", ctypes.c_int32)]
+
+        arr = (Layer * L)()
+        for i, lay in enumerate(layers):
+            arr[i] = Layer(lay["qs"].data_ptr(), lay["q_hist"].data_ptr(), lay["newest"].data_ptr(),
+                           lay["length"].data_ptr(), lay["k"].data_ptr(), lay["v"].data_ptr(),
+                           lay["seq_lens"].data_ptr(), (P * 2)(*[x.data_ptr() for x in lay["idx"]]),
+                           (P * 2)(*[x.data_ptr() for x in lay["nsel"]]),
+                           (P * 2)(*[e.handle.value for e in lay["ev"]]), out.data_ptr(), lay["ws"].data_ptr(),
+                           lay["ws"].numel(), lay["cur"], lay["t"])
+        times = (ctypes.c_double * 3)()
+        drv.bench_rotation.argtypes = [P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P]
+        drv.bench_rotation.restype = ctypes.c_int
+        rc = drv.bench_rotation(None if ctx is None else ctx.handle, ctypes.byref(dims), ctypes.byref(cfg), arr, L,
+                                args.warmup, args.steps, attn.cuda_stream, None if sel is None else sel.cuda_stream,
+                                times)
+        if rc != 0:
+            raise RuntimeError("bench_rotation failed: %d" % rc)
+        for i, lay in enumerate(layers):
+            lay["cur"], lay["t"] = arr[i].cur, arr[i].t
+        return times[0], times[1], times[2]
 
     attn.wait_stream(torch.cuda.current_stream())
-    for i in range(args.warmup):
-        one_step(i)
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    w0 = time.perf_counter()
-    ev0.record(attn)
-    for i in range(args.warmup, args.warmup + args.steps):
-        one_step(i)
-    issued = time.perf_counter() - w0
-    if sel is not None:
-        attn.wait_stream(sel)
-    ev1.record(attn)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    gpu_ms = ev0.elapsed_time(ev1)
-    ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
+    loops = {}
+    for name in drivers:
+        gpu_ms, wall_ms, issue_ms = (time_python_loop if name == "python" else time_cpp_loop)()
+        per = max(gpu_ms, wall_ms) / args.steps
+        loops[name] = {"ms_per_step": round(per, 5), "steps_per_s": round(1e3 / per, 2),
+                       "events_ms_per_step": round(gpu_ms / args.steps, 5),
+                       "wall_ms_per_step": round(wall_ms / args.steps, 5),
+                       "host_issue_ms_per_step": round(issue_ms / args.steps, 5),
+                       "host_issue_frac": round(issue_ms / max(gpu_ms, wall_ms), 3)}
+        log("%s loop, timed %d steps: %.4f ms/step (events %.4f, wall %.4f, host issue %.4f)"
+            % (name, args.steps, per, gpu_ms / args.steps, wall_ms / args.steps, issue_ms / args.steps))
+    ms_per_step = loops["python"]["ms_per_step"]
     steps_per_s = 1e3 / ms_per_step
     lens_list = [int(x) for x in layers[0]["seq_lens"].tolist()]
     nbytes = step_bytes(wl, lens_list)
-    log("timed %d steps: %.4f ms/step (events %.4f, wall %.4f, host issue %.4f)"
-        % (args.steps, ms_per_step, gpu_ms / args.steps, wall * 1e3 / args.steps, issued * 1e3 / args.steps))
 
     # Per-kernel timing: each entry point launched alone, back to back on one
     # stream, over the rotating KV caches, bracketed by events on that stream.
@@ -376,9 +448,14 @@ def main() -> int:
     sk_bytes = score_kernel_bytes(wl, lens_list)
     achieved = sk_bytes / (kern["score_us"] * 1e-6) / 1e9
     traffic = measured_traffic(SCORE_SOURCES) if headline else None
+    in_step = in_step_score_launch_us() if headline and args.mode == "two_streams" else None
     roofline = {"kernel": "score_candidates", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "algorithmic_bytes_per_launch": sk_bytes, "avg_launch_us": round(kern["score_us"], 2)}
+                "algorithmic_bytes_per_launch": sk_bytes, "avg_launch_us": round(kern["score_us"], 2),
+                # the same launch inside the overlapped steps, where the attention shares HBM with it
+                # (kernel trace of the default command, committed in profiles/; null when stale)
+                "in_step_avg_launch_us": in_step,
+                "in_step_frac": (round(sk_bytes / (in_step * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4) if in_step else None)}
     log("per-kernel us: %s" % json.dumps({k_: round(v_, 2) for k_, v_ in kern.items()}))
 
     page = None
@@ -396,7 +473,9 @@ def main() -> int:
     rec = {
         "metric": METRIC, "value": round(steps_per_s, 2), "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "arithmetic": "bf16 K/V; score: bf16 MFMA on hi+lo bf16 terms of the fp32 predicted query, fp32 "
+                      "accumulate; attention: fp32 softmax and accumulation; predictor: fp64 Gram and solve",
         "config": {"workload": wl.name, "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": D,
                    "context": wl.t_cap, "top_c": C, "window": wl.window, "recent": wl.recent, "kv_dtype": "bf16",
                    "kv_buffers": L, "mode": args.mode,
@@ -404,6 +483,9 @@ def main() -> int:
         "achieved_GBps": round(nbytes["score_select_attend"] * steps_per_s / 1e9, 1),
         "achieved_GBps_full_step": round(nbytes["full_step"] * steps_per_s / 1e9, 1),
         "bytes_per_step": nbytes,
+        # the same timed loop issued by the Python binding (value) and from C++ (bench_driver.cpp)
+        "loops": loops,
+        "hw_queues": os.environ.get("GPU_MAX_HW_QUEUES", "HIP default"),
         "kernels_us": {k_: round(v_, 2) for k_, v_ in kern.items()},
         "roofline": roofline,
         "page_baseline": page,

@@ -23,13 +23,13 @@
  *    must be 16-byte aligned, else ASP_ERR_WORKSPACE.
  *  - A "unit" is one (sequence b, KV head g); G = n_q_heads / n_kv_heads query
  *    heads h = g*G .. g*G+G-1 share KV head g.
- *  - The library allocates no device memory, keeps no data between calls and
+ *  - The library allocates no device memory, keeps no state of its own and
  *    never waits on the host: work is enqueued on the given stream(s) and the
- *    call returns.  The one piece of library state is the pair of streams and
- *    pair of events that asp_step creates per device on its first two-stream
- *    call (released by asp_release_streams).  Calls are re-entrant; two calls
- *    that write the same buffers (or share a workspace) must be ordered by the
- *    caller.
+ *    call returns.  The two-stream asp_step needs a caller-owned asp_context
+ *    (a stream and two events, made by asp_context_create and released by
+ *    asp_context_destroy).  Calls are re-entrant and may run concurrently
+ *    from several host threads; two calls that write the same buffers, share
+ *    a workspace or share a context must be ordered by the caller.
  *  - Every entry point except asp_step enqueues kernel launches only (no
  *    memset or copy node, no event), so a sequence of them can be captured
  *    into a HIP graph on one stream and replayed.
@@ -59,7 +59,8 @@ typedef enum {
   ASP_ERR_INVALID_ARG = 1, /* a dimension, config value or pointer is invalid */
   ASP_ERR_UNSUPPORTED = 2, /* valid in principle, not implemented (e.g. head_dim 96) */
   ASP_ERR_WORKSPACE = 3,   /* ws is NULL or ws_bytes < asp_workspace_size(...) */
-  ASP_ERR_HIP = 4          /* a HIP launch / event / stream call failed */
+  ASP_ERR_HIP = 4,         /* a HIP launch / event / stream call failed */
+  ASP_ERR_HOST_MEMORY = 5  /* a host allocation failed (asp_context_create) */
 } asp_status;
 
 typedef enum { ASP_KV_BF16 = 0, ASP_KV_F32 = 1 } asp_kv_dtype;
@@ -144,7 +145,12 @@ asp_status asp_predict_query(const asp_dims* dims, const asp_cfg* cfg, const flo
  * call overwrites with each unit's coarse histogram: bin j counts the scores
  * i < seq_lens[b] whose order key (the scores' monotone map to uint32 that
  * asp_select_topc ranks by) has j as its top 11 bits.  Passing it on to
- * asp_select_topc saves that call a pass over the scores. */
+ * asp_select_topc saves that call a pass over the scores.
+ * Keys must be finite.  For bf16 keys the fp32 predicted query enters the
+ * products as a pair of bf16 terms (hi + lo), so an infinite key element can
+ * give NaN (ranked as -inf) where the exact product is infinite; a non-finite
+ * key gives an unspecified score for its token (and an unspecified, still
+ * well-formed, selection downstream), never an access outside the arguments. */
 #define ASP_HIST_BINS 2048
 asp_status asp_score_keys(const asp_dims* dims, const float* q_pred, const void* k, const int32_t* seq_lens,
                           float* scores, uint32_t* hist, hipStream_t stream);
@@ -270,6 +276,36 @@ asp_status asp_page_select(const asp_dims* dims, const asp_cfg* cfg, int32_t pag
                            const void* kmin, const void* kmax, const int32_t* seq_lens, int32_t* idx,
                            int32_t* n_sel, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Caller-owned state of the two-stream asp_step ([abstract], second
+ * component; [summary] "Approach": selection runs beside the decoding loop):
+ * one HIP stream (default priority) on which the score passes of successive
+ * steps run back to back, and two events that order it with the caller's
+ * streams.
+ * asp_context_create makes one on `device` (0 <= device < the device count,
+ * else ASP_ERR_INVALID_ARG) and stores it in *ctx (NULL on failure).  flags:
+ * 0, or ASP_CTX_SCORE_ALL_CUS; other bits give ASP_ERR_INVALID_ARG.
+ *  - 0: the score stream leaves the last 32-CU group of the device (one XCD of
+ *    MI355X) to the latency-bound launches of the step (predictor, selection,
+ *    attention merge), which would otherwise wait for CU slots behind the
+ *    score blocks (a CU-masked stream; where the device has a single group or
+ *    the mask is refused, an unmasked one).  A CU-masked stream synchronises
+ *    with the legacy default stream.
+ *  - ASP_CTX_SCORE_ALL_CUS: the score stream may use every CU.
+ * A context serves one asp_step call at a time (calls that share it must be
+ * ordered by the caller, e.g. made from one host thread); different contexts
+ * are independent and may be used concurrently.  Its stream needs a hardware
+ * queue of its own beside the caller's two streams: HIP gives a process four
+ * unless GPU_MAX_HW_QUEUES says otherwise, and streams that share a queue run
+ * in submission order.
+ * asp_context_destroy waits for the context's stream to drain, then releases
+ * the stream and the events (NULL is a no-op); ASP_ERR_HIP if a HIP call
+ * failed (the rest is still released).  Returns ASP_ERR_HOST_MEMORY when the
+ * host allocation fails, ASP_ERR_HIP when a stream or event cannot be made. */
+typedef struct asp_context_s asp_context;
+#define ASP_CTX_SCORE_ALL_CUS 1u
+asp_status asp_context_create(int32_t device, uint32_t flags, asp_context** ctx);
+asp_status asp_context_destroy(asp_context* ctx);
+
 /* One decode step of one layer ([abstract], second component; [summary]
  * "Approach": selection for the next step is taken off the decode critical
  * path and overlapped with the current step's attention).
@@ -281,38 +317,26 @@ asp_status asp_page_select(const asp_dims* dims, const asp_cfg* cfg, int32_t pag
  * keys are scored and the next step's selection is written to
  * idx_next/n_sel_next.
  *  - sel_stream NULL or equal to attn_stream: everything runs in that order on
- *    attn_stream (attention first); q_ready and idx_cur_ready are ignored (may
- *    be NULL); idx_next_ready, when not NULL, is recorded when the selection
- *    is written.
- *  - otherwise (two streams): the step forks onto two streams of the library
- *    (created once per device, default priority, kept until
- *    asp_release_streams or the process ends) and joins back through events,
- *    so that the score passes of successive calls run back to back; the
- *    score stream is CU-masked to leave the last 32-CU group (one XCD) to
- *    the latency-bound launches, and as a CU-masked stream it synchronises
- *    with the legacy default stream:
- *      the library's predictor stream waits for attn_stream as it stands at
- *      entry (q_cur is ready in attn_stream's order) and for idx_cur_ready,
- *      then pushes q_cur into the ring and predicts (q_ready is recorded when
- *      that completes); the library's score stream waits for q_ready and
- *      scores; sel_stream waits for the scores, selects into
- *      idx_next/n_sel_next, advances the ring and records idx_next_ready (when
- *      not NULL); attn_stream waits for idx_cur_ready and runs the attention
- *      over idx_cur and its merge.
+ *    attn_stream (attention first); ctx and idx_cur_ready are ignored (may be
+ *    NULL); idx_next_ready, when not NULL, is recorded when the selection is
+ *    written.
+ *  - otherwise (two streams): ctx (a context made on the current device) and
+ *    idx_cur_ready are required, else ASP_ERR_INVALID_ARG.
+ *      attn_stream waits for idx_cur_ready, then pushes q_cur into the ring
+ *      and predicts the next query, then runs the attention over idx_cur and
+ *      its merge;
+ *      the context's stream waits for the prediction and scores the keys;
+ *      sel_stream waits for the scores, selects into idx_next/n_sel_next,
+ *      advances the ring and records idx_next_ready (when not NULL).
  *    idx_cur_ready is the event recorded when the selection idx_cur was
  *    written (the idx_next_ready of the step that made it, which must also be
  *    the last step that used this workspace: in a decode loop each layer keeps
- *    its own workspace, idx/n_sel buffer pair and event pair).  q_ready and
- *    idx_cur_ready must be valid events.  The caller swaps idx/n_sel buffers
- *    and events between the steps of a layer; the selection of step t writes
- *    the buffer that step t-1's attention read, and is ordered after it
- *    through attn_stream's state at entry.  When the call returns, `out` is
- *    complete in attn_stream's order; the selection and the ring are complete
- *    in sel_stream's order (idx_next_ready).  Calls from several host threads
- *    on one device are serialised inside the library.  The four streams
- *    (with the default stream, five) should each have a hardware queue: HIP
- *    gives a process 4 unless GPU_MAX_HW_QUEUES says otherwise, and streams
- *    that share a queue run in submission order.
+ *    its own workspace, idx/n_sel buffer pair and event pair).  The caller
+ *    swaps idx/n_sel buffers and events between the steps of a layer; the
+ *    selection of step t writes the buffer that step t-1's attention read,
+ *    and is ordered after it through attn_stream.  When the call returns,
+ *    `out` is complete in attn_stream's order; the selection and the ring
+ *    are complete in sel_stream's order (idx_next_ready).
  * asp_step returns ASP_ERR_UNSUPPORTED when attn_stream or sel_stream is being
  * captured into a graph.
  * Bootstrap mode (idx_cur == NULL): everything runs on attn_stream: push,
@@ -321,27 +345,18 @@ asp_status asp_page_select(const asp_dims* dims, const asp_cfg* cfg, int32_t pag
  * Every mode selects by the candidate route of asp_score_candidates and
  * asp_select_candidates, so the selection equals that of asp_score_keys with
  * asp_select_topc; results do not depend on the stream arrangement (the
- * kernels are deterministic).
+ * kernels are deterministic).  Keys must be finite, as for asp_score_keys.
  * Shapes as in the entry points above; ws/ws_bytes:
  * asp_workspace_size(ASP_OP_STEP) bytes, 16-byte aligned, used by all the
  * streams (disjoint regions), so it must not be shared with a concurrent step.
  * Its first 4*batch*n_kv_heads bytes are the per-unit threshold hints of the
  * candidate route, which each step updates for the next step of the layer. */
-asp_status asp_step(const asp_dims* dims, const asp_cfg* cfg, const float* q_cur, float* q_hist,
-                    int32_t* hist_newest, int32_t* hist_len, const void* k, const void* v,
+asp_status asp_step(asp_context* ctx, const asp_dims* dims, const asp_cfg* cfg, const float* q_cur,
+                    float* q_hist, int32_t* hist_newest, int32_t* hist_len, const void* k, const void* v,
                     const int32_t* seq_lens, const int32_t* idx_cur, const int32_t* n_sel_cur,
                     int32_t* idx_next, int32_t* n_sel_next, float* out, void* ws, size_t ws_bytes,
-                    hipStream_t attn_stream, hipStream_t sel_stream, hipEvent_t q_ready,
-                    hipEvent_t idx_cur_ready, hipEvent_t idx_next_ready);
-
-/* Waits for and destroys the streams and events that two-stream asp_step
- * calls created (on every device); the next such call creates them again.
- * Call it before the process ends, with no asp_step call in progress: it lets
- * the library's streams end before the HIP runtime is torn down, which some
- * tools that wrap the runtime (profilers) need.  The Python binding calls it
- * at interpreter exit.  Returns ASP_ERR_HIP if a HIP call failed (the
- * remaining streams and events are still released). */
-asp_status asp_release_streams(void);
+                    hipStream_t attn_stream, hipStream_t sel_stream, hipEvent_t idx_cur_ready,
+                    hipEvent_t idx_next_ready);
 
 #ifdef __cplusplus
 }

@@ -8,9 +8,9 @@ library is not built, every call raises ``AspError``.
 """
 from __future__ import annotations
 
-import atexit
 import ctypes
 import os
+import weakref
 from typing import Optional
 
 import torch
@@ -21,7 +21,7 @@ __all__ = [
     "KV_BF16", "KV_F32", "HIST_BINS",
     "asp_workspace_size", "asp_status_string", "asp_push_query", "asp_predict_query", "asp_score_keys",
     "asp_select_topc", "asp_score_candidates", "asp_select_candidates", "asp_sparse_decode", "asp_step",
-    "asp_selection_overlap", "asp_release_streams",
+    "asp_selection_overlap", "AspContext", "CTX_SCORE_ALL_CUS", "PreparedStep",
     "asp_page_summary_size", "asp_page_summary", "asp_page_scores", "asp_page_select_workspace_size",
     "asp_page_select", "page_count",
 ]
@@ -32,8 +32,9 @@ _LIB_PATH = os.path.join(_HERE, "libasp.so")
 OP_PUSH, OP_PREDICT, OP_SCORE, OP_SELECT, OP_DECODE, OP_STEP, OP_CANDIDATES = range(7)
 KV_BF16, KV_F32 = 0, 1
 HIST_BINS = 2048  # bins of the coarse score histograms (ASP_HIST_BINS)
+CTX_SCORE_ALL_CUS = 1  # asp_context_create flag: the score stream may use every CU
 _STATUS_NAMES = {0: "ASP_OK", 1: "ASP_ERR_INVALID_ARG", 2: "ASP_ERR_UNSUPPORTED", 3: "ASP_ERR_WORKSPACE",
-                 4: "ASP_ERR_HIP"}
+                 4: "ASP_ERR_HIP", 5: "ASP_ERR_HOST_MEMORY"}
 
 
 class AspError(RuntimeError):
@@ -87,9 +88,10 @@ def load():
     lib.asp_score_candidates.argtypes = [D, C, P, P, P, P, SZ, P]
     lib.asp_select_candidates.argtypes = [D, C, P, P, P, P, P, P, SZ, P]
     lib.asp_sparse_decode.argtypes = [D, C, P, P, P, P, P, P, P, P, SZ, P]
-    lib.asp_step.argtypes = [D, C, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P, P, P, P, P]
+    lib.asp_step.argtypes = [P, D, C, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P, P, P, P]
     lib.asp_selection_overlap.argtypes = [D, C, P, P, P, P, P, P]
-    lib.asp_release_streams.argtypes = []
+    lib.asp_context_create.argtypes = [ctypes.c_int32, ctypes.c_uint32, ctypes.POINTER(ctypes.c_void_p)]
+    lib.asp_context_destroy.argtypes = [P]
     I32 = ctypes.c_int32
     lib.asp_page_summary_size.argtypes = [D, I32]
     lib.asp_page_summary_size.restype = SZ
@@ -100,11 +102,9 @@ def load():
     lib.asp_page_select.argtypes = [D, C, I32, P, P, P, P, P, P, P, SZ, P]
     for name in ("asp_push_query", "asp_predict_query", "asp_score_keys", "asp_select_topc",
                  "asp_score_candidates", "asp_select_candidates", "asp_sparse_decode", "asp_step",
-                 "asp_selection_overlap", "asp_release_streams"):
+                 "asp_selection_overlap", "asp_context_create", "asp_context_destroy"):
         getattr(lib, name).restype = I32
     _lib = lib
-    # the library's streams end before the HIP runtime is torn down
-    atexit.register(lib.asp_release_streams)
     return lib
 
 
@@ -311,9 +311,36 @@ def asp_sparse_decode(dims: Dims, cfg: Cfg, q, k, v, seq_lens, idx, n_sel, out, 
                                                          _stream_handle(stream)))
 
 
-def asp_step(dims: Dims, cfg: Cfg, q_cur, q_hist, hist_newest, hist_len, k, v, seq_lens, idx_cur, n_sel_cur,
-             idx_next, n_sel_next, out, ws, attn_stream=None, sel_stream=None, q_ready: Optional[HipEvent] = None,
-             idx_cur_ready: Optional[HipEvent] = None, idx_next_ready: Optional[HipEvent] = None) -> None:
+class AspContext:
+    """asp_context: the stream and events of two-stream asp_step calls, owned
+    by this object (asp_context_create / asp_context_destroy).
+
+    device: the CUDA/HIP device index (default: the current device).  flags: 0
+    (the score stream leaves the last 32-CU group to the step's latency-bound
+    launches) or CTX_SCORE_ALL_CUS.  One context serves one asp_step call at a
+    time; use one per host thread.  close() (or the end of the process)
+    releases it.
+    """
+
+    def __init__(self, device: Optional[int] = None, flags: int = 0):
+        lib = load()
+        dev = torch.cuda.current_device() if device is None else int(device)
+        h = ctypes.c_void_p()
+        _raise("asp_context_create", lib.asp_context_create(dev, int(flags), ctypes.byref(h)))
+        self.handle = h
+        self.device = dev
+        # released before the HIP runtime is torn down at interpreter exit
+        self._finalizer = weakref.finalize(self, lib.asp_context_destroy, h)
+
+    def close(self) -> None:
+        """Wait for the context's stream and release it (idempotent)."""
+        if self._finalizer.alive:
+            status = self._finalizer()
+            _raise("asp_context_destroy", status)
+
+
+def _step_args(ctx, dims, cfg, q_cur, q_hist, hist_newest, hist_len, k, v, seq_lens, idx_cur, n_sel_cur, idx_next,
+               n_sel_next, out, ws, attn_stream, sel_stream, idx_cur_ready, idx_next_ready):
     B, Hq, Hkv, D, T = dims.batch, dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.t_cap
     W, C = cfg.window, cfg.top_c
     _check(q_cur, "q_cur", (B, Hq, D), torch.float32)
@@ -329,13 +356,51 @@ def asp_step(dims: Dims, cfg: Cfg, q_cur, q_hist, hist_newest, hist_len, k, v, s
     _check(idx_next, "idx_next", (B, Hkv, C), torch.int32)
     _check(n_sel_next, "n_sel_next", (B, Hkv), torch.int32)
     _check(out, "out", (B, Hq, D), torch.float32)
+    if ctx is not None and not isinstance(ctx, AspContext):
+        raise AspError("ctx must be an AspContext or None")
     wp, wb = _ws(ws)
     attn = _stream_handle(attn_stream)
     sel = None if sel_stream is None else _stream_handle(sel_stream)
-    _raise("asp_step", load().asp_step(ctypes.byref(dims), ctypes.byref(cfg), _ptr(q_cur), _ptr(q_hist),
-                                       _ptr(hist_newest), _ptr(hist_len), _ptr(k), _ptr(v), _ptr(seq_lens),
-                                       _ptr(idx_cur), _ptr(n_sel_cur), _ptr(idx_next), _ptr(n_sel_next), _ptr(out),
-                                       wp, wb, attn, sel, _ev(q_ready), _ev(idx_cur_ready), _ev(idx_next_ready)))
+    return (None if ctx is None else ctx.handle, ctypes.byref(dims), ctypes.byref(cfg), _ptr(q_cur), _ptr(q_hist),
+            _ptr(hist_newest), _ptr(hist_len), _ptr(k), _ptr(v), _ptr(seq_lens), _ptr(idx_cur), _ptr(n_sel_cur),
+            _ptr(idx_next), _ptr(n_sel_next), _ptr(out), wp, wb, attn, sel, _ev(idx_cur_ready), _ev(idx_next_ready))
+
+
+def asp_step(dims: Dims, cfg: Cfg, q_cur, q_hist, hist_newest, hist_len, k, v, seq_lens, idx_cur, n_sel_cur,
+             idx_next, n_sel_next, out, ws, attn_stream=None, sel_stream=None, ctx: Optional[AspContext] = None,
+             idx_cur_ready: Optional[HipEvent] = None, idx_next_ready: Optional[HipEvent] = None) -> None:
+    """One decode step of one layer (include/asp.h).  Two distinct streams need
+    ctx (an AspContext on the current device) and idx_cur_ready."""
+    args = _step_args(ctx, dims, cfg, q_cur, q_hist, hist_newest, hist_len, k, v, seq_lens, idx_cur, n_sel_cur,
+                      idx_next, n_sel_next, out, ws, attn_stream, sel_stream, idx_cur_ready, idx_next_ready)
+    _raise("asp_step", load().asp_step(*args))
+
+
+class PreparedStep:
+    """asp_step with its arguments checked and marshalled once, for a decode
+    loop that calls the same step (same tensors, streams and events) again and
+    again: calling the object makes the C call with the stored arguments.
+
+    The tensors, streams, events and context are referenced until the object is
+    dropped.  Their contents may change between calls (a new query written
+    into q_cur, for instance); their storage must not.
+    """
+
+    def __init__(self, dims: Dims, cfg: Cfg, q_cur, q_hist, hist_newest, hist_len, k, v, seq_lens, idx_cur,
+                 n_sel_cur, idx_next, n_sel_next, out, ws, attn_stream=None, sel_stream=None,
+                 ctx: Optional[AspContext] = None, idx_cur_ready: Optional[HipEvent] = None,
+                 idx_next_ready: Optional[HipEvent] = None):
+        self._keep = (dims, cfg, q_cur, q_hist, hist_newest, hist_len, k, v, seq_lens, idx_cur, n_sel_cur,
+                      idx_next, n_sel_next, out, ws, attn_stream, sel_stream, ctx, idx_cur_ready, idx_next_ready)
+        self._args = _step_args(ctx, dims, cfg, q_cur, q_hist, hist_newest, hist_len, k, v, seq_lens, idx_cur,
+                                n_sel_cur, idx_next, n_sel_next, out, ws, attn_stream, sel_stream, idx_cur_ready,
+                                idx_next_ready)
+        self._fn = load().asp_step
+
+    def __call__(self) -> None:
+        status = self._fn(*self._args)
+        if status != 0:
+            _raise("asp_step", status)
 
 
 def page_count(t_cap: int, page_size: int) -> int:
@@ -396,9 +461,3 @@ def asp_page_select(dims: Dims, cfg: Cfg, page_size: int, q, kmin, kmax, seq_len
     _raise("asp_page_select", load().asp_page_select(ctypes.byref(dims), ctypes.byref(cfg), int(page_size), _ptr(q),
                                                      _ptr(kmin), _ptr(kmax), _ptr(seq_lens), _ptr(idx), _ptr(n_sel),
                                                      wp, wb, _stream_handle(stream)))
-
-
-def asp_release_streams() -> None:
-    """Wait for and destroy the library's streams of two-stream asp_step calls
-    (they are created again by the next such call).  Also runs at exit."""
-    _raise("asp_release_streams", load().asp_release_streams())

@@ -72,6 +72,26 @@ def build_c_abi_check() -> list:
     return built
 
 
+BENCH_DRIVER = os.path.join(ROOT, "bench_driver")
+
+
+def build_bench_driver() -> str:
+    """bench_driver.so, the C++ timing loop bench.py calls through ctypes; it
+    finds libasp.so through a path relative to itself."""
+    out = BENCH_DRIVER + ".so"
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "--offload-arch=" + ARCH, "-O2", "-std=c++17", "-Wall", "-fPIC", "-shared",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I" + os.path.join(ROOT, "include"), BENCH_DRIVER + ".cpp", "-L" + PKG, "-lasp",
+           "-Wl,-rpath,$ORIGIN/query_aware_sparse_amd", "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for the bench driver:\n%s\n%s" % (" ".join(cmd), r.stderr))
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     print(build_library())
     print(build_c_abi_check())
+    print(build_bench_driver())

@@ -3,7 +3,7 @@
 // entry point.
 #include <math.h>
 
-#include <mutex>
+#include <new>
 
 #include "../../include/asp.h"
 #include "asp_internal.h"
@@ -106,33 +106,32 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
     if ((expr) != hipSuccess) return ASP_ERR_HIP;  \
   } while (0)
 
-// The two streams the pipelined step forks its predictor and its score pass
-// onto, with the events that join them: `in` marks the caller's attention
-// stream at entry (q_cur ready), `scored` the end of the score pass.  One set
-// per device, created on first use (default priority; the score stream has a
-// CU mask, see create_score_stream) and kept until the process ends.  The events are re-recorded by every step; each
-// wait takes the record made just before it, under fork_mu.
-struct StepFork {
-  hipStream_t pred = nullptr, score = nullptr;
-  hipEvent_t in = nullptr, scored = nullptr;
+}  // namespace
+
+// Caller-owned state of the two-stream asp_step: the stream that runs the
+// score passes and the two events that order the step's streams.  Created by
+// asp_context_create on one device, used by one asp_step call at a time, and
+// released by asp_context_destroy; the library keeps nothing else.
+struct asp_context_s {
+  int device;
+  uint32_t flags;
+  hipStream_t score;    // score passes of successive calls run back to back here
+  hipEvent_t pred;      // recorded by the predictor launch (q_pred and the ring slot written)
+  hipEvent_t scored;    // recorded by the score launch (candidates kept)
 };
-constexpr int kMaxDevices = 64;
-StepFork g_fork[kMaxDevices];
-std::mutex g_fork_mu;
+
+namespace {
 
 // The score stream's CU mask: every CU but those of the last 32-CU group.  On
 // MI355X (256 CUs) the mask words map to the eight XCDs, so the score passes
 // run on seven XCDs and leave the eighth to the latency-bound launches
 // (predictor, select, merge), which otherwise wait for CU slots behind score
-// blocks.  Measured at the Qwen3-8B layer shape: 107.7 us per step against
-// 111.1 us unmasked; masks that split an XCD (216, 232, 240 CUs) are slower
-// than either, since the score grid is spread evenly over the XCDs it may use.
-// Falls back to an unmasked stream where the device has one group or the mask
-// is refused.
-hipError_t create_score_stream(int dev, hipStream_t* st) {
+// blocks.  Falls back to an unmasked stream where the device has one group or
+// the mask is refused.
+hipError_t create_score_stream(int dev, bool masked, hipStream_t* st) {
   int ncu = 0;
-  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && ncu % 32 == 0 &&
-      ncu / 32 >= 2 && ncu / 32 <= 32) {
+  if (masked && hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      ncu % 32 == 0 && ncu / 32 >= 2 && ncu / 32 <= 32) {
     uint32_t mask[32] = {};
     const int words = ncu / 32;
     for (int w = 0; w + 1 < words; ++w) mask[w] = 0xffffffffu;
@@ -142,30 +141,15 @@ hipError_t create_score_stream(int dev, hipStream_t* st) {
   return hipStreamCreateWithFlags(st, hipStreamNonBlocking);
 }
 
-// Called with g_fork_mu held.
-hipError_t step_fork(StepFork** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  StepFork& f = g_fork[dev];
-  if (f.scored == nullptr) {  // all four are created together, or none is kept
-    const unsigned ev_flags = hipEventDisableTiming | hipEventDisableSystemFence;
-    StepFork n;
-    if ((e = hipStreamCreateWithFlags(&n.pred, hipStreamNonBlocking)) == hipSuccess &&
-        (e = create_score_stream(dev, &n.score)) == hipSuccess &&
-        (e = hipEventCreateWithFlags(&n.in, ev_flags)) == hipSuccess &&
-        (e = hipEventCreateWithFlags(&n.scored, ev_flags)) == hipSuccess) {
-      f = n;
-    } else {
-      if (n.pred) (void)hipStreamDestroy(n.pred);
-      if (n.score) (void)hipStreamDestroy(n.score);
-      if (n.in) (void)hipEventDestroy(n.in);
-      return e;
-    }
+// Releases what a context holds (any member may be null).
+void context_release(asp_context* c) {
+  if (c->score) {
+    (void)hipStreamSynchronize(c->score);
+    (void)hipStreamDestroy(c->score);
   }
-  *out = &f;
-  return hipSuccess;
+  if (c->pred) (void)hipEventDestroy(c->pred);
+  if (c->scored) (void)hipEventDestroy(c->scored);
+  delete c;
 }
 
 // Selection work of one step on one stream: the predictor pushes q_cur into
@@ -204,6 +188,7 @@ const char* asp_status_string(asp_status status) {
     case ASP_ERR_UNSUPPORTED: return "unsupported shape (head_dim must be 64 or 128, GQA group 1, 2, 4 or 8)";
     case ASP_ERR_WORKSPACE: return "workspace missing or smaller than asp_workspace_size()";
     case ASP_ERR_HIP: return "a HIP kernel launch, event or stream call failed";
+    case ASP_ERR_HOST_MEMORY: return "host memory allocation failed";
   }
   return "unknown status";
 }
@@ -360,12 +345,45 @@ asp_status asp_page_select(const asp_dims* dims, const asp_cfg* cfg, int32_t pag
   return hip_status(asp::launch_page_select(s, page_size, q, kmin, kmax, seq_lens, idx, n_sel, ws, stream));
 }
 
-asp_status asp_step(const asp_dims* dims, const asp_cfg* cfg, const float* q_cur, float* q_hist,
+asp_status asp_context_create(int32_t device, uint32_t flags, asp_context** ctx) {
+  if (ctx == nullptr) return ASP_ERR_INVALID_ARG;
+  *ctx = nullptr;
+  if ((flags & ~(uint32_t)ASP_CTX_SCORE_ALL_CUS) != 0) return ASP_ERR_INVALID_ARG;
+  int n = 0, cur = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || hipGetDevice(&cur) != hipSuccess) return ASP_ERR_HIP;
+  if (device < 0 || device >= n) return ASP_ERR_INVALID_ARG;
+  asp_context* c = new (std::nothrow) asp_context{device, flags, nullptr, nullptr, nullptr};
+  if (c == nullptr) return ASP_ERR_HOST_MEMORY;
+  hipError_t e = cur == device ? hipSuccess : hipSetDevice(device);
+  if (e == hipSuccess) e = create_score_stream(device, (flags & ASP_CTX_SCORE_ALL_CUS) == 0, &c->score);
+  const unsigned ev_flags = hipEventDisableTiming | hipEventDisableSystemFence;
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->pred, ev_flags);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->scored, ev_flags);
+  if (cur != device) (void)hipSetDevice(cur);
+  if (e != hipSuccess) {
+    context_release(c);
+    return ASP_ERR_HIP;
+  }
+  *ctx = c;
+  return ASP_OK;
+}
+
+asp_status asp_context_destroy(asp_context* ctx) {
+  if (ctx == nullptr) return ASP_OK;
+  bool ok = hipStreamSynchronize(ctx->score) == hipSuccess;
+  ok &= hipStreamDestroy(ctx->score) == hipSuccess;
+  ok &= hipEventDestroy(ctx->pred) == hipSuccess;
+  ok &= hipEventDestroy(ctx->scored) == hipSuccess;
+  delete ctx;
+  return ok ? ASP_OK : ASP_ERR_HIP;
+}
+
+asp_status asp_step(asp_context* ctx, const asp_dims* dims, const asp_cfg* cfg, const float* q_cur, float* q_hist,
                     int32_t* hist_newest, int32_t* hist_len, const void* k, const void* v,
                     const int32_t* seq_lens, const int32_t* idx_cur, const int32_t* n_sel_cur,
                     int32_t* idx_next, int32_t* n_sel_next, float* out, void* ws, size_t ws_bytes,
-                    hipStream_t attn_stream, hipStream_t sel_stream, hipEvent_t q_ready,
-                    hipEvent_t idx_cur_ready, hipEvent_t idx_next_ready) {
+                    hipStream_t attn_stream, hipStream_t sel_stream, hipEvent_t idx_cur_ready,
+                    hipEvent_t idx_next_ready) {
   Shape s;
   asp_status st = check_all(dims, cfg, &s);
   if (st != ASP_OK) return st;
@@ -377,9 +395,14 @@ asp_status asp_step(const asp_dims* dims, const asp_cfg* cfg, const float* q_cur
   if (!aligned16(ws)) return ASP_ERR_WORKSPACE;
   const bool pipelined = idx_cur != nullptr;
   const bool two_streams = pipelined && sel_stream != nullptr && sel_stream != attn_stream;
-  if (two_streams && (q_ready == nullptr || idx_cur_ready == nullptr)) return ASP_ERR_INVALID_ARG;
-  // The step records events on its launches and forks onto the library's
-  // streams; recording it into a graph is not supported.
+  if (two_streams) {
+    if (ctx == nullptr || idx_cur_ready == nullptr) return ASP_ERR_INVALID_ARG;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return ASP_ERR_HIP;
+    if (dev != ctx->device) return ASP_ERR_INVALID_ARG;  // the context's stream is on another device
+  }
+  // The step records events on its launches and forks onto the context's
+  // stream; recording it into a graph is not supported.
   if (asp::capturing(attn_stream) || (sel_stream != nullptr && asp::capturing(sel_stream)))
     return ASP_ERR_UNSUPPORTED;
   const StepLayout lay = step_layout(s);
@@ -405,64 +428,30 @@ asp_status asp_step(const asp_dims* dims, const asp_cfg* cfg, const float* q_cur
     return run_selection(s, q_cur, q_hist, hist_newest, hist_len, k, seq_lens, idx_next, n_sel_next, q_pred, cw,
                          attn_stream, idx_next_ready);
   }
-  // Two streams, forked four ways so that the score passes of successive
-  // calls run back to back while the latency-bound launches overlap them:
-  //  - the fork's predictor stream waits for attn_stream as it stands at entry
-  //    (q_cur ready, and with it the attention that produced q_cur in a decode
-  //    loop) and for idx_cur_ready (the previous selection made with this
-  //    workspace has finished with the candidates, the hints and the ring),
-  //    then pushes and predicts; the launch records q_ready;
-  //  - the fork's score stream waits for q_ready and scores; the launch records
-  //    the fork's `scored` event;
+  // Two streams of the caller and the context's score stream:
+  //  - attn_stream waits for idx_cur_ready (the selection it attends over is
+  //    written, and the previous selection made with this workspace has
+  //    finished with the candidates, the hints and the ring), then the
+  //    predictor pushes q_cur into the ring and predicts (its launch records
+  //    the context's `pred` event), then the attention over idx_cur and its
+  //    merge run;
+  //  - the score stream waits for `pred` and scores (the launch records
+  //    `scored`);
   //  - sel_stream waits for `scored` and selects (its first launch advances
-  //    the ring); the last launch records idx_next_ready;
-  //  - attn_stream waits for idx_cur_ready and runs the attention and merge.
-  // The predictor waits for idx_cur_ready itself rather than through
-  // attn_stream: a chain of two cross-stream waits costs a step ~3 us more.
-  // Events recorded by a launch itself cost no extra queue packet.
-  std::lock_guard<std::mutex> lock(g_fork_mu);
-  StepFork* f = nullptr;
-  ASP_TRY_HIP(step_fork(&f));
-  ASP_TRY_HIP(hipEventRecord(f->in, attn_stream));
-  ASP_TRY_HIP(hipStreamWaitEvent(f->pred, f->in, 0));
-  ASP_TRY_HIP(hipStreamWaitEvent(f->pred, idx_cur_ready, 0));
-  ASP_TRY_HIP(asp::launch_predict(s, q_hist, hist_newest, hist_len, q_cur, q_pred, f->pred, q_ready));
-  ASP_TRY_HIP(hipStreamWaitEvent(f->score, q_ready, 0));
-  ASP_TRY_HIP(asp::launch_score_candidates(s, q_pred, k, seq_lens, cw, false, f->score, f->scored));
-  ASP_TRY_HIP(hipStreamWaitEvent(sel_stream, f->scored, 0));
+  //    the ring); the last launch records idx_next_ready.
+  // Events recorded by a launch itself cost no extra queue packet.  A wait on
+  // an event that has not completed costs the host ~14 us, so the step makes
+  // two (pred, scored); idx_cur_ready has usually completed by the time the
+  // layer's next step is issued.
+  ASP_TRY_HIP(hipStreamWaitEvent(attn_stream, idx_cur_ready, 0));
+  ASP_TRY_HIP(asp::launch_predict(s, q_hist, hist_newest, hist_len, q_cur, q_pred, attn_stream, ctx->pred));
+  ASP_TRY_HIP(hipStreamWaitEvent(ctx->score, ctx->pred, 0));
+  ASP_TRY_HIP(asp::launch_score_candidates(s, q_pred, k, seq_lens, cw, false, ctx->score, ctx->scored));
+  ASP_TRY_HIP(hipStreamWaitEvent(sel_stream, ctx->scored, 0));
   ASP_TRY_HIP(asp::launch_select_candidates(s, q_pred, k, seq_lens, cw, idx_next, n_sel_next, hist_newest, hist_len,
                                             sel_stream, idx_next_ready));
-  ASP_TRY_HIP(hipStreamWaitEvent(attn_stream, idx_cur_ready, 0));
   ASP_TRY_HIP(asp::launch_attend(s, q_cur, k, v, seq_lens, idx_cur, n_sel_cur, out, partials, attn_stream));
   return ASP_OK;
-}
-
-asp_status asp_release_streams(void) {
-  std::lock_guard<std::mutex> lock(g_fork_mu);
-  bool any = false;
-  for (const StepFork& f : g_fork) any |= f.scored != nullptr;
-  if (!any) return ASP_OK;  // nothing was created (no HIP call is made)
-  int cur = 0;
-  const bool have_cur = hipGetDevice(&cur) == hipSuccess;
-  bool ok = true;
-  for (int dev = 0; dev < kMaxDevices; ++dev) {
-    StepFork& f = g_fork[dev];
-    if (f.scored == nullptr) continue;
-    ok &= hipSetDevice(dev) == hipSuccess;
-    for (hipStream_t* st : {&f.pred, &f.score}) {
-      if (*st == nullptr) continue;
-      ok &= hipStreamSynchronize(*st) == hipSuccess;
-      ok &= hipStreamDestroy(*st) == hipSuccess;
-      *st = nullptr;
-    }
-    for (hipEvent_t* ev : {&f.in, &f.scored}) {
-      if (*ev == nullptr) continue;
-      ok &= hipEventDestroy(*ev) == hipSuccess;
-      *ev = nullptr;
-    }
-  }
-  if (have_cur) ok &= hipSetDevice(cur) == hipSuccess;
-  return ok ? ASP_OK : ASP_ERR_HIP;
 }
 
 }  // extern "C"

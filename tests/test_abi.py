@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "asp_workspace_size", "asp_status_string", "asp_push_query", "asp_predict_query", "asp_score_keys",
         "asp_select_topc", "asp_score_candidates", "asp_select_candidates", "asp_sparse_decode", "asp_step",
-        "asp_selection_overlap", "asp_release_streams", "asp_page_summary_size", "asp_page_summary",
+        "asp_selection_overlap", "asp_context_create", "asp_context_destroy", "asp_page_summary_size",
+        "asp_page_summary",
         "asp_page_scores", "asp_page_select_workspace_size", "asp_page_select"])
 
 
@@ -40,13 +41,18 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(raw, name), name
 
 
-def test_release_streams_without_any_is_a_no_op(lib):
-    # no two-stream step has run in this process: nothing to release, no HIP call
-    A.asp_release_streams()
+def test_context_argument_checks(lib):
+    # rejected on the host before any HIP call; destroying NULL is a no-op
+    h = ctypes.c_void_p(1234)
+    assert lib.asp_context_create(0, 0, None) == 1
+    assert lib.asp_context_create(0, 2, ctypes.byref(h)) == 1  # unknown flag bit
+    assert h.value is None  # *ctx is cleared on failure
+    assert lib.asp_context_create(0, 0x80000000, ctypes.byref(h)) == 1
+    assert lib.asp_context_destroy(None) == 0
 
 
 def test_status_strings(lib):
-    for code in range(5):
+    for code in range(6):
         assert A.asp_status_string(code)
     assert A.asp_status_string(77) == "unknown status"
 
@@ -158,15 +164,18 @@ def test_null_pointers_and_short_workspace_rejected(lib):
                                     ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(256), need_c, None) == 1
     one = ctypes.c_void_p(16)
     # asp_step: idx_cur without n_sel_cur; missing workspace
-    args = [ctypes.byref(d), ctypes.byref(c)] + [one] * 7  # q_cur .. seq_lens
+    args = [None, ctypes.byref(d), ctypes.byref(c)] + [one] * 7  # ctx, dims, cfg, q_cur .. seq_lens
     #                   idx_cur n_sel_cur idx_nx nsel_nx out  ws    ws_bytes  attn  sel   events
-    assert lib.asp_step(*args, one, None, one, one, one, one, 1 << 40, None, None, None, None, None) == 1
-    assert lib.asp_step(*args, None, None, one, one, one, None, 0, None, None, None, None, None) == 3
-    # two distinct streams need a q_ready event and an idx_cur_ready event
+    assert lib.asp_step(*args, one, None, one, one, one, one, 1 << 40, None, None, None, None) == 1
+    assert lib.asp_step(*args, None, None, one, one, one, None, 0, None, None, None, None) == 3
+    # two distinct streams need a context and an idx_cur_ready event
     assert lib.asp_step(*args, one, one, one, one, one, one, 1 << 40, ctypes.c_void_p(1), ctypes.c_void_p(2),
-                        None, None, None) == 1
+                        None, None) == 1
     assert lib.asp_step(*args, one, one, one, one, one, one, 1 << 40, ctypes.c_void_p(1), ctypes.c_void_p(2),
-                        ctypes.c_void_p(3), None, None) == 1
+                        ctypes.c_void_p(3), None) == 1
+    args[0] = ctypes.c_void_p(64)  # a context (never dereferenced before the event check)
+    assert lib.asp_step(*args, one, one, one, one, one, one, 1 << 40, ctypes.c_void_p(1), ctypes.c_void_p(2),
+                        None, None) == 1
 
 
 def test_page_sizes_and_argument_checks(lib):

@@ -65,7 +65,7 @@ def _full_shape_check(p: Problem, units):
     idx = [torch.full((B, Hkv, C), -7, dtype=torch.int32, device=DEV) for _ in range(2)]
     nsel = [torch.zeros((B, Hkv), dtype=torch.int32, device=DEV) for _ in range(2)]
     ev = [A.HipEvent(), A.HipEvent()]
-    q_ready = A.HipEvent()
+    ctx = A.AspContext()
     attn, sel = torch.cuda.Stream(), torch.cuda.Stream()
     attn.wait_stream(torch.cuda.current_stream())
     q0d, q1d = q0.to(DEV), q1.to(DEV)  # held until the streams are done with them
@@ -76,7 +76,7 @@ def _full_shape_check(p: Problem, units):
     got0 = _snap(p, idx[0], nsel[0])
     assert np.array_equal(np_(p.q_hist), np_(ring1[0]))
     A.asp_step(d, c, q1d, p.q_hist, p.newest, p.length, p.k, p.v, p.seq_lens, idx[0], nsel[0], idx[1],
-               nsel[1], p.out, ws, attn_stream=attn, sel_stream=sel, q_ready=q_ready, idx_cur_ready=ev[0],
+               nsel[1], p.out, ws, attn_stream=attn, sel_stream=sel, ctx=ctx, idx_cur_ready=ev[0],
                idx_next_ready=ev[1])
     torch.cuda.synchronize()
     got1 = _snap(p, idx[1], nsel[1])

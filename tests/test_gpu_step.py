@@ -6,9 +6,10 @@
   computed from the GPU's prediction, selection bit-exact on the GPU's fp32
   scores and within the 1e-5 * max|score| boundary gap of the oracle's own fp64
   selection, attention within 1e-2 on the GPU's selection.
-* asp_step (bootstrap, pipelined on one stream, pipelined on two streams, also
-  with the library's streams released and created again mid-run) is
-  bit-identical to the same schedule built from the individual entry points.
+* asp_step (bootstrap, pipelined on one stream, pipelined on two streams with
+  a context, also with the context destroyed and a new one made mid-run, and
+  with a context whose score stream may use every CU) is bit-identical to the
+  same schedule built from the individual entry points.
 """
 import numpy as np
 import pytest
@@ -129,18 +130,19 @@ def test_qwen3_8b_layer_full_shape_staged():
     _staged_check(p, p.queries[wl.history_steps])
 
 
-def _step_run(p: Problem, mode: str, n_steps: int, release_after=None, hints=None):
+def _step_run(p: Problem, mode: str, n_steps: int, release_after=None, hints=None, ctx_flags=0):
     """Run n_steps decode steps with asp_step in `mode`; return per-step outputs.
-    release_after: step after which the library's streams are released (the
-    next two-stream step creates them again).  hints: {step: value} written
-    over the workspace's per-unit threshold hints after that step."""
+    release_after: step after which the context is destroyed and a new one
+    made for the next two-stream step.  hints: {step: value} written over the
+    workspace's per-unit threshold hints after that step.  ctx_flags: flags of
+    the contexts made."""
     wl, d, c = p.wl, p.dims, p.cfg
     B, Hkv, C = wl.batch, wl.n_kv_heads, wl.top_c
     ws = torch.empty(A.asp_workspace_size(d, c, A.OP_STEP), dtype=torch.uint8, device=DEV)
     idx = [torch.full((B, Hkv, C), -5, dtype=torch.int32, device=DEV) for _ in range(2)]
     nsel = [torch.zeros((B, Hkv), dtype=torch.int32, device=DEV) for _ in range(2)]
     ev = [A.HipEvent(), A.HipEvent()]
-    q_ready = A.HipEvent()
+    ctx = A.AspContext(flags=ctx_flags) if mode == "two_streams" else None
     attn = torch.cuda.Stream()
     sel = torch.cuda.Stream() if mode == "two_streams" else None
     results = []
@@ -155,13 +157,14 @@ def _step_run(p: Problem, mode: str, n_steps: int, release_after=None, hints=Non
                            nsel[nxt], p.out, ws, attn_stream=attn, idx_next_ready=ev[nxt])
             else:
                 A.asp_step(d, c, q, p.q_hist, p.newest, p.length, p.k, p.v, p.seq_lens, idx[cur], nsel[cur],
-                           idx[nxt], nsel[nxt], p.out, ws, attn_stream=attn, sel_stream=sel, q_ready=q_ready,
+                           idx[nxt], nsel[nxt], p.out, ws, attn_stream=attn, sel_stream=sel, ctx=ctx,
                            idx_cur_ready=ev[cur], idx_next_ready=ev[nxt])
         torch.cuda.synchronize()
         results.append((np_(p.out).copy(), np_(idx[nxt]).copy(), np_(nsel[nxt]).copy(), np_(p.q_hist).copy(),
                         np_(p.newest).copy(), np_(p.length).copy()))
-        if s == release_after:
-            A.asp_release_streams()
+        if s == release_after and ctx is not None:
+            ctx.close()
+            ctx = A.AspContext(flags=ctx_flags)
         if hints and s in hints:
             ws[:4 * B * Hkv].view(torch.int32).fill_(hints[s])
             torch.cuda.synchronize()
@@ -218,15 +221,18 @@ def test_step_modes_bit_identical_to_entry_points(wl_name):
     wl = wk.CONFIGS.get(wl_name) or SMALL_STEP_CASES[wl_name]
     n = 5
     runs = {}
-    modes = ("one_stream", "two_streams", "two_streams_release", "two_streams_hints", "one_stream_hints")
+    modes = ("one_stream", "two_streams", "two_streams_release", "two_streams_all_cus", "two_streams_hints",
+             "one_stream_hints")
     for mode in ("manual",) + modes:
         p = Problem(wl, kv_device=DEV if wl.batch > 1 else "cpu", n_steps=n, lens=STEP_LENS.get(wl_name))
         p.fill_history()
         torch.cuda.synchronize()
         if mode == "manual":
             runs[mode] = _manual_run(p, n)
-        elif mode == "two_streams_release":  # the library's streams released mid-run and created again
+        elif mode == "two_streams_release":  # the context destroyed mid-run and a new one made
             runs[mode] = _step_run(p, "two_streams", n, release_after=2)
+        elif mode == "two_streams_all_cus":  # a score stream without a CU mask
+            runs[mode] = _step_run(p, "two_streams", n, ctx_flags=A.CTX_SCORE_ALL_CUS)
         elif mode.endswith("_hints"):  # hints that keep nothing (every unit rescored), then every key
             runs[mode] = _step_run(p, mode[:-len("_hints")], n, hints={0: -1, 1: 0, 3: -1})
         else:
@@ -241,7 +247,7 @@ def test_step_modes_bit_identical_to_entry_points(wl_name):
                                          ("qwen3-8b-layer", 4, 3)])
 def test_two_stream_layer_rotation_matches_entry_points(wl_name, L, n):
     """The bench's schedule: L layers in rotation on two streams, one workspace,
-    idx pair and event pair per layer and one shared q_ready event; every step
+    idx pair and event pair per layer and one shared context; every step
     of every layer equals the entry-point schedule of that layer (at the bench
     shape too: four 1 GiB layers)."""
     base = wk.CONFIGS.get(wl_name) or SMALL_STEP_CASES[wl_name]
@@ -261,7 +267,7 @@ def test_two_stream_layer_rotation_matches_entry_points(wl_name, L, n):
     nsel = [[torch.zeros((B, Hkv), dtype=torch.int32, device=DEV) for _ in range(2)] for _ in range(L)]
     ev = [[A.HipEvent(), A.HipEvent()] for _ in range(L)]
     outs = [torch.empty_like(p.out) for p in probs]
-    q_ready = A.HipEvent()
+    ctx = A.AspContext()
     attn, sel = torch.cuda.Stream(), torch.cuda.Stream()
     attn.wait_stream(torch.cuda.current_stream())
     got = [[] for _ in range(L)]
@@ -281,7 +287,7 @@ def test_two_stream_layer_rotation_matches_entry_points(wl_name, L, n):
             else:
                 A.asp_step(d, c, q, p.q_hist, p.newest, p.length, p.k, p.v, p.seq_lens, idx[l][cur], nsel[l][cur],
                            idx[l][nxt], nsel[l][nxt], outs[l], ws[l], attn_stream=attn, sel_stream=sel,
-                           q_ready=q_ready, idx_cur_ready=ev[l][cur], idx_next_ready=ev[l][nxt])
+                           ctx=ctx, idx_cur_ready=ev[l][cur], idx_next_ready=ev[l][nxt])
             # snapshots in each writer's stream order: the attention output on the
             # attention stream, the selection and the ring where the step completes
             # them (the selection stream once pipelined)
