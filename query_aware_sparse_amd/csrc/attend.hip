@@ -1,8 +1,16 @@
-// Launches of the sparse attention and its merge; the attention block body is
-// in attend_block.h.
+// Launches of the sparse attention and its merge.  bf16 K/V: the matrix-core
+// block of attend_mfma.h, a few splits per unit (about ATTM_TARGET_BLOCKS
+// blocks in all, at least ATTM_WAVES chunks per split), the merge only when a
+// unit is split.  fp32 K/V: the VALU block of attend_block.h, one split per
+// attend_tokens_per_block() tokens, then the merge.
 #include "attend_block.h"
+#include "attend_mfma.h"
 
 namespace asp {
+
+// Random 256-byte row gathers reach the read ceiling with some 256 blocks of
+// 512 threads in flight (fewer leave the per-CU request rate as the bound).
+constexpr int ATTM_TARGET_BLOCKS = 256;
 
 int attend_tokens_per_block(int D, int kv) {
   const int row_bytes = D * (kv == 0 ? 2 : 4);
@@ -10,9 +18,31 @@ int attend_tokens_per_block(int D, int kv) {
   return ATT_WAVES * ATT_NL * kpw;
 }
 
+// List positions per split of the bf16 path (a multiple of the chunk).
+static int attm_per(const Shape& s, int nsplit) {
+  const int total = s.C + s.R;
+  const int per = (total + nsplit - 1) / nsplit;
+  return (per + ATTM_CHUNK - 1) / ATTM_CHUNK * ATTM_CHUNK;
+}
+
 int attend_num_splits(const Shape& s) {
+  const int total = s.C + s.R;
+  if (s.kv == 0) {
+    const int units = s.B * s.Hkv;
+    const int want = units > 0 ? (ATTM_TARGET_BLOCKS + units - 1) / units : 1;
+    const int cap = (total + ATTM_WAVES * ATTM_CHUNK - 1) / (ATTM_WAVES * ATTM_CHUNK);
+    int ns = want < cap ? want : cap;
+    if (ns < 1) ns = 1;
+    // splits that the rounding of `per` leaves empty are not launched
+    return (total + attm_per(s, ns) - 1) / attm_per(s, ns);
+  }
   const int tpb = attend_tokens_per_block(s.D, s.kv);
-  return (s.C + s.R + tpb - 1) / tpb;
+  return (total + tpb - 1) / tpb;
+}
+
+// Positions of the list handled by one split (one attention block).
+static int attend_split_positions(const Shape& s) {
+  return s.kv == 0 ? attm_per(s, attend_num_splits(s)) : attend_tokens_per_block(s.D, s.kv);
 }
 
 size_t attend_partials_bytes(const Shape& s) {
@@ -34,6 +64,17 @@ __global__ void __launch_bounds__(ATT_THREADS) attend_kernel(const float* __rest
                                  blockIdx.x, blockIdx.y, smem);
 }
 
+template <int D, int G, bool RECENT>
+__global__ void __launch_bounds__(ATTM_THREADS) attend_mfma_kernel(
+    const float* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ idx, const int32_t* __restrict__ n_sel,
+    float* __restrict__ out, float* __restrict__ part_acc, float* __restrict__ part_ml, int Hq, int Hkv, int T_cap,
+    int C, int R, int nsplit, int per) {
+  __shared__ __align__(16) unsigned char smem[attm_lds_bytes<D, G>()];
+  attend_mfma_block<D, G, RECENT>(q, k, v, seq_lens, idx, n_sel, out, part_acc, part_ml, Hq, Hkv, T_cap, C, R,
+                                  nsplit, per, blockIdx.x, blockIdx.y, smem);
+}
+
 // One workgroup per (sequence, query head): log-sum-exp merge of the partials.
 // The first wavefront reads the m/l pairs of all splits (independent loads,
 // splits strided over its lanes) and forms the maximum, the split weights and
@@ -46,7 +87,7 @@ __global__ void __launch_bounds__(128) merge_kernel(const float* __restrict__ pa
                                                     const int32_t* __restrict__ seq_lens,
                                                     const int32_t* __restrict__ n_sel, float* __restrict__ out,
                                                     int Hq, int Hkv, int G, int D, int T_cap, int C, int R,
-                                                    int nsplit, int tpb) {
+                                                    int nsplit, int per) {
   constexpr int PER = MERGE_MAX_SPLITS / 64;
   __shared__ float sw[MERGE_MAX_SPLITS];
   __shared__ float s_inv_l;
@@ -55,7 +96,7 @@ __global__ void __launch_bounds__(128) merge_kernel(const float* __restrict__ pa
   const int g = h / G, hh = h % G;
   const int unit = b * Hkv + g;
   const AttendList al = attend_list(n_sel, seq_lens, unit, Hkv, C, R, T_cap);
-  const int ns = min((al.n + al.r + tpb - 1) / tpb, MERGE_MAX_SPLITS);
+  const int ns = min(min((al.n + al.r + per - 1) / per, nsplit), MERGE_MAX_SPLITS);
   const int t = threadIdx.x;
   if (t < 64) {
     float m[PER], l[PER];
@@ -124,6 +165,35 @@ static hipError_t launch_attend_d(const Shape& s, const float* q, const void* k,
   return hipGetLastError();
 }
 
+template <int D>
+static hipError_t launch_attend_mfma(const Shape& s, const float* q, const void* k, const void* v,
+                                     const int32_t* seq_lens, const int32_t* idx, const int32_t* n_sel, float* out,
+                                     float* part_acc, float* part_ml, hipStream_t st) {
+  const int nsplit = attend_num_splits(s);
+  const int per = attm_per(s, nsplit);
+  const dim3 grid(nsplit, s.B * s.Hkv);
+  const uint16_t* kk = static_cast<const uint16_t*>(k);
+  const uint16_t* vv = static_cast<const uint16_t*>(v);
+#define ASP_ATTM_LAUNCH(GG)                                                                                       \
+  do {                                                                                                            \
+    if (s.R > 0)                                                                                                  \
+      hipLaunchKernelGGL((attend_mfma_kernel<D, GG, true>), grid, dim3(ATTM_THREADS), 0, st, q, kk, vv, seq_lens, \
+                         idx, n_sel, out, part_acc, part_ml, s.Hq, s.Hkv, s.T_cap, s.C, s.R, nsplit, per);        \
+    else                                                                                                          \
+      hipLaunchKernelGGL((attend_mfma_kernel<D, GG, false>), grid, dim3(ATTM_THREADS), 0, st, q, kk, vv,          \
+                         seq_lens, idx, n_sel, out, part_acc, part_ml, s.Hq, s.Hkv, s.T_cap, s.C, 0, nsplit, per); \
+  } while (0)
+  switch (s.G) {
+    case 1: ASP_ATTM_LAUNCH(1); break;
+    case 2: ASP_ATTM_LAUNCH(2); break;
+    case 4: ASP_ATTM_LAUNCH(4); break;
+    case 8: ASP_ATTM_LAUNCH(8); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef ASP_ATTM_LAUNCH
+  return hipGetLastError();
+}
+
 hipError_t launch_attend(const Shape& s, const float* q, const void* k, const void* v, const int32_t* seq_lens,
                          const int32_t* idx, const int32_t* n_sel, float* out, void* partials, hipStream_t st) {
   if (s.B == 0) return hipSuccess;
@@ -131,13 +201,15 @@ hipError_t launch_attend(const Shape& s, const float* q, const void* k, const vo
   float* part_acc = static_cast<float*>(partials);
   float* part_ml = part_acc + (size_t)s.B * s.Hkv * nsplit * s.G * s.D;
   hipError_t e;
-  if (s.kv == 0)
-    e = s.D == 64 ? launch_attend_d<uint16_t, 64>(s, q, k, v, seq_lens, idx, n_sel, part_acc, part_ml, st)
-                  : launch_attend_d<uint16_t, 128>(s, q, k, v, seq_lens, idx, n_sel, part_acc, part_ml, st);
-  else
+  if (s.kv == 0) {
+    e = s.D == 64 ? launch_attend_mfma<64>(s, q, k, v, seq_lens, idx, n_sel, out, part_acc, part_ml, st)
+                  : launch_attend_mfma<128>(s, q, k, v, seq_lens, idx, n_sel, out, part_acc, part_ml, st);
+    if (e != hipSuccess || nsplit == 1) return e;  // one split: the blocks wrote out
+  } else {
     e = s.D == 64 ? launch_attend_d<float, 64>(s, q, k, v, seq_lens, idx, n_sel, part_acc, part_ml, st)
                   : launch_attend_d<float, 128>(s, q, k, v, seq_lens, idx, n_sel, part_acc, part_ml, st);
-  if (e != hipSuccess) return e;
+    if (e != hipSuccess) return e;
+  }
   return launch_merge(s, seq_lens, n_sel, out, partials, st);
 }
 
@@ -148,7 +220,7 @@ hipError_t launch_merge(const Shape& s, const int32_t* seq_lens, const int32_t* 
   const float* part_acc = static_cast<const float*>(partials);
   const float* part_ml = part_acc + (size_t)s.B * s.Hkv * nsplit * s.G * s.D;
   hipLaunchKernelGGL(merge_kernel, dim3(s.B * s.Hq), dim3(128), 0, st, part_acc, part_ml, seq_lens, n_sel, out,
-                     s.Hq, s.Hkv, s.G, s.D, s.T_cap, s.C, s.R, nsplit, attend_tokens_per_block(s.D, s.kv));
+                     s.Hq, s.Hkv, s.G, s.D, s.T_cap, s.C, s.R, nsplit, attend_split_positions(s));
   return hipGetLastError();
 }
 

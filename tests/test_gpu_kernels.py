@@ -307,3 +307,19 @@ def test_attend_dense_case_and_unsorted_indices():
     # C = T: every token selected (dense decode attention); order of idx irrelevant.
     _attend_case(1, 2, 4, 128, 1024, 1024, "bf16", [1024], seed=31)
     _attend_case(1, 2, 4, 128, 1024, 1024, "bf16", [1024], seed=31, sorted_idx=False)
+
+
+@pytest.mark.parametrize("G,D", [(4, 128), (8, 128), (2, 64)])
+def test_attend_many_units_one_split(G, D):
+    # 256 units: the bf16 attention runs one block per unit, which writes the
+    # normalised output itself (no partials, no merge launch); lists of every
+    # length from empty to full, and a list that ends inside a chunk.
+    err = _attend_case(32, 8, G, D, 2048, 512, "bf16", [512, 0, 1, 31, 33, 300, 511], seed=7 + G + D)
+    assert err < 1e-4
+
+
+def test_attend_split_boundaries():
+    # 64 units at C = 2048 (four splits of 512 positions) with lists that end
+    # exactly on and just past a split and a chunk boundary.
+    err = _attend_case(8, 8, 4, 128, 4096, 2048, "bf16", [2048, 512, 513, 1536, 1537, 32, 33, 0], seed=5)
+    assert err < 1e-4
