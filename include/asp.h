@@ -60,7 +60,8 @@ typedef enum {
   ASP_ERR_UNSUPPORTED = 2, /* valid in principle, not implemented (e.g. head_dim 96) */
   ASP_ERR_WORKSPACE = 3,   /* ws is NULL or ws_bytes < asp_workspace_size(...) */
   ASP_ERR_HIP = 4,         /* a HIP launch / event / stream call failed */
-  ASP_ERR_HOST_MEMORY = 5  /* a host allocation failed (asp_context_create) */
+  ASP_ERR_HOST_MEMORY = 5, /* a host allocation failed (asp_context_create) */
+  ASP_ERR_SCRATCH = 6      /* more scratch than ASP_STATIC_SCRATCH_BYTES (asp_sparse_decode_static) */
 } asp_status;
 
 typedef enum { ASP_KV_BF16 = 0, ASP_KV_F32 = 1 } asp_kv_dtype;
@@ -231,6 +232,26 @@ asp_status asp_selection_overlap(const asp_dims* dims, const asp_cfg* cfg, const
 asp_status asp_sparse_decode(const asp_dims* dims, const asp_cfg* cfg, const float* q, const void* k, const void* v,
                              const int32_t* seq_lens, const int32_t* idx, const int32_t* n_sel, float* out, void* ws,
                              size_t ws_bytes, hipStream_t stream);
+
+/* asp_sparse_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same attention and merge, with the split-K partials in a
+ * scratch buffer built into the library instead of a caller's workspace.
+ * Arguments, results and errors as asp_sparse_decode, minus ws/ws_bytes; the
+ * call allocates nothing (no hipMalloc, no allocating library routine).
+ * The scratch is ASP_STATIC_SCRATCH_BYTES of device memory per GPU, held from
+ * the library's load until the process ends; a shape whose partials
+ * (asp_workspace_size(ASP_OP_DECODE) bytes) exceed it gives ASP_ERR_SCRATCH
+ * before anything is enqueued.  Its contents need no initialisation (every
+ * partial is written before it is read) and are left behind by each call.
+ * Every call on one GPU uses that GPU's single copy: two calls whose work
+ * overlaps on a device (different streams, different host threads, not
+ * ordered by the caller) race and give unspecified outputs.  The first call
+ * on a device looks the buffer's address up with that device current. */
+#define ASP_STATIC_SCRATCH_BYTES (8u << 20)
+asp_status asp_sparse_decode_static(const asp_dims* dims, const asp_cfg* cfg, const float* q, const void* k,
+                                    const void* v, const int32_t* seq_lens, const int32_t* idx, const int32_t* n_sel,
+                                    float* out, hipStream_t stream);
 
 /* Page-level selection, the baseline the pages compare against ([summary]
  * "Problem" and "Experimental setup", its baselines; [abstract]: Quest, which

@@ -21,7 +21,8 @@ __all__ = [
     "KV_BF16", "KV_F32", "HIST_BINS",
     "asp_workspace_size", "asp_status_string", "asp_push_query", "asp_predict_query", "asp_score_keys",
     "asp_select_topc", "asp_score_candidates", "asp_select_candidates", "asp_sparse_decode", "asp_step",
-    "asp_selection_overlap", "AspContext", "CTX_SCORE_ALL_CUS", "PreparedStep",
+    "asp_selection_overlap", "AspContext", "CTX_SCORE_ALL_CUS", "PreparedStep", "asp_sparse_decode_static",
+    "STATIC_SCRATCH_BYTES",
     "asp_page_summary_size", "asp_page_summary", "asp_page_scores", "asp_page_select_workspace_size",
     "asp_page_select", "page_count",
 ]
@@ -33,8 +34,9 @@ OP_PUSH, OP_PREDICT, OP_SCORE, OP_SELECT, OP_DECODE, OP_STEP, OP_CANDIDATES = ra
 KV_BF16, KV_F32 = 0, 1
 HIST_BINS = 2048  # bins of the coarse score histograms (ASP_HIST_BINS)
 CTX_SCORE_ALL_CUS = 1  # asp_context_create flag: the score stream may use every CU
+STATIC_SCRATCH_BYTES = 8 << 20  # built-in scratch of asp_sparse_decode_static (ASP_STATIC_SCRATCH_BYTES)
 _STATUS_NAMES = {0: "ASP_OK", 1: "ASP_ERR_INVALID_ARG", 2: "ASP_ERR_UNSUPPORTED", 3: "ASP_ERR_WORKSPACE",
-                 4: "ASP_ERR_HIP", 5: "ASP_ERR_HOST_MEMORY"}
+                 4: "ASP_ERR_HIP", 5: "ASP_ERR_HOST_MEMORY", 6: "ASP_ERR_SCRATCH"}
 
 
 class AspError(RuntimeError):
@@ -88,6 +90,7 @@ def load():
     lib.asp_score_candidates.argtypes = [D, C, P, P, P, P, SZ, P]
     lib.asp_select_candidates.argtypes = [D, C, P, P, P, P, P, P, SZ, P]
     lib.asp_sparse_decode.argtypes = [D, C, P, P, P, P, P, P, P, P, SZ, P]
+    lib.asp_sparse_decode_static.argtypes = [D, C, P, P, P, P, P, P, P, P]
     lib.asp_step.argtypes = [P, D, C, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P, P, P, P]
     lib.asp_selection_overlap.argtypes = [D, C, P, P, P, P, P, P]
     lib.asp_context_create.argtypes = [ctypes.c_int32, ctypes.c_uint32, ctypes.POINTER(ctypes.c_void_p)]
@@ -102,7 +105,7 @@ def load():
     lib.asp_page_select.argtypes = [D, C, I32, P, P, P, P, P, P, P, SZ, P]
     for name in ("asp_push_query", "asp_predict_query", "asp_score_keys", "asp_select_topc",
                  "asp_score_candidates", "asp_select_candidates", "asp_sparse_decode", "asp_step",
-                 "asp_selection_overlap", "asp_context_create", "asp_context_destroy"):
+                 "asp_selection_overlap", "asp_context_create", "asp_context_destroy", "asp_sparse_decode_static"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -309,6 +312,24 @@ def asp_sparse_decode(dims: Dims, cfg: Cfg, q, k, v, seq_lens, idx, n_sel, out, 
                                                          _ptr(v), _ptr(seq_lens), _ptr(idx), _ptr(n_sel), _ptr(out),
                                                          wp, wb,
                                                          _stream_handle(stream)))
+
+
+def asp_sparse_decode_static(dims: Dims, cfg: Cfg, q, k, v, seq_lens, idx, n_sel, out, stream=None) -> None:
+    """asp_sparse_decode with the library's built-in scratch instead of a
+    workspace: it allocates nothing.  Calls whose work overlaps on one GPU race
+    (they share that GPU's scratch).  seq_lens may be None when cfg.recent is 0."""
+    B, Hq, Hkv, D, T, C = dims.batch, dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.t_cap, cfg.top_c
+    _check(q, "q", (B, Hq, D), torch.float32)
+    _check(k, "k", (B, Hkv, T, D), _kv_dtype(dims))
+    _check(v, "v", (B, Hkv, T, D), _kv_dtype(dims))
+    if seq_lens is not None:
+        _check(seq_lens, "seq_lens", (B,), torch.int32)
+    _check(idx, "idx", (B, Hkv, C), torch.int32)
+    _check(n_sel, "n_sel", (B, Hkv), torch.int32)
+    _check(out, "out", (B, Hq, D), torch.float32)
+    _raise("asp_sparse_decode_static", load().asp_sparse_decode_static(
+        ctypes.byref(dims), ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(seq_lens), _ptr(idx), _ptr(n_sel),
+        _ptr(out), _stream_handle(stream)))
 
 
 class AspContext:

@@ -3,6 +3,7 @@
 // entry point.
 #include <math.h>
 
+#include <mutex>
 #include <new>
 
 #include "../../include/asp.h"
@@ -171,6 +172,38 @@ asp_status check_cand_ws(const Shape& s, void* ws, size_t ws_bytes) {
   return ASP_OK;
 }
 
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+// Scratch of asp_sparse_decode_static: the attention's split-K partials.  One
+// copy per device, held while the library is loaded.  Host code never uses
+// this name as an address (it is the host-side stand-in of the symbol): the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[ASP_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipErrorNotInitialized;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// The device address of `scratch` on the current device, looked up on the
+// first call made with that device current.
+asp_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return ASP_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return ASP_ERR_UNSUPPORTED;
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once, [&slot] { slot.err = hipGetSymbolAddress(&slot.ptr, HIP_SYMBOL(scratch)); });
+  if (slot.err != hipSuccess || slot.ptr == nullptr) return ASP_ERR_HIP;
+  *out = slot.ptr;
+  return ASP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -189,6 +222,8 @@ const char* asp_status_string(asp_status status) {
     case ASP_ERR_WORKSPACE: return "workspace missing or smaller than asp_workspace_size()";
     case ASP_ERR_HIP: return "a HIP kernel launch, event or stream call failed";
     case ASP_ERR_HOST_MEMORY: return "host memory allocation failed";
+    case ASP_ERR_SCRATCH:
+      return "the shape needs more attention scratch than the built-in buffer (ASP_STATIC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }
@@ -292,6 +327,22 @@ asp_status asp_sparse_decode(const asp_dims* dims, const asp_cfg* cfg, const flo
   const size_t need = ws_bytes_for(s, ASP_OP_DECODE);
   if (ws == nullptr || ws_bytes < need) return ASP_ERR_WORKSPACE;
   return hip_status(asp::launch_attend(s, q, k, v, seq_lens, idx, n_sel, out, ws, stream));
+}
+
+asp_status asp_sparse_decode_static(const asp_dims* dims, const asp_cfg* cfg, const float* q, const void* k,
+                                    const void* v, const int32_t* seq_lens, const int32_t* idx, const int32_t* n_sel,
+                                    float* out, hipStream_t stream) {
+  Shape s;
+  asp_status st = check_all(dims, cfg, &s);
+  if (st != ASP_OK) return st;
+  if (!q || !k || !v || !idx || !n_sel || !out) return ASP_ERR_INVALID_ARG;
+  if (s.R > 0 && seq_lens == nullptr) return ASP_ERR_INVALID_ARG;
+  if (!aligned16(k) || !aligned16(v) || !aligned4(q) || !aligned4(out)) return ASP_ERR_INVALID_ARG;
+  if (asp::attend_partials_bytes(s) > (size_t)ASP_STATIC_SCRATCH_BYTES) return ASP_ERR_SCRATCH;
+  void* partials = nullptr;
+  st = scratch_on_current_device(&partials);
+  if (st != ASP_OK) return st;
+  return hip_status(asp::launch_attend(s, q, k, v, seq_lens, idx, n_sel, out, partials, stream));
 }
 
 size_t asp_page_summary_size(const asp_dims* dims, int32_t page_size) {

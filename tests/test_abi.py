@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "asp_workspace_size", "asp_status_string", "asp_push_query", "asp_predict_query", "asp_score_keys",
         "asp_select_topc", "asp_score_candidates", "asp_select_candidates", "asp_sparse_decode", "asp_step",
-        "asp_selection_overlap", "asp_context_create", "asp_context_destroy", "asp_page_summary_size",
+        "asp_selection_overlap", "asp_context_create", "asp_context_destroy", "asp_sparse_decode_static",
+        "asp_page_summary_size",
         "asp_page_summary",
         "asp_page_scores", "asp_page_select_workspace_size", "asp_page_select"])
 
@@ -52,7 +53,7 @@ def test_context_argument_checks(lib):
 
 
 def test_status_strings(lib):
-    for code in range(6):
+    for code in range(7):
         assert A.asp_status_string(code)
     assert A.asp_status_string(77) == "unknown status"
 
