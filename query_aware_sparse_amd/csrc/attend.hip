@@ -76,11 +76,12 @@ __global__ void __launch_bounds__(ATTM_THREADS) attend_mfma_kernel(
 }
 
 // One workgroup per (sequence, query head): log-sum-exp merge of the partials.
-// The first wavefront reads the m/l pairs of all splits (independent loads,
-// splits strided over its lanes) and forms the maximum, the split weights and
-// the normaliser with cross-lane reductions; each output coordinate then reads
-// its partial sums with independent loads.
+// Thread d combines output coordinate d.  The splits are read in batches of
+// MERGE_BATCH, each thread issuing the batch's (max, sum) pairs and its own
+// partial sums together (one memory round trip per batch), with a running
+// maximum across batches.
 constexpr int MERGE_MAX_SPLITS = 256;
+constexpr int MERGE_BATCH = 8;
 
 __global__ void __launch_bounds__(128) merge_kernel(const float* __restrict__ part_acc,
                                                     const float* __restrict__ part_ml,
@@ -88,53 +89,47 @@ __global__ void __launch_bounds__(128) merge_kernel(const float* __restrict__ pa
                                                     const int32_t* __restrict__ n_sel, float* __restrict__ out,
                                                     int Hq, int Hkv, int G, int D, int T_cap, int C, int R,
                                                     int nsplit, int per) {
-  constexpr int PER = MERGE_MAX_SPLITS / 64;
-  __shared__ float sw[MERGE_MAX_SPLITS];
-  __shared__ float s_inv_l;
   const int bh = blockIdx.x;
   const int b = bh / Hq, h = bh % Hq;
   const int g = h / G, hh = h % G;
   const int unit = b * Hkv + g;
+  const int d = threadIdx.x;
+  if (d >= D) return;
   const AttendList al = attend_list(n_sel, seq_lens, unit, Hkv, C, R, T_cap);
   const int ns = min(min((al.n + al.r + per - 1) / per, nsplit), MERGE_MAX_SPLITS);
-  const int t = threadIdx.x;
-  if (t < 64) {
-    float m[PER], l[PER];
+  float M = -INFINITY, L = 0.0f, O = 0.0f;
+  for (int s0 = 0; s0 < ns; s0 += MERGE_BATCH) {
+    float m[MERGE_BATCH], l[MERGE_BATCH], a[MERGE_BATCH];
 #pragma unroll
-    for (int r = 0; r < PER; ++r) {
-      const int sp = t + 64 * r;
-      m[r] = -INFINITY;
-      l[r] = 0.0f;
+    for (int i = 0; i < MERGE_BATCH; ++i) {
+      const int sp = s0 + i;
+      m[i] = -INFINITY;
+      l[i] = 0.0f;
+      a[i] = 0.0f;
       if (sp < ns) {
         const size_t p = ((size_t)unit * nsplit + sp) * G + hh;
-        m[r] = part_ml[p * 2];
-        l[r] = part_ml[p * 2 + 1];
+        m[i] = part_ml[p * 2];
+        l[i] = part_ml[p * 2 + 1];
+        a[i] = part_acc[p * D + d];
       }
     }
-    float mx = m[0];
+    float bm = m[0];
 #pragma unroll
-    for (int r = 1; r < PER; ++r) mx = fmaxf(mx, m[r]);
-    const float M = group_max<64>(mx);
-    float lw = 0.0f;
+    for (int i = 1; i < MERGE_BATCH; ++i) bm = fmaxf(bm, m[i]);
+    const float Mn = fmaxf(M, bm);
+    if (Mn == -INFINITY) continue;  // splits whose tokens were all skipped carry m = -inf and l = 0
+    const float sc = M == -INFINITY ? 0.0f : exp2f(M - Mn);
+    L *= sc;
+    O *= sc;
 #pragma unroll
-    for (int r = 0; r < PER; ++r) {
-      const int sp = t + 64 * r;
-      // splits whose tokens were all skipped carry m = -inf and l = 0
-      const float w = (sp < ns && m[r] != -INFINITY) ? exp2f(m[r] - M) : 0.0f;
-      if (sp < ns) sw[sp] = w;
-      lw = fmaf(l[r], w, lw);
+    for (int i = 0; i < MERGE_BATCH; ++i) {
+      const float w = m[i] == -INFINITY ? 0.0f : exp2f(m[i] - Mn);
+      L = fmaf(w, l[i], L);
+      O = fmaf(w, a[i], O);
     }
-    const float L = group_sum<64>(lw);
-    if (t == 0) s_inv_l = L > 0.0f ? 1.0f / L : 0.0f;
+    M = Mn;
   }
-  __syncthreads();
-  const float inv_l = s_inv_l;
-  for (int d = t; d < D; d += blockDim.x) {
-    float o = 0.0f;
-    const float* pa = part_acc + (((size_t)unit * nsplit) * G + hh) * D + d;
-    for (int s = 0; s < ns; ++s) o = fmaf(pa[(size_t)s * G * D], sw[s], o);
-    out[(size_t)bh * D + d] = o * inv_l;
-  }
+  out[(size_t)bh * D + d] = L > 0.0f ? O / L : 0.0f;
 }
 
 template <typename KV, int D>

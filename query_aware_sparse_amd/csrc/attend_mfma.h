@@ -41,6 +41,7 @@ namespace asp {
 constexpr int ATTM_THREADS = 512;
 constexpr int ATTM_WAVES = ATTM_THREADS / 64;
 constexpr int ATTM_CHUNK = 16;
+constexpr int ATTM_DEPTH = 2;  // chunks whose row gathers are in flight per wave
 
 typedef __bf16 attm_bf16x8 __attribute__((ext_vector_type(8)));
 typedef short attm_i16x4 __attribute__((ext_vector_type(4)));
@@ -256,27 +257,33 @@ __device__ __forceinline__ void attend_mfma_block(const float* __restrict__ q, c
   for (int i = 0; i < D / 16; ++i) o[i] = attm_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   float m_run = -INFINITY, l_run = 0.0f;
 
-  // The wave's chunks: p_begin + 16 (wave + 8 j).  While chunk j is computed,
-  // the rows of chunk j + 1 and the lookup of chunk j + 2 are in flight.
+  // The wave's chunks j = 0, 1, ...: positions p_begin + 16 (wave + 8 j).
+  // Chunk j lives in buffer j % ATTM_DEPTH.  While it is computed, the row
+  // gathers of the next ATTM_DEPTH - 1 chunks and the lookup of the one after
+  // are in flight.
   constexpr int STRIDE = ATTM_WAVES * ATTM_CHUNK;
-  AttmChunk<D> ca, cb;
-  int p0 = p_begin + wave * ATTM_CHUNK;
-  AttmTok tok1 = {-1, false}, tok2 = {-1, false};
-  if (p0 < p_end) {
-    const AttmTok tok0 = attm_lookup<RECENT>(ib, al, p0, p_end, lane);
-    tok1 = attm_lookup<RECENT>(ib, al, p0 + STRIDE, p_end, lane);
-    attm_load<D, RECENT>(ca, kb, vb, tok0, al, T_cap, lane);
-  }
-  for (; p0 < p_end; p0 += 2 * STRIDE) {
-    const int p1 = p0 + STRIDE;
-    tok2 = attm_lookup<RECENT>(ib, al, p1 + STRIDE, p_end, lane);
-    if (p1 < p_end) attm_load<D, RECENT>(cb, kb, vb, tok1, al, T_cap, lane);
-    attm_compute<D>(ca, qhi, qlo, o, m_run, l_run, lane);
-    if (p1 >= p_end) break;
-    const int p2 = p1 + STRIDE;
-    tok1 = attm_lookup<RECENT>(ib, al, p2 + STRIDE, p_end, lane);
-    if (p2 < p_end) attm_load<D, RECENT>(ca, kb, vb, tok2, al, T_cap, lane);
-    attm_compute<D>(cb, qhi, qlo, o, m_run, l_run, lane);
+  constexpr int NB = ATTM_DEPTH;
+  const int first = p_begin + wave * ATTM_CHUNK;
+  AttmChunk<D> buf[NB];
+  AttmTok look[NB];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) look[u] = attm_lookup<RECENT>(ib, al, first + u * STRIDE, p_end, lane);
+#pragma unroll
+  for (int u = 0; u + 1 < NB; ++u)
+    if (first + u * STRIDE < p_end) attm_load<D, RECENT>(buf[u], kb, vb, look[u], al, T_cap, lane);
+  for (int j0 = 0; first + j0 * STRIDE < p_end; j0 += NB) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int j = j0 + u;
+      if (first + j * STRIDE >= p_end) break;
+      constexpr int LAST = NB - 1;
+      // the slot of chunk j + NB - 1 held chunk j - 1, already computed
+      const int pl = first + (j + LAST) * STRIDE;
+      const AttmTok nxt = attm_lookup<RECENT>(ib, al, pl + STRIDE, p_end, lane);  // chunk j + NB
+      if (pl < p_end) attm_load<D, RECENT>(buf[(u + LAST) % NB], kb, vb, look[(u + LAST) % NB], al, T_cap, lane);
+      look[u] = nxt;  // chunk j's lookup was used when its rows were gathered
+      attm_compute<D>(buf[u], qhi, qlo, o, m_run, l_run, lane);
+    }
   }
   // The head's sum over the lanes that hold its tokens.
   l_run += __shfl_xor(l_run, 16);
