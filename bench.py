@@ -105,7 +105,7 @@ def measured_traffic(kernel_sources):
 
 STEP_SOURCES = [os.path.join(ROOT, "query_aware_sparse_amd", "csrc", f)
                 for f in ("api.hip", "predict.hip", "score.hip", "score_block.h", "select.hip", "attend.hip",
-                          "attend_block.h", "asp_internal.h")]
+                          "attend_mfma.h", "attend_block.h", "asp_internal.h")]
 
 
 def in_step_score_launch_us():
@@ -178,6 +178,53 @@ def host_cpu() -> dict:
             "usable": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
 
 
+_DRIVER = None
+
+
+def driver():
+    """bench_driver.so (the C++ timing loop and the stream hold), built by
+    __graft_entry__.build() beside this file."""
+    global _DRIVER
+    if _DRIVER is None:
+        import ctypes
+        _DRIVER = ctypes.CDLL(os.path.join(ROOT, "bench_driver.so"))
+        _DRIVER.bench_hold.argtypes = [ctypes.c_void_p, ctypes.c_double]
+        _DRIVER.bench_hold.restype = ctypes.c_int
+    return _DRIVER
+
+
+def hold(stream, us: float) -> None:
+    """Holds `stream` for about `us` microseconds with a single-wave wait kernel."""
+    if driver().bench_hold(stream.cuda_stream, float(us)) != 0:
+        raise RuntimeError("bench_hold failed")
+
+
+def raw_call(A, name, *args):
+    """The C entry point `name` with its arguments marshalled once: tensors as
+    device pointers, Dims/Cfg by reference, streams as handles, ints as they
+    are.  Calling the result costs one ctypes call; the timing loops use it for
+    arguments the binding has already accepted in their warm-up calls."""
+    import ctypes
+    import torch
+    conv = []
+    for a in args:
+        if isinstance(a, torch.Tensor):
+            conv.append(ctypes.c_void_p(a.data_ptr()))
+        elif isinstance(a, (A.Dims, A.Cfg)):
+            conv.append(ctypes.byref(a))
+        elif isinstance(a, torch.cuda.Stream):
+            conv.append(ctypes.c_void_p(a.cuda_stream))
+        else:
+            conv.append(a)
+    fn = getattr(A.load(), name)
+
+    def call():
+        status = fn(*conv)
+        if status != 0:
+            raise RuntimeError("%s failed: %d" % (name, status))
+    return call
+
+
 def page_baseline(A, dims, cfg, wl, layers, P, time_entry, out, ws_dec, attn, n) -> dict:
     """The page-level (Quest) baseline on the same layers: its per-page min/max
     summaries are built once per KV cache; each of its decode steps scores the
@@ -209,15 +256,35 @@ def page_baseline(A, dims, cfg, wl, layers, P, time_entry, out, ws_dec, attn, n)
         A.asp_sparse_decode(dims, cfg, q_of(i), lay["k"], lay["v"], lay["seq_lens"], idx, nsel, out, ws_dec,
                             stream=attn)
 
+    def rc(name, *a):
+        return raw_call(A, name, *a)
+
+    def page_step_raw(i):
+        lay, (kmin, kmax) = layers[i % L], summ[i % L]
+        sel_call = rc("asp_page_select", dims, cfg, P, q_of(i), kmin, kmax, lay["seq_lens"], idx, nsel, ws, ws.numel(),
+                      attn)
+        dec_call = rc("asp_sparse_decode", dims, cfg, q_of(i), lay["k"], lay["v"], lay["seq_lens"], idx, nsel, out,
+                      ws_dec, ws_dec.numel(), attn)
+
+        def call():
+            sel_call()
+            dec_call()
+        return call
+
     t = {
         "summary_us": time_entry(lambda i: A.asp_page_summary(dims, P, layers[i % L]["k"], layers[i % L]["seq_lens"],
                                                               summ[i % L][0], summ[i % L][1], stream=attn), 20),
-        "page_scores_us": time_entry(lambda i: A.asp_page_scores(dims, P, q_of(i), summ[i % L][0], summ[i % L][1],
-                                                                 layers[i % L]["seq_lens"], pscores, stream=attn), n),
-        "page_select_us": time_entry(lambda i: A.asp_page_select(dims, cfg, P, q_of(i), summ[i % L][0],
-                                                                 summ[i % L][1], layers[i % L]["seq_lens"], idx, nsel,
-                                                                 ws, stream=attn), n),
-        "step_us": time_entry(page_step, n),
+        "page_scores_us": time_entry(
+            lambda i: A.asp_page_scores(dims, P, q_of(i), summ[i % L][0], summ[i % L][1], layers[i % L]["seq_lens"],
+                                        pscores, stream=attn), n,
+            lambda i: rc("asp_page_scores", dims, P, q_of(i), summ[i][0], summ[i][1], layers[i]["seq_lens"], pscores,
+                         attn)),
+        "page_select_us": time_entry(
+            lambda i: A.asp_page_select(dims, cfg, P, q_of(i), summ[i % L][0], summ[i % L][1],
+                                        layers[i % L]["seq_lens"], idx, nsel, ws, stream=attn), n,
+            lambda i: rc("asp_page_select", dims, cfg, P, q_of(i), summ[i][0], summ[i][1], layers[i]["seq_lens"], idx,
+                         nsel, ws, ws.numel(), attn)),
+        "step_us": time_entry(page_step, n, page_step_raw),
     }
     lens = [int(x) for x in layers[0]["seq_lens"].tolist()]
     esize = 2 if wl.kv_dtype == "bf16" else 4
@@ -246,6 +313,10 @@ def main() -> int:
     ap.add_argument("--page-size", type=int, default=16,
                     help="page size of the page-level (Quest) baseline timed beside the step (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--hold-us", type=float, default=0.0,
+                    help="hold the attention stream this long before each timed loop (a bounded wait kernel), so "
+                         "that the host queues the timed steps first and the GPU sets their pace; for kernel traces, "
+                         "whose tracer slows the host.  ms_per_step then comes from the GPU events alone")
     ap.add_argument("--no-cpp-driver", dest="cpp_driver", action="store_false",
                     help="skip the second timing of the same loop issued from C++ (bench_driver.so)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -338,6 +409,8 @@ def main() -> int:
             order[i]()
         torch.cuda.synchronize()
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if args.hold_us > 0:
+            hold(attn, args.hold_us)
         w0 = time.perf_counter()
         ev0.record(attn)
         for i in range(args.warmup, args.warmup + args.steps):
@@ -355,7 +428,7 @@ def main() -> int:
 
     def time_cpp_loop():
         import ctypes
-        drv = ctypes.CDLL(os.path.join(ROOT, "bench_driver.so"))
+        drv = driver()
         P = ctypes.c_void_p
 
         class Layer(ctypes.Structure):
@@ -372,11 +445,12 @@ def main() -> int:
                            (P * 2)(*[e.handle.value for e in lay["ev"]]), out.data_ptr(), lay["ws"].data_ptr(),
                            lay["ws"].numel(), lay["cur"], lay["t"])
         times = (ctypes.c_double * 3)()
-        drv.bench_rotation.argtypes = [P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P]
+        drv.bench_rotation.argtypes = [P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, ctypes.c_double,
+                                       P]
         drv.bench_rotation.restype = ctypes.c_int
         rc = drv.bench_rotation(None if ctx is None else ctx.handle, ctypes.byref(dims), ctypes.byref(cfg), arr, L,
                                 args.warmup, args.steps, attn.cuda_stream, None if sel is None else sel.cuda_stream,
-                                times)
+                                args.hold_us, times)
         if rc != 0:
             raise RuntimeError("bench_rotation failed: %d" % rc)
         for i, lay in enumerate(layers):
@@ -387,7 +461,8 @@ def main() -> int:
     loops = {}
     for name in drivers:
         gpu_ms, wall_ms, issue_ms = (time_python_loop if name == "python" else time_cpp_loop)()
-        per = max(gpu_ms, wall_ms) / args.steps
+        # with a hold before the loop the wall time includes it: the events alone time the steps
+        per = (gpu_ms if args.hold_us > 0 else max(gpu_ms, wall_ms)) / args.steps
         loops[name] = {"ms_per_step": round(per, 5), "steps_per_s": round(1e3 / per, 2),
                        "events_ms_per_step": round(gpu_ms / args.steps, 5),
                        "wall_ms_per_step": round(wall_ms / args.steps, 5),
@@ -402,13 +477,20 @@ def main() -> int:
 
     # Per-kernel timing: each entry point launched alone, back to back on one
     # stream, over the rotating KV caches, bracketed by events on that stream.
-    def time_entry(fn, n):
+    # The warm-up calls go through the binding (which checks the arguments);
+    # the timed calls are the same C calls with their arguments marshalled
+    # once, so that the host issues them faster than the GPU runs them.
+    def time_entry(fn, n, raw=None):
         for i in range(5):
             fn(i)
+        calls = [raw(i) for i in range(L)] if raw is not None else None
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(attn)
         for i in range(n):
-            fn(i)
+            if calls is not None:
+                calls[i % L]()
+            else:
+                fn(i)
         e1.record(attn)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / n  # us per launch
@@ -419,6 +501,7 @@ def main() -> int:
     scores = torch.empty((B, Hkv, wl.t_cap), dtype=torch.float32, device=dev)
     idx_t = torch.empty((B, Hkv, C), dtype=torch.int32, device=dev)
     nsel_t = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+    ws_sel = torch.empty(A.asp_workspace_size(dims, cfg, A.OP_SELECT), dtype=torch.uint8, device=dev)
     for l, lay in enumerate(layers):
         A.asp_predict_query(dims, cfg, lay["q_hist"], lay["newest"], lay["length"], q_pred[l], stream=attn)
     n = args.kernel_launches
@@ -426,24 +509,42 @@ def main() -> int:
     def lay_(i):
         return layers[i % L]
 
+    def rc(name, *a):
+        return raw_call(A, name, *a)
+
     kern = {
-        "predict_us": time_entry(lambda i: A.asp_predict_query(dims, cfg, lay_(i)["q_hist"], lay_(i)["newest"],
-                                                               lay_(i)["length"], q_pred[i % L], stream=attn), n),
+        "predict_us": time_entry(
+            lambda i: A.asp_predict_query(dims, cfg, lay_(i)["q_hist"], lay_(i)["newest"], lay_(i)["length"],
+                                          q_pred[i % L], stream=attn), n,
+            lambda i: rc("asp_predict_query", dims, cfg, lay_(i)["q_hist"], lay_(i)["newest"], lay_(i)["length"],
+                         q_pred[i], attn)),
         # the step's score launch: keys at or above the layer's hints kept as candidates
-        "score_us": time_entry(lambda i: A.asp_score_candidates(dims, cfg, q_pred[i % L], lay_(i)["k"],
-                                                                lay_(i)["seq_lens"], ws_step[i % L], stream=attn), n),
-        "select_us": time_entry(lambda i: A.asp_select_candidates(dims, cfg, q_pred[i % L], lay_(i)["k"],
-                                                                  lay_(i)["seq_lens"], idx_t, nsel_t, ws_step[i % L],
-                                                                  stream=attn), n),
+        "score_us": time_entry(
+            lambda i: A.asp_score_candidates(dims, cfg, q_pred[i % L], lay_(i)["k"], lay_(i)["seq_lens"],
+                                             ws_step[i % L], stream=attn), n,
+            lambda i: rc("asp_score_candidates", dims, cfg, q_pred[i], lay_(i)["k"], lay_(i)["seq_lens"], ws_step[i],
+                         ws_step[i].numel(), attn)),
+        "select_us": time_entry(
+            lambda i: A.asp_select_candidates(dims, cfg, q_pred[i % L], lay_(i)["k"], lay_(i)["seq_lens"], idx_t,
+                                              nsel_t, ws_step[i % L], stream=attn), n,
+            lambda i: rc("asp_select_candidates", dims, cfg, q_pred[i], lay_(i)["k"], lay_(i)["seq_lens"], idx_t,
+                         nsel_t, ws_step[i], ws_step[i].numel(), attn)),
         # the score-row route of the standalone entry points, for comparison
-        "score_keys_us": time_entry(lambda i: A.asp_score_keys(dims, q_pred[i % L], lay_(i)["k"],
-                                                               lay_(i)["seq_lens"], scores, stream=attn), n),
-        "select_topc_us": time_entry(lambda i: A.asp_select_topc(dims, cfg, scores, layers[0]["seq_lens"], idx_t,
-                                                                 nsel_t, stream=attn), n),
-        "attend_us": time_entry(lambda i: A.asp_sparse_decode(dims, cfg, layers[i % L]["qs"][0], layers[i % L]["k"],
-                                                              layers[i % L]["v"], layers[i % L]["seq_lens"],
-                                                              layers[i % L]["idx"][0],
-                                                              layers[i % L]["nsel"][0], out, ws_dec, stream=attn), n),
+        "score_keys_us": time_entry(
+            lambda i: A.asp_score_keys(dims, q_pred[i % L], lay_(i)["k"], lay_(i)["seq_lens"], scores, stream=attn),
+            n, lambda i: rc("asp_score_keys", dims, q_pred[i], lay_(i)["k"], lay_(i)["seq_lens"], scores, None, attn)),
+        "select_topc_us": time_entry(
+            lambda i: A.asp_select_topc(dims, cfg, scores, layers[0]["seq_lens"], idx_t, nsel_t, ws_sel,
+                                        stream=attn), n,
+            lambda i: rc("asp_select_topc", dims, cfg, scores, None, layers[0]["seq_lens"], idx_t, nsel_t, ws_sel,
+                         ws_sel.numel(), attn)),
+        "attend_us": time_entry(
+            lambda i: A.asp_sparse_decode(dims, cfg, lay_(i)["qs"][0], lay_(i)["k"], lay_(i)["v"],
+                                          lay_(i)["seq_lens"], lay_(i)["idx"][0], lay_(i)["nsel"][0], out, ws_dec,
+                                          stream=attn), n,
+            lambda i: rc("asp_sparse_decode", dims, cfg, lay_(i)["qs"][0], lay_(i)["k"], lay_(i)["v"],
+                         lay_(i)["seq_lens"], lay_(i)["idx"][0], lay_(i)["nsel"][0], out, ws_dec, ws_dec.numel(),
+                         attn)),
     }
     sk_bytes = score_kernel_bytes(wl, lens_list)
     achieved = sk_bytes / (kern["score_us"] * 1e-6) / 1e9
@@ -486,6 +587,7 @@ def main() -> int:
         # the same timed loop issued by the Python binding (value) and from C++ (bench_driver.cpp)
         "loops": loops,
         "hw_queues": os.environ.get("GPU_MAX_HW_QUEUES", "HIP default"),
+        "hold_us": args.hold_us,
         "kernels_us": {k_: round(v_, 2) for k_, v_ in kern.items()},
         "roofline": roofline,
         "page_baseline": page,

@@ -11,7 +11,30 @@
 
 #include "asp.h"
 
+// One wave that spins until `ticks` of the constant-rate wall clock have
+// passed (a bounded loop), holding the stream it runs on.
+__global__ void hold_kernel(long long ticks) {
+  const long long t0 = wall_clock64();
+  while (wall_clock64() - t0 < ticks) {
+  }
+}
+
 extern "C" {
+
+// Holds `stream` for about `us` microseconds (a single-wave kernel), so that
+// the host can queue the timed steps behind it and the GPU, not the host,
+// then sets their pace (used for kernel traces, whose tracer slows the host).
+// Returns 0, or -1 for a HIP error.
+int bench_hold(hipStream_t stream, double us) {
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
+      khz <= 0)
+    return -1;
+  const long long ticks = (long long)(us * 1e-3 * khz);
+  if (ticks <= 0) return 0;
+  hipLaunchKernelGGL(hold_kernel, dim3(1), dim3(64), 0, stream, ticks);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
 
 // One layer of the rotation: its queries (qs[t] is the actual query of its
 // step t, [B][Hq][D] fp32), ring, KV cache, selection buffer pair and event
@@ -41,9 +64,11 @@ typedef struct {
 // stream is joined into it, and by the host clock; times[0] = GPU ms between
 // the events, times[1] = wall ms (first record to the end of the final
 // synchronisation), times[2] = host ms spent issuing the timed steps.
+// hold_us > 0: attn is first held that long (bench_hold), after the warm-up
+// and before the first event; the wall time then includes the hold.
 // Returns 0, or the first failing asp_status / -1 for a HIP error.
 int bench_rotation(asp_context* ctx, const asp_dims* dims, const asp_cfg* cfg, bench_layer* layers, int n_layers,
-                   int warmup, int steps, hipStream_t attn, hipStream_t sel, double* times) {
+                   int warmup, int steps, hipStream_t attn, hipStream_t sel, double hold_us, double* times) {
   using clk = std::chrono::steady_clock;
   const size_t q_n = (size_t)dims->batch * dims->n_q_heads * dims->head_dim;
   hipEvent_t e0, e1, joined;
@@ -65,6 +90,7 @@ int bench_rotation(asp_context* ctx, const asp_dims* dims, const asp_cfg* cfg, b
   for (int i = 0; i < warmup && rc == 0; ++i) rc = step(i);
   if (rc == 0 && hipDeviceSynchronize() != hipSuccess) rc = -1;
   if (rc == 0) {
+    if (hold_us > 0.0) rc = bench_hold(attn, hold_us);
     const auto w0 = clk::now();
     if (hipEventRecord(e0, attn) != hipSuccess) rc = -1;
     for (int i = warmup; i < warmup + steps && rc == 0; ++i) rc = step(i);
