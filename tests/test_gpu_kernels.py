@@ -323,3 +323,47 @@ def test_attend_split_boundaries():
     # exactly on and just past a split and a chunk boundary.
     err = _attend_case(8, 8, 4, 128, 4096, 2048, "bf16", [2048, 512, 513, 1536, 1537, 32, 33, 0], seed=5)
     assert err < 1e-4
+
+
+@pytest.mark.parametrize("kv", ["bf16", "f32"])
+def test_nonfinite_keys_leave_finite_rows_exact_and_selection_well_formed(kv):
+    # Keys must be finite (asp.h).  Rows holding +-inf or NaN elements get
+    # unspecified scores, but every finite row still scores exactly (integer
+    # inputs), and both selection routes still give C_eff distinct ascending
+    # in-range indices; the candidate route equals the score-row route on the
+    # GPU's own scores.
+    B, Hkv, G, D, T_cap, C = 2, 2, 4, 128, 3000, 700
+    Hq = G * Hkv
+    q, k = _score_inputs(B, Hq, Hkv, D, T_cap, kv, True, seed=33)
+    bad = {(0, 0, 5): np.inf, (0, 1, 17): -np.inf, (1, 0, 2999): np.nan, (1, 1, 0): np.inf, (0, 0, 2048): np.nan}
+    kf = k.float()
+    for (b, g, i), val in bad.items():
+        kf[b, g, i, (i * 7) % D] = val
+    k = kf.to(k.dtype)
+    lens = torch.tensor([T_cap, T_cap], dtype=torch.int32)
+    dims = dims_for(A, B, Hq, Hkv, D, T_cap, kv)
+    cfg = A.Cfg(8, C, 1e-2)
+    gq, gk, gl = q.to(DEV), k.to(DEV), lens.to(DEV)
+    scores = torch.empty((B, Hkv, T_cap), dtype=torch.float32, device=DEV)
+    A.asp_score_keys(dims, gq, gk, gl, scores)
+    got = np_(scores)
+    ref = oracle.score(q.numpy(), kv_np(k), lens.numpy())
+    finite = np.isfinite(k.float().numpy()).all(axis=3)
+    np.testing.assert_array_equal(got[finite], ref[finite])
+    idx_rows = torch.empty((B, Hkv, C), dtype=torch.int32, device=DEV)
+    n_rows = torch.empty((B, Hkv), dtype=torch.int32, device=DEV)
+    A.asp_select_topc(dims, cfg, scores, gl, idx_rows, n_rows)
+    ws = torch.zeros(A.asp_workspace_size(dims, cfg, A.OP_CANDIDATES), dtype=torch.uint8, device=DEV)
+    idx_c = torch.empty_like(idx_rows)
+    n_c = torch.empty_like(n_rows)
+    A.asp_score_candidates(dims, cfg, gq, gk, gl, ws)
+    A.asp_select_candidates(dims, cfg, gq, gk, gl, idx_c, n_c, ws)
+    torch.cuda.synchronize()
+    ri, rn = oracle.select(got, lens.numpy(), C)  # bit-exact on the GPU's own scores, non-finite ones included
+    for i_, n_ in ((np_(idx_rows), np_(n_rows)), (np_(idx_c), np_(n_c))):
+        np.testing.assert_array_equal(i_, ri)
+        np.testing.assert_array_equal(n_, rn)
+        for b in range(B):
+            for g in range(Hkv):
+                sel = i_[b, g, :C]
+                assert n_[b, g] == C and (np.diff(sel) > 0).all() and sel[0] >= 0 and sel[-1] < T_cap
