@@ -32,7 +32,8 @@
  *    a workspace or share a context must be ordered by the caller.
  *  - Every entry point except asp_step enqueues kernel launches only (no
  *    memset or copy node, no event), so a sequence of them can be captured
- *    into a HIP graph on one stream and replayed.
+ *    into a HIP graph on one stream and replayed; so can asp_step on one
+ *    stream (it records idx_next_ready when given one).
  *  - Arguments are validated on the host before anything is enqueued; on any
  *    error nothing is enqueued.  Values that live in device memory (seq_lens,
  *    hist_newest, hist_len, idx, n_sel) cannot be checked on the host: the
@@ -358,8 +359,10 @@ asp_status asp_context_destroy(asp_context* ctx);
  *    and is ordered after it through attn_stream.  When the call returns,
  *    `out` is complete in attn_stream's order; the selection and the ring
  *    are complete in sel_stream's order (idx_next_ready).
- * asp_step returns ASP_ERR_UNSUPPORTED when attn_stream or sel_stream is being
- * captured into a graph.
+ * With two streams, asp_step returns ASP_ERR_UNSUPPORTED when attn_stream or
+ * sel_stream is being captured into a graph; the one-stream modes (sel_stream
+ * NULL or attn_stream, and bootstrap) make kernel launches and at most one
+ * event record on attn_stream and may be captured.
  * Bootstrap mode (idx_cur == NULL): everything runs on attn_stream: push,
  * predict, score, select into idx_next, then attention over idx_next; the
  * workspace's hints are reset first, so that this selection keeps every key.

@@ -452,10 +452,11 @@ asp_status asp_step(asp_context* ctx, const asp_dims* dims, const asp_cfg* cfg, 
     if (hipGetDevice(&dev) != hipSuccess) return ASP_ERR_HIP;
     if (dev != ctx->device) return ASP_ERR_INVALID_ARG;  // the context's stream is on another device
   }
-  // The step records events on its launches and forks onto the context's
-  // stream; recording it into a graph is not supported.
-  if (asp::capturing(attn_stream) || (sel_stream != nullptr && asp::capturing(sel_stream)))
-    return ASP_ERR_UNSUPPORTED;
+  // With two streams the step forks onto the context's stream and waits on the
+  // caller's event: recording that into a graph is not supported.  The
+  // one-stream modes make plain launches (and an event record) on one stream
+  // and may be captured.
+  if (two_streams && (asp::capturing(attn_stream) || asp::capturing(sel_stream))) return ASP_ERR_UNSUPPORTED;
   const StepLayout lay = step_layout(s);
   if (ws == nullptr || ws_bytes < lay.total) return ASP_ERR_WORKSPACE;
   unsigned char* base = static_cast<unsigned char*>(ws);

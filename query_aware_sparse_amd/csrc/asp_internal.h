@@ -103,15 +103,20 @@ inline bool capturing(hipStream_t st) {
 
 // Launch that records `done` (nullable) when the kernel completes.  The event
 // rides on the kernel's own completion signal (hipExtLaunchKernelGGL), so it
-// costs no extra queue packet.
+// costs no extra queue packet.  While `st` is being captured into a graph the
+// launch is a plain one followed by an event record, the form stream capture
+// defines.
 template <typename... KArgs, typename... Args>
 hipError_t launch_recording(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t st, hipEvent_t done,
                             Args... args) {
-  if (done != nullptr)
+  if (done != nullptr && !capturing(st)) {
     hipExtLaunchKernelGGL(kernel, grid, block, 0, st, nullptr, done, 0, args...);
-  else
-    hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
-  return hipGetLastError();
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && done != nullptr) e = hipEventRecord(done, st);
+  return e;
 }
 
 // ---------------------------------------------------------------- device helpers

@@ -6,8 +6,10 @@ captured on one stream into a graph.  The graph is replayed several times,
 with eager work (a new query copied into the captured input buffer) and a
 synchronisation between replays; after every replay the attention output,
 the selection and the query ring must equal, bit for bit, the same entry
-points run eagerly on a second copy of the state.  (asp_step itself refuses
-stream capture.)
+points run eagerly on a second copy of the state.  The same holds for
+asp_step in its one-stream pipelined mode (two steps captured, with their
+selection events), while a two-stream asp_step refuses capture with
+ASP_ERR_UNSUPPORTED and enqueues nothing.
 """
 import numpy as np
 import pytest
@@ -139,3 +141,90 @@ def test_captured_page_step_replays_match_eager():
         torch.cuda.synchronize()
         for name in ("idx", "n", "out"):
             np.testing.assert_array_equal(np_(gb[name]), np_(eb[name]), err_msg="replay %d %s" % (rep, name))
+
+
+def _step_state(p: Problem):
+    wl = p.wl
+    B, Hkv, Hq, D, C = wl.batch, wl.n_kv_heads, wl.n_q_heads, wl.head_dim, wl.top_c
+    st = dict(q_hist=p.q_hist.clone(), newest=p.newest.clone(), length=p.length.clone(),
+              idx=[torch.full((B, Hkv, C), -1, dtype=torch.int32, device=DEV) for _ in range(2)],
+              n_sel=[torch.zeros((B, Hkv), dtype=torch.int32, device=DEV) for _ in range(2)],
+              out=torch.zeros((B, Hq, D), dtype=torch.float32, device=DEV),
+              ws=torch.empty(A.asp_workspace_size(p.dims, p.cfg, A.OP_STEP), dtype=torch.uint8, device=DEV),
+              ev=[A.HipEvent(), A.HipEvent()])
+    return st
+
+
+def _asp_step(p: Problem, st, q, cur, stream, bootstrap=False):
+    nxt = 1 - cur
+    A.asp_step(p.dims, p.cfg, q, st["q_hist"], st["newest"], st["length"], p.k, p.v, p.seq_lens,
+               None if bootstrap else st["idx"][cur], None if bootstrap else st["n_sel"][cur], st["idx"][nxt],
+               st["n_sel"][nxt], st["out"], st["ws"], attn_stream=stream, idx_next_ready=st["ev"][nxt])
+
+
+@pytest.mark.parametrize("wl_name", ["g4-recent", "g8-d64-w64"])
+def test_captured_one_stream_asp_step_replays_match_eager(wl_name):
+    # Two one-stream pipelined asp_step calls (selection 1 -> 0 -> 1), with the
+    # events they record, captured once and replayed with new queries; every
+    # replay equals the same calls made eagerly on a second copy of the state.
+    require_gpu()
+    wl = SMALL_STEP_CASES[wl_name]
+    n_rep = 4
+    p = Problem(wl, kv_device=DEV, n_steps=2 * n_rep + 2, lens=STEP_LENS.get(wl_name))
+    p.fill_history()
+    torch.cuda.synchronize()
+    t0 = wl.history_steps
+    gs, es = _step_state(p), _step_state(p)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    q0 = p.queries[t0].to(DEV)
+    for st in (gs, es):  # the bootstrap step, eager on both copies: selection 1
+        _asp_step(p, st, q0, 0, side, bootstrap=True)
+    torch.cuda.synchronize()
+    qa_buf = torch.empty((wl.batch, wl.n_q_heads, wl.head_dim), dtype=torch.float32, device=DEV)
+    qb_buf = torch.empty_like(qa_buf)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        _asp_step(p, gs, qa_buf, 1, side)   # attends selection 1, selects 0
+        _asp_step(p, gs, qb_buf, 0, side)   # attends selection 0, selects 1
+    torch.cuda.synchronize()
+    for rep in range(n_rep):
+        qa, qb = p.queries[t0 + 1 + 2 * rep].to(DEV), p.queries[t0 + 2 + 2 * rep].to(DEV)
+        qa_buf.copy_(qa)
+        qb_buf.copy_(qb)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _asp_step(p, es, qa, 1, side)
+        _asp_step(p, es, qb, 0, side)
+        torch.cuda.synchronize()
+        for name in ("out", "q_hist", "newest", "length"):
+            np.testing.assert_array_equal(np_(gs[name]), np_(es[name]), err_msg="replay %d %s" % (rep, name))
+        for i in (0, 1):
+            np.testing.assert_array_equal(np_(gs["idx"][i]), np_(es["idx"][i]), err_msg="replay %d idx" % rep)
+            np.testing.assert_array_equal(np_(gs["n_sel"][i]), np_(es["n_sel"][i]), err_msg="replay %d n" % rep)
+
+
+def test_two_stream_asp_step_refuses_capture():
+    require_gpu()
+    wl = SMALL_STEP_CASES["g4-recent"]
+    p = Problem(wl, kv_device=DEV, n_steps=3, lens=STEP_LENS.get("g4-recent"))
+    p.fill_history()
+    st = _step_state(p)
+    side, sel = torch.cuda.Stream(), torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    q = p.queries[wl.history_steps].to(DEV)
+    _asp_step(p, st, q, 0, side, bootstrap=True)
+    torch.cuda.synchronize()
+    ctx = A.AspContext()
+    before = np_(st["idx"][0]).copy()
+    g = torch.cuda.CUDAGraph()
+    with pytest.raises(A.AspError) as e:
+        with torch.cuda.graph(g, stream=side):
+            A.asp_step(p.dims, p.cfg, q, st["q_hist"], st["newest"], st["length"], p.k, p.v, p.seq_lens,
+                       st["idx"][1], st["n_sel"][1], st["idx"][0], st["n_sel"][0], st["out"], st["ws"],
+                       attn_stream=side, sel_stream=sel, ctx=ctx, idx_cur_ready=st["ev"][1],
+                       idx_next_ready=st["ev"][0])
+    assert e.value.status == 2  # ASP_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(np_(st["idx"][0]), before)  # nothing ran
