@@ -494,15 +494,18 @@ asp_status asp_step(asp_context* ctx, const asp_dims* dims, const asp_cfg* cfg, 
   // Events recorded by a launch itself cost no extra queue packet.  A wait on
   // an event that has not completed costs the host ~14 us, so the step makes
   // two (pred, scored); idx_cur_ready has usually completed by the time the
-  // layer's next step is issued.
+  // layer's next step is issued.  The attention is issued before those two
+  // waits: when the GPU is idle (the first steps of a run) it then starts
+  // right after the predictor instead of after the host's waits, and the next
+  // step's predictor, queued behind it, is not held back.
   ASP_TRY_HIP(hipStreamWaitEvent(attn_stream, idx_cur_ready, 0));
   ASP_TRY_HIP(asp::launch_predict(s, q_hist, hist_newest, hist_len, q_cur, q_pred, attn_stream, ctx->pred));
+  ASP_TRY_HIP(asp::launch_attend(s, q_cur, k, v, seq_lens, idx_cur, n_sel_cur, out, partials, attn_stream));
   ASP_TRY_HIP(hipStreamWaitEvent(ctx->score, ctx->pred, 0));
   ASP_TRY_HIP(asp::launch_score_candidates(s, q_pred, k, seq_lens, cw, false, ctx->score, ctx->scored));
   ASP_TRY_HIP(hipStreamWaitEvent(sel_stream, ctx->scored, 0));
   ASP_TRY_HIP(asp::launch_select_candidates(s, q_pred, k, seq_lens, cw, idx_next, n_sel_next, hist_newest, hist_len,
                                             sel_stream, idx_next_ready));
-  ASP_TRY_HIP(asp::launch_attend(s, q_cur, k, v, seq_lens, idx_cur, n_sel_cur, out, partials, attn_stream));
   return ASP_OK;
 }
 
