@@ -113,7 +113,7 @@ def ragged_kv():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("W,C", [(16, 2048), (32, 4096), (8, 512)])
+@pytest.mark.parametrize("W,C", [(16, 2048), (32, 4096), (8, 512), (16, 1024)])
 def test_ragged_long_cot_full_size(ragged_kv, W, C):
     wl = wk.RAGGED.replace(window=W, top_c=C, history_steps=W + 4)
     p = Problem(wl, n_steps=3, kv=ragged_kv)
