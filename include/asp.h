@@ -25,9 +25,11 @@
  *    heads h = g*G .. g*G+G-1 share KV head g.
  *  - The library allocates no device memory, keeps no state of its own and
  *    never waits on the host: work is enqueued on the given stream(s) and the
- *    call returns.  The two-stream asp_step needs a caller-owned asp_context
- *    (a stream and two events, made by asp_context_create and released by
- *    asp_context_destroy).  Calls are re-entrant and may run concurrently
+ *    call returns.  The one exception is asp_sparse_decode_static, whose
+ *    scratch is a device array built into the library (its address is looked
+ *    up once per device).  The two-stream asp_step needs a caller-owned
+ *    asp_context (a stream and two events, made by asp_context_create and
+ *    released by asp_context_destroy).  Calls are re-entrant and may run concurrently
  *    from several host threads; two calls that write the same buffers, share
  *    a workspace or share a context must be ordered by the caller.
  *  - Every entry point except asp_step enqueues kernel launches only (no
