@@ -17,15 +17,13 @@
 // v_mfma_f32_16x16x32_bf16 per 32 coordinates, with the keys as the B operand
 // (lane l: key l%16, coordinates 8*(l/16)..+7 of each 32-wide step) and the
 // query heads as rows of the A operand.  Keys arrive with fully coalesced
-// non-temporal 16-byte loads (each wave-wide load covers whole key rows; two
-// 16-key tiles per iteration, and each tile's registers take the next
-// iteration's tile as soon as they are written to LDS, so that loads stay in
-// flight while a wave transposes and multiplies) and are transposed into the
-// MFMA layout through two per-wave, XOR-swizzled LDS slots: loading 64-byte
-// column slices of 16 rows straight into the operand layout costs ~15% of the
-// bandwidth on this part.  Two slots keep the block at 36-40 KiB of LDS, so
-// four blocks (16 waves) share a CU; blocks of 512 keys keep the tail of the
-// launch short.  The
+// non-temporal 16-byte loads (each wave-wide load covers whole key rows; four
+// 16-key tiles in flight per wave) and are transposed into the MFMA layout
+// through two per-wave, XOR-swizzled LDS slots: loading 64-byte column slices
+// of 16 rows straight into the operand layout costs ~15% of the bandwidth on
+// this part.  Two slots instead of one per tile in flight keep the block at
+// 40 KiB of LDS, so four blocks (16 waves) share a CU; blocks of 512 keys keep
+// the tail of the launch short.  The
 // predicted query is fp32; it enters as two bf16 terms, hi = rne(q) and
 // lo = rne(q - hi), so the product keeps ~17 significant bits of q (relative
 // error <= 2^-18 per term) and accumulates in fp32.
@@ -58,7 +56,7 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-constexpr int SCORE_MFMA_U = 2;     // 16-key tiles loaded per wave and iteration
+constexpr int SCORE_MFMA_U = 4;     // 16-key tiles loaded per wave and iteration
 constexpr int SCORE_MFMA_SLOTS = 2;  // LDS transpose slots per wave (double buffer)
 
 // Every wave of a block sees SCORE_KEYS_PER_BLOCK / SCORE_WAVES keys (whole
@@ -170,32 +168,20 @@ __device__ __forceinline__ void score_mfma_block(const float* __restrict__ q_pre
       kept += (uint32_t)__popcll(bal);
     }
   };
-  // Coalesced non-temporal loads: each wave-wide load is RPI whole key rows.
-  // Tile u of the next iteration is loaded into tile u's registers as soon as
-  // they have been written to LDS, so that a wave keeps its loads in flight
-  // while it transposes and multiplies the current tiles.
-  constexpr int STEP = SCORE_WAVES * 16 * U;
-  u32x4 gld[U][NI];
-  auto load_tile = [&](int tb, int u) {
-    if (tb + u * 16 + 16 <= k1) {  // whole tile in range (uniform)
+  for (int base = k0 + wave * 16 * U; base < k1; base += SCORE_WAVES * 16 * U) {
+    // Coalesced non-temporal loads: each wave-wide load is RPI whole key rows.
+    u32x4 gld[U][NI];
 #pragma unroll
-      for (int i = 0; i < NI; ++i)
-        gld[u][i] = __builtin_nontemporal_load(kb + (size_t)(tb + u * 16 + RPI * i + lrow) * CH + lchunk);
-    } else {
+    for (int u = 0; u < U; ++u) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        const int key = tb + u * 16 + RPI * i + lrow;
+        const int key = base + u * 16 + RPI * i + lrow;
         gld[u][i] = key < k1 ? __builtin_nontemporal_load(kb + (size_t)key * CH + lchunk) : u32x4{0u, 0u, 0u, 0u};
       }
     }
-  };
-  const int base0 = k0 + wave * 16 * U;
-  if (base0 < k1) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) load_tile(base0, u);
-  }
-  for (int base = base0; base < k1; base += STEP) {
-    const bool more = base + STEP < k1;  // uniform
+    if constexpr (OUT != OUT_SCORES) {
+      if (pend_base >= 0) keep_pending();
+    }
     // Transpose through LDS, one 16-key tile at a time through two slots:
     // tile u+1 is written while the MFMAs read tile u.  Chunk q of tile row r
     // is stored at q ^ (r % CH), which keeps both the row-wise writes and the
@@ -206,12 +192,8 @@ __device__ __forceinline__ void score_mfma_block(const float* __restrict__ q_pre
         const int r = RPI * i + lrow;
         tile[wave][u % TB][r][lchunk ^ (r % CH)] = gld[u][i];
       }
-      if (more) load_tile(base + STEP, u);
     };
     put(0);
-    if constexpr (OUT != OUT_SCORES) {
-      if (pend_base >= 0) keep_pending();
-    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
