@@ -219,6 +219,37 @@ asp_status asp_selection_overlap(const asp_dims* dims, const asp_cfg* cfg, const
                                  const int32_t* n_sel_a, const int32_t* idx_b, const int32_t* n_sel_b,
                                  int32_t* overlap, hipStream_t stream);
 
+/* Check of the arguments that live in device memory, which the host-side
+ * validation cannot see (no passage of the pages: part of this interface's
+ * error convention).  The other entry points clamp such values (see the
+ * conventions above); this call reports whether they are what the library's
+ * own producers leave.  It enqueues a clear of *status and one check launch
+ * (kernel launches only, so it may be captured), reads its inputs only, and
+ * ORs into *status (one uint32 in device memory, 4-byte aligned) the bits of
+ * every violated condition, 0 when all hold:
+ *   ASP_CHECK_SEQ_LEN      seq_lens[b] outside [0, t_cap];
+ *   ASP_CHECK_HIST_LEN     hist_len[b] outside [0, window];
+ *   ASP_CHECK_HIST_NEWEST  hist_len[b] > 0 and hist_newest[b] outside [0, window);
+ *   ASP_CHECK_N_SEL        n_sel[b][g] outside [0, min(top_c, seq_lens[b])];
+ *   ASP_CHECK_IDX          an entry idx[b][g][j], j < n_sel[b][g] (clamped to
+ *                          [0, top_c]), outside [0, seq_lens[b]) or not below
+ *                          the next such entry (the list is strictly ascending);
+ *   ASP_CHECK_IDX_PAD      an entry at or beyond n_sel[b][g] that is not -1
+ *                          (no entry point reads those entries).
+ * seq_lens[B] int32 is required; hist_newest/hist_len ([B] int32) and
+ * idx/n_sel ([B][Hkv][top_c], [B][Hkv] int32) are optional pairs (both NULL
+ * skips those checks; one of a pair NULL is ASP_ERR_INVALID_ARG).  The status
+ * word is valid once the stream reaches the end of the call's work. */
+#define ASP_CHECK_SEQ_LEN 0x01u
+#define ASP_CHECK_HIST_LEN 0x02u
+#define ASP_CHECK_HIST_NEWEST 0x04u
+#define ASP_CHECK_N_SEL 0x08u
+#define ASP_CHECK_IDX 0x10u
+#define ASP_CHECK_IDX_PAD 0x20u
+asp_status asp_check_device_args(const asp_dims* dims, const asp_cfg* cfg, const int32_t* seq_lens,
+                                 const int32_t* hist_newest, const int32_t* hist_len, const int32_t* idx,
+                                 const int32_t* n_sel, uint32_t* status, hipStream_t stream);
+
 /* Sparse decode attention over the selected tokens ([card] "Layout" and "Key
  * finding": attention over the top-C tokens only).  For every (b, h), with
  * g = h / G, n = n_sel[b][g] clamped to [0, C], T = seq_lens[b] clamped to

@@ -22,7 +22,8 @@ __all__ = [
     "asp_workspace_size", "asp_status_string", "asp_push_query", "asp_predict_query", "asp_score_keys",
     "asp_select_topc", "asp_score_candidates", "asp_select_candidates", "asp_sparse_decode", "asp_step",
     "asp_selection_overlap", "AspContext", "CTX_SCORE_ALL_CUS", "PreparedStep", "asp_sparse_decode_static",
-    "STATIC_SCRATCH_BYTES",
+    "STATIC_SCRATCH_BYTES", "asp_check_device_args", "CHECK_SEQ_LEN", "CHECK_HIST_LEN", "CHECK_HIST_NEWEST",
+    "CHECK_N_SEL", "CHECK_IDX", "CHECK_IDX_PAD",
     "asp_page_summary_size", "asp_page_summary", "asp_page_scores", "asp_page_select_workspace_size",
     "asp_page_select", "page_count",
 ]
@@ -35,6 +36,8 @@ KV_BF16, KV_F32 = 0, 1
 HIST_BINS = 2048  # bins of the coarse score histograms (ASP_HIST_BINS)
 CTX_SCORE_ALL_CUS = 1  # asp_context_create flag: the score stream may use every CU
 STATIC_SCRATCH_BYTES = 8 << 20  # built-in scratch of asp_sparse_decode_static (ASP_STATIC_SCRATCH_BYTES)
+# asp_check_device_args status bits (ASP_CHECK_*)
+CHECK_SEQ_LEN, CHECK_HIST_LEN, CHECK_HIST_NEWEST, CHECK_N_SEL, CHECK_IDX, CHECK_IDX_PAD = 1, 2, 4, 8, 16, 32
 _STATUS_NAMES = {0: "ASP_OK", 1: "ASP_ERR_INVALID_ARG", 2: "ASP_ERR_UNSUPPORTED", 3: "ASP_ERR_WORKSPACE",
                  4: "ASP_ERR_HIP", 5: "ASP_ERR_HOST_MEMORY", 6: "ASP_ERR_SCRATCH"}
 
@@ -93,6 +96,7 @@ def load():
     lib.asp_sparse_decode_static.argtypes = [D, C, P, P, P, P, P, P, P, P]
     lib.asp_step.argtypes = [P, D, C, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P, P, P, P]
     lib.asp_selection_overlap.argtypes = [D, C, P, P, P, P, P, P]
+    lib.asp_check_device_args.argtypes = [D, C, P, P, P, P, P, P, P]
     lib.asp_context_create.argtypes = [ctypes.c_int32, ctypes.c_uint32, ctypes.POINTER(ctypes.c_void_p)]
     lib.asp_context_destroy.argtypes = [P]
     I32 = ctypes.c_int32
@@ -294,6 +298,25 @@ def asp_selection_overlap(dims: Dims, cfg: Cfg, idx_a, n_sel_a, idx_b, n_sel_b, 
     _raise("asp_selection_overlap", load().asp_selection_overlap(ctypes.byref(dims), ctypes.byref(cfg), _ptr(idx_a),
                                                                  _ptr(n_sel_a), _ptr(idx_b), _ptr(n_sel_b),
                                                                  _ptr(overlap), _stream_handle(stream)))
+
+
+def asp_check_device_args(dims: Dims, cfg: Cfg, seq_lens, status, hist_newest=None, hist_len=None, idx=None,
+                          n_sel=None, stream=None) -> None:
+    """status: a one-element int32 tensor on the device; after the stream has run the
+    call it holds the OR of the CHECK_* bits of the violated conditions (0: none)."""
+    B, Hkv, C = dims.batch, dims.n_kv_heads, cfg.top_c
+    _check(seq_lens, "seq_lens", (B,), torch.int32)
+    _check(status, "status", (1,), torch.int32)
+    if hist_newest is not None or hist_len is not None:
+        _check(hist_newest, "hist_newest", (B,), torch.int32)
+        _check(hist_len, "hist_len", (B,), torch.int32)
+    if idx is not None or n_sel is not None:
+        _check(idx, "idx", (B, Hkv, C), torch.int32)
+        _check(n_sel, "n_sel", (B, Hkv), torch.int32)
+    _raise("asp_check_device_args", load().asp_check_device_args(ctypes.byref(dims), ctypes.byref(cfg),
+                                                                 _ptr(seq_lens), _ptr(hist_newest), _ptr(hist_len),
+                                                                 _ptr(idx), _ptr(n_sel), _ptr(status),
+                                                                 _stream_handle(stream)))
 
 
 def asp_sparse_decode(dims: Dims, cfg: Cfg, q, k, v, seq_lens, idx, n_sel, out, ws, stream=None) -> None:

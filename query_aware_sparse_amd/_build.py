@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libasp.so")
-SOURCES = ["api.hip", "predict.hip", "score.hip", "select.hip", "attend.hip", "overlap.hip", "page.hip"]
+SOURCES = ["api.hip", "predict.hip", "score.hip", "select.hip", "attend.hip", "overlap.hip", "page.hip",
+           "check.hip"]
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

@@ -315,6 +315,21 @@ asp_status asp_selection_overlap(const asp_dims* dims, const asp_cfg* cfg, const
   return hip_status(asp::launch_overlap(s, idx_a, n_sel_a, idx_b, n_sel_b, overlap, stream));
 }
 
+asp_status asp_check_device_args(const asp_dims* dims, const asp_cfg* cfg, const int32_t* seq_lens,
+                                 const int32_t* hist_newest, const int32_t* hist_len, const int32_t* idx,
+                                 const int32_t* n_sel, uint32_t* status, hipStream_t stream) {
+  Shape s;
+  asp_status st = check_all(dims, cfg, &s);
+  if (st != ASP_OK) return st;
+  if (!seq_lens || !status) return ASP_ERR_INVALID_ARG;
+  if ((hist_newest == nullptr) != (hist_len == nullptr) || (idx == nullptr) != (n_sel == nullptr))
+    return ASP_ERR_INVALID_ARG;
+  if (!aligned4(seq_lens) || !aligned4(status) || !aligned4(hist_newest) || !aligned4(hist_len) || !aligned4(idx) ||
+      !aligned4(n_sel))
+    return ASP_ERR_INVALID_ARG;
+  return hip_status(asp::launch_check(s, seq_lens, hist_newest, hist_len, idx, n_sel, status, stream));
+}
+
 asp_status asp_sparse_decode(const asp_dims* dims, const asp_cfg* cfg, const float* q, const void* k, const void* v,
                              const int32_t* seq_lens, const int32_t* idx, const int32_t* n_sel, float* out, void* ws,
                              size_t ws_bytes, hipStream_t stream) {

@@ -81,6 +81,9 @@ hipError_t launch_score_candidates(const Shape& s, const float* q_pred, const vo
 hipError_t launch_select_candidates(const Shape& s, const float* q_pred, const void* k, const int32_t* seq_lens,
                                     const CandWs& cw, int32_t* idx, int32_t* n_sel, int32_t* adv_newest,
                                     int32_t* adv_len, hipStream_t st, hipEvent_t done = nullptr);
+// Device-argument check (check.hip): clears *status, then ORs ASP_CHECK_* bits into it.
+hipError_t launch_check(const Shape& s, const int32_t* seq_lens, const int32_t* hist_newest, const int32_t* hist_len,
+                        const int32_t* idx, const int32_t* n_sel, uint32_t* status, hipStream_t st);
 // Per unit, the number of indices that two ascending selections share
 // (s.C <= overlap_max_c()).
 int overlap_max_c();

@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
         "asp_workspace_size", "asp_status_string", "asp_push_query", "asp_predict_query", "asp_score_keys",
         "asp_select_topc", "asp_score_candidates", "asp_select_candidates", "asp_sparse_decode", "asp_step",
         "asp_selection_overlap", "asp_context_create", "asp_context_destroy", "asp_sparse_decode_static",
-        "asp_page_summary_size",
+        "asp_check_device_args", "asp_page_summary_size",
         "asp_page_summary",
         "asp_page_scores", "asp_page_select_workspace_size", "asp_page_select"])
 
@@ -177,6 +177,26 @@ def test_null_pointers_and_short_workspace_rejected(lib):
     args[0] = ctypes.c_void_p(64)  # a context (never dereferenced before the event check)
     assert lib.asp_step(*args, one, one, one, one, one, one, 1 << 40, ctypes.c_void_p(1), ctypes.c_void_p(2),
                         None, None) == 1
+
+
+def test_device_argument_check_rejects_bad_host_arguments(lib):
+    # rejected on the host before any HIP call
+    d, c = _dims(), A.Cfg(16, 2048, 1e-2)
+    one, odd = ctypes.c_void_p(16), ctypes.c_void_p(18)
+    chk = lib.asp_check_device_args
+    assert chk(ctypes.byref(d), ctypes.byref(c), None, None, None, None, None, one, None) == 1  # no seq_lens
+    assert chk(ctypes.byref(d), ctypes.byref(c), one, None, None, None, None, None, None) == 1  # no status
+    assert chk(ctypes.byref(d), ctypes.byref(c), one, one, None, None, None, one, None) == 1  # half a ring
+    assert chk(ctypes.byref(d), ctypes.byref(c), one, None, None, None, one, one, None) == 1  # half a selection
+    assert chk(ctypes.byref(d), ctypes.byref(c), one, None, None, None, None, odd, None) == 1  # misaligned status
+    assert chk(ctypes.byref(d), ctypes.byref(A.Cfg(6, 64, 1e-2)), one, None, None, None, None, one, None) == 1
+    assert chk(None, ctypes.byref(c), one, None, None, None, None, one, None) == 1
+    assert (A.CHECK_SEQ_LEN, A.CHECK_HIST_LEN, A.CHECK_HIST_NEWEST, A.CHECK_N_SEL, A.CHECK_IDX,
+            A.CHECK_IDX_PAD) == (1, 2, 4, 8, 16, 32)
+    text = open(HEADER).read()
+    for name, bit in (("SEQ_LEN", 1), ("HIST_LEN", 2), ("HIST_NEWEST", 4), ("N_SEL", 8), ("IDX", 16),
+                      ("IDX_PAD", 32)):
+        assert re.search(r"#define ASP_CHECK_%s 0x%02xu" % (name, bit), text), name
 
 
 def test_page_sizes_and_argument_checks(lib):
