@@ -78,6 +78,7 @@ enum class Mode { one_stream, two_streams };
 struct Layer {
   float *q_hist = nullptr, *out = nullptr, *q = nullptr;
   int32_t *newest = nullptr, *len = nullptr, *idx[2] = {}, *nsel[2] = {};
+  uint32_t* status = nullptr;  // asp_check_device_args' word
   void* ws = nullptr;
   size_t ws_bytes = 0;
   hipStream_t attn = nullptr, sel = nullptr;
@@ -93,6 +94,7 @@ struct Layer {
     CHECK_HIP(hipMalloc((void**)&q, q_n * 4));
     CHECK_HIP(hipMalloc((void**)&newest, B * 4));
     CHECK_HIP(hipMalloc((void**)&len, B * 4));
+    CHECK_HIP(hipMalloc((void**)&status, 4));
     for (int i = 0; i < 2; ++i) {
       CHECK_HIP(hipMalloc((void**)&idx[i], (size_t)B * Hkv * C * 4));
       CHECK_HIP(hipMalloc((void**)&nsel[i], (size_t)B * Hkv * 4));
@@ -110,8 +112,18 @@ struct Layer {
     return 0;
   }
 
-  int snapshot(int buf) {
+  // Also checks that the lengths, the ring and the selection just written are
+  // what the library's producers leave (no asp_check_device_args bit set).
+  int snapshot(int buf, const int32_t* lens) {
     const int B = kDims.batch, Hq = kDims.n_q_heads, Hkv = kDims.n_kv_heads, D = kDims.head_dim;
+    CHECK_ASP(asp_check_device_args(&kDims, &kCfg, lens, newest, len, idx[buf], nsel[buf], status, attn));
+    uint32_t bits = 0;
+    CHECK_HIP(hipMemcpyAsync(&bits, status, 4, hipMemcpyDeviceToHost, attn));
+    CHECK_HIP(hipStreamSynchronize(attn));
+    if (bits != 0u) {
+      std::fprintf(stderr, "asp_check_device_args reported 0x%x\n", bits);
+      return 5;
+    }
     Snapshot s;
     s.out.resize((size_t)B * Hq * D);
     s.ring.resize((size_t)B * Hq * kCfg.window * D);
@@ -145,7 +157,7 @@ struct Layer {
     CHECK_ASP(asp_step(nullptr, &kDims, &kCfg, q, q_hist, newest, len, in.k, in.v, in.lens, nullptr, nullptr,
                        idx[0], nsel[0], out, ws, ws_bytes, attn, nullptr, nullptr, ev[0]));
     if (int rc = sync()) return rc;
-    if (int rc = snapshot(0)) return rc;
+    if (int rc = snapshot(0, in.lens)) return rc;
     for (int s = 0; s < kSteps; ++s) {
       const int cur = s % 2, nxt = 1 - cur;
       CHECK_HIP(hipMemcpyAsync(q, in.qs.data() + (size_t)(W + s) * q_n, q_n * 4, hipMemcpyHostToDevice, attn));
@@ -156,7 +168,7 @@ struct Layer {
         CHECK_ASP(asp_step(ctx, &kDims, &kCfg, q, q_hist, newest, len, in.k, in.v, in.lens, idx[cur], nsel[cur],
                            idx[nxt], nsel[nxt], out, ws, ws_bytes, attn, sel, ev[cur], ev[nxt]));
       if (int rc = sync()) return rc;
-      if (int rc = snapshot(nxt)) return rc;
+      if (int rc = snapshot(nxt, in.lens)) return rc;
     }
     return 0;
   }
