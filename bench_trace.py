@@ -7,8 +7,13 @@ on the machine that took them).
       bench_hold kernel to 1 ms after the last step score launch, which runs
       on a queue other than the held attention stream) and those of the
       per-entry-point timing loops after them (calls, average, median, min,
-      max in us); and, on the score launches' queue, the median period and
-      the median gap between consecutive step score launches.
+      max in us); on the score launches' queue, the median period and the
+      median gap between consecutive step score launches, the median time
+      from the end of each score launch's own predictor launch to its start
+      and the share of score launches whose predictor ended after the
+      previous score launch; on the attention queue, the median chain of a step (predictor
+      start to the end of the step's last launch there) and the median idle
+      time before each predictor launch.
   python3 bench_trace.py pmc DIR COUNTER OUT.json
       DIR holds a --pmc COUNTER run: per kernel, the dispatches and the
       median counter value per dispatch (KiB for FETCH_SIZE / WRITE_SIZE).
@@ -56,6 +61,29 @@ def trace(d: str, out: str) -> None:
         res["score_queue"] = {"step_score_launches": len(sl),
                               "period_median_us": round(st.median(periods), 2) if periods else None,
                               "gap_median_us": round(st.median(gaps), 2) if gaps else None}
+        # What each step score launch waited for: its own predictor launch
+        # (the i-th of the timed steps on the attention queue; score launch i
+        # uses prediction i) or the previous score launch.
+        preds = [k for k in ks if "predict_kernel" in k[2] and k[3] == attn_q and h_end <= k[0] <= hi]
+        after_pred, pred_last = [], 0
+        for i in range(1, min(len(sl), len(preds))):
+            after_pred.append((sl[i][0] - preds[i][1]) / 1000)
+            pred_last += preds[i][1] > sl[i - 1][1]
+        aq = [k for k in ks if k[3] == attn_q and h_end <= k[0] <= hi and "hold_kernel" not in k[2]]
+        idle, chain = [], []
+        for j, k in enumerate(aq):
+            if "predict_kernel" not in k[2]:
+                continue
+            if j > 0:
+                idle.append((k[0] - aq[j - 1][1]) / 1000)
+            nxt = next((m for m in range(j + 1, len(aq)) if "predict_kernel" in aq[m][2]), len(aq))
+            chain.append((aq[nxt - 1][1] - k[0]) / 1000)
+        if after_pred:
+            res["score_queue"]["pred_end_to_score_start_median_us"] = round(st.median(after_pred), 2)
+            res["score_queue"]["pred_ended_after_previous_score"] = round(pred_last / len(after_pred), 3)
+        if chain:
+            res["attn_queue"] = {"chain_median_us": round(st.median(chain), 2),
+                                 "idle_before_predictor_median_us": round(st.median(idle), 2) if idle else None}
         res["in_step"] = {n: _stats(v) for n, v in in_step.items()}
         res["standalone"] = {n: _stats(v) for n, v in rest.items()}
     allk = defaultdict(list)
