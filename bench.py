@@ -122,23 +122,42 @@ def in_step_score_launch_us():
     return rec.get("score_candidates_avg_us")
 
 
+# Keys per oracle sample: about the Qwen3-8B layer (64 units x 32768 keys); at
+# least two units per thread of a 16-core host, so that the sample keeps every
+# thread busy as the whole layer does.
+CPU_SAMPLE_KEYS = 64 * 32768
+CPU_SAMPLE_MIN_UNITS = 32
+
+
 def cpu_baseline(wl, layer, q_t) -> dict:
     """The oracle (fp64, plain) timed on the host cores for one full step of one
-    layer (all units), on inputs copied back from the device."""
+    layer (all units), on inputs copied back from the device.  A layer with
+    many more keys than the Qwen3-8B layer (the ragged long-CoT batch) is
+    timed on its first sequences (at least CPU_SAMPLE_MIN_UNITS units, more
+    while the sample stays within CPU_SAMPLE_KEYS keys), and the step time is
+    scaled by the keys the whole layer scans."""
     import numpy as np
     import torch
     import oracle
 
-    k, v = layer["k"], layer["v"]
+    lens_all = layer["seq_lens"].cpu().numpy()
+    per_seq = wl.n_kv_heads * np.maximum(lens_all, 0).astype(np.int64)
+    nb, acc = 0, 0
+    min_seqs = -(-CPU_SAMPLE_MIN_UNITS // wl.n_kv_heads)
+    while nb < wl.batch and (nb < min_seqs or acc + per_seq[nb] <= CPU_SAMPLE_KEYS):
+        acc += per_seq[nb]
+        nb += 1
+    scale = float(per_seq.sum()) / float(per_seq[:nb].sum()) if nb < wl.batch else 1.0
+    k, v = layer["k"][:nb], layer["v"][:nb]
     kn = k.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
     vn = v.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
-    lens = layer["seq_lens"].cpu().numpy()
-    hist = layer["q_hist"].cpu().numpy()
-    newest = layer["newest"].cpu().numpy()
-    length = layer["length"].cpu().numpy()
-    q = q_t.cpu().numpy()
-    idx_prev = layer["idx"][layer["cur"]].cpu().numpy()
-    n_prev = layer["nsel"][layer["cur"]].cpu().numpy()
+    lens = lens_all[:nb].copy()
+    hist = layer["q_hist"][:nb].cpu().numpy()
+    newest = layer["newest"][:nb].cpu().numpy()
+    length = layer["length"][:nb].cpu().numpy()
+    q = q_t[:nb].cpu().numpy()
+    idx_prev = layer["idx"][layer["cur"]][:nb].cpu().numpy()
+    n_prev = layer["nsel"][layer["cur"]][:nb].cpu().numpy()
 
     def one_step():
         o = oracle.attend(q, kn, vn, idx_prev, n_prev)
@@ -156,10 +175,16 @@ def cpu_baseline(wl, layer, q_t) -> dict:
         el = time.perf_counter() - t0
         if (reps >= 3 and el >= 10.0) or el > 30.0:  # a bounded sample of ~10 s of CPU work
             break
-    per_step = el / reps
+    per_step = el / reps * scale
+    if nb == wl.batch:
+        what = "full step of one layer (all %d units)" % (wl.batch * wl.n_kv_heads)
+    else:
+        what = ("step of the first %d of %d sequences (%d of %d units, %d of %d keys), scaled by the keys "
+                "(x%.2f)" % (nb, wl.batch, nb * wl.n_kv_heads, wl.batch * wl.n_kv_heads, int(per_seq[:nb].sum()),
+                             int(per_seq.sum()), scale))
     return {"value": 1.0 / per_step, "unit": "steps/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "full step of one layer (all %d units), %d timed repetitions (%.1f s) after 1 warm-up, "
-                      "%.3f s each" % (wl.batch * wl.n_kv_heads, reps, el, per_step),
+            "sample": "%s, %d timed repetitions (%.1f s) after 1 warm-up, %.3f s per full step"
+                      % (what, reps, el, per_step),
             "host": host_cpu()}
 
 
