@@ -134,9 +134,11 @@ def make_kv(wl: Workload, seq_lens: torch.Tensor, layer: int = 0, device="cpu"):
         tb = int(lens[b])
         nh = heavy_count(wl, tb)
         if nh > 0:
-            gh = _gen(device, wl.seed, layer, _TAG_HEAVY, b)
+            # heavy rows drawn on the host (a permutation there needs no
+            # device sort) and scaled where the cache lives
+            gh = _gen("cpu", wl.seed, layer, _TAG_HEAVY, b)
             for g in range(Hkv):
-                pos = torch.randperm(tb, generator=gh, device=device)[:nh]
+                pos = torch.randperm(tb, generator=gh)[:nh].to(device)
                 kb[g, pos, :] *= wl.heavy_factor
         k[b].copy_(kb.to(dt))
         v[b].copy_(vb.to(dt))
