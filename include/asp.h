@@ -28,14 +28,14 @@
  *    call returns.  The one exception is asp_sparse_decode_static, whose
  *    scratch is a device array built into the library (its address is looked
  *    up once per device).  The two-stream asp_step needs a caller-owned
- *    asp_context (a stream and two events, made by asp_context_create and
+ *    asp_context (a stream and three events, made by asp_context_create and
  *    released by asp_context_destroy).  Calls are re-entrant and may run concurrently
  *    from several host threads; two calls that write the same buffers, share
  *    a workspace or share a context must be ordered by the caller.
- *  - Every entry point except asp_step enqueues kernel launches only (no
- *    memset or copy node, no event), so a sequence of them can be captured
- *    into a HIP graph on one stream and replayed; so can asp_step on one
- *    stream (it records idx_next_ready when given one).
+ *  - Every entry point except asp_step and asp_context_join enqueues kernel
+ *    launches only (no memset or copy node, no event), so a sequence of them
+ *    can be captured into a HIP graph on one stream and replayed; so can
+ *    asp_step, on one stream or on two under the rules given with it.
  *  - Arguments are validated on the host before anything is enqueued; on any
  *    error nothing is enqueued.  Values that live in device memory (seq_lens,
  *    hist_newest, hist_len, idx, n_sel) cannot be checked on the host: the
@@ -334,7 +334,7 @@ asp_status asp_page_select(const asp_dims* dims, const asp_cfg* cfg, int32_t pag
 /* Caller-owned state of the two-stream asp_step ([abstract], second
  * component; [summary] "Approach": selection runs beside the decoding loop):
  * one HIP stream (default priority) on which the score passes of successive
- * steps run back to back, and two events that order it with the caller's
+ * steps run back to back, and three events that order it with the caller's
  * streams.
  * asp_context_create makes one on `device` (0 <= device < the device count,
  * else ASP_ERR_INVALID_ARG) and stores it in *ctx (NULL on failure).  flags:
@@ -355,11 +355,18 @@ asp_status asp_page_select(const asp_dims* dims, const asp_cfg* cfg, int32_t pag
  * asp_context_destroy waits for the context's stream to drain, then releases
  * the stream and the events (NULL is a no-op); ASP_ERR_HIP if a HIP call
  * failed (the rest is still released).  Returns ASP_ERR_HOST_MEMORY when the
- * host allocation fails, ASP_ERR_HIP when a stream or event cannot be made. */
+ * host allocation fails, ASP_ERR_HIP when a stream or event cannot be made.
+ * asp_context_join makes `stream` wait for every score pass enqueued on the
+ * context so far (an event recorded on the context's stream, waited on by
+ * `stream`; it enqueues nothing else).  A graph capture that contains
+ * two-stream asp_step calls must, before it ends, join the context's stream
+ * (this call, after the last such step) and the caller's sel_stream back into
+ * the capture's origin stream.  ASP_ERR_INVALID_ARG for a NULL ctx. */
 typedef struct asp_context_s asp_context;
 #define ASP_CTX_SCORE_ALL_CUS 1u
 asp_status asp_context_create(int32_t device, uint32_t flags, asp_context** ctx);
 asp_status asp_context_destroy(asp_context* ctx);
+asp_status asp_context_join(asp_context* ctx, hipStream_t stream);
 
 /* One decode step of one layer ([abstract], second component; [summary]
  * "Approach": selection for the next step is taken off the decode critical
@@ -375,8 +382,9 @@ asp_status asp_context_destroy(asp_context* ctx);
  *    attn_stream (attention first); ctx and idx_cur_ready are ignored (may be
  *    NULL); idx_next_ready, when not NULL, is recorded when the selection is
  *    written.
- *  - otherwise (two streams): ctx (a context made on the current device) and
- *    idx_cur_ready are required, else ASP_ERR_INVALID_ARG.
+ *  - otherwise (two streams): ctx (a context made on the current device) is
+ *    required, and idx_cur_ready too unless attn_stream is being captured,
+ *    else ASP_ERR_INVALID_ARG.
  *      attn_stream waits for idx_cur_ready, then pushes q_cur into the ring
  *      and predicts the next query, then runs the attention over idx_cur and
  *      its merge;
@@ -392,10 +400,17 @@ asp_status asp_context_destroy(asp_context* ctx);
  *    and is ordered after it through attn_stream.  When the call returns,
  *    `out` is complete in attn_stream's order; the selection and the ring
  *    are complete in sel_stream's order (idx_next_ready).
- * With two streams, asp_step returns ASP_ERR_UNSUPPORTED when attn_stream or
- * sel_stream is being captured into a graph; the one-stream modes (sel_stream
- * NULL or attn_stream, and bootstrap) make kernel launches and at most one
- * event record on attn_stream and may be captured.
+ * Graph capture: every mode may be captured with attn_stream as the origin
+ * (the one-stream modes make kernel launches and at most one event record on
+ * attn_stream).  With two streams, the call forks the context's stream and
+ * sel_stream off attn_stream inside the capture, so sel_stream must not be
+ * capturing into another graph (ASP_ERR_UNSUPPORTED), idx_cur_ready must be
+ * NULL or an event recorded earlier in the same capture (a wait on an event
+ * recorded outside it is refused by HIP), and the capture must end with
+ * both forked streams joined back into attn_stream (asp_context_join, and a
+ * wait on an event recorded on sel_stream).  With idx_cur_ready NULL, the
+ * caller orders the step after the selection it reads (graphs replayed on one
+ * stream run one after the other).
  * Bootstrap mode (idx_cur == NULL): everything runs on attn_stream: push,
  * predict, score, select into idx_next, then attention over idx_next; the
  * workspace's hints are reset first, so that this selection keeps every key.

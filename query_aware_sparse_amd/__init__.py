@@ -99,6 +99,7 @@ def load():
     lib.asp_check_device_args.argtypes = [D, C, P, P, P, P, P, P, P]
     lib.asp_context_create.argtypes = [ctypes.c_int32, ctypes.c_uint32, ctypes.POINTER(ctypes.c_void_p)]
     lib.asp_context_destroy.argtypes = [P]
+    lib.asp_context_join.argtypes = [P, P]
     I32 = ctypes.c_int32
     lib.asp_page_summary_size.argtypes = [D, I32]
     lib.asp_page_summary_size.restype = SZ
@@ -109,7 +110,8 @@ def load():
     lib.asp_page_select.argtypes = [D, C, I32, P, P, P, P, P, P, P, SZ, P]
     for name in ("asp_push_query", "asp_predict_query", "asp_score_keys", "asp_select_topc",
                  "asp_score_candidates", "asp_select_candidates", "asp_sparse_decode", "asp_step",
-                 "asp_selection_overlap", "asp_context_create", "asp_context_destroy", "asp_sparse_decode_static"):
+                 "asp_selection_overlap", "asp_context_create", "asp_context_destroy", "asp_sparse_decode_static",
+                 "asp_context_join", "asp_check_device_args"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -381,6 +383,12 @@ class AspContext:
         if self._finalizer.alive:
             status = self._finalizer()
             _raise("asp_context_destroy", status)
+
+    def join(self, stream) -> None:
+        """asp_context_join: `stream` waits for every score pass enqueued on the
+        context so far (under graph capture, the join a capture with two-stream
+        steps needs before it ends)."""
+        _raise("asp_context_join", load().asp_context_join(self.handle, _stream_handle(stream)))
 
 
 def _step_args(ctx, dims, cfg, q_cur, q_hist, hist_newest, hist_len, k, v, seq_lens, idx_cur, n_sel_cur, idx_next,

@@ -119,6 +119,7 @@ struct asp_context_s {
   hipStream_t score;    // score passes of successive calls run back to back here
   hipEvent_t pred;      // recorded by the predictor launch (q_pred and the ring slot written)
   hipEvent_t scored;    // recorded by the score launch (candidates kept)
+  hipEvent_t joined;    // recorded by asp_context_join on the score stream
 };
 
 namespace {
@@ -150,6 +151,7 @@ void context_release(asp_context* c) {
   }
   if (c->pred) (void)hipEventDestroy(c->pred);
   if (c->scored) (void)hipEventDestroy(c->scored);
+  if (c->joined) (void)hipEventDestroy(c->joined);
   delete c;
 }
 
@@ -418,13 +420,14 @@ asp_status asp_context_create(int32_t device, uint32_t flags, asp_context** ctx)
   int n = 0, cur = 0;
   if (hipGetDeviceCount(&n) != hipSuccess || hipGetDevice(&cur) != hipSuccess) return ASP_ERR_HIP;
   if (device < 0 || device >= n) return ASP_ERR_INVALID_ARG;
-  asp_context* c = new (std::nothrow) asp_context{device, flags, nullptr, nullptr, nullptr};
+  asp_context* c = new (std::nothrow) asp_context{device, flags, nullptr, nullptr, nullptr, nullptr};
   if (c == nullptr) return ASP_ERR_HOST_MEMORY;
   hipError_t e = cur == device ? hipSuccess : hipSetDevice(device);
   if (e == hipSuccess) e = create_score_stream(device, (flags & ASP_CTX_SCORE_ALL_CUS) == 0, &c->score);
   const unsigned ev_flags = hipEventDisableTiming | hipEventDisableSystemFence;
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->pred, ev_flags);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->scored, ev_flags);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->joined, ev_flags);
   if (cur != device) (void)hipSetDevice(cur);
   if (e != hipSuccess) {
     context_release(c);
@@ -440,8 +443,16 @@ asp_status asp_context_destroy(asp_context* ctx) {
   ok &= hipStreamDestroy(ctx->score) == hipSuccess;
   ok &= hipEventDestroy(ctx->pred) == hipSuccess;
   ok &= hipEventDestroy(ctx->scored) == hipSuccess;
+  ok &= hipEventDestroy(ctx->joined) == hipSuccess;
   delete ctx;
   return ok ? ASP_OK : ASP_ERR_HIP;
+}
+
+asp_status asp_context_join(asp_context* ctx, hipStream_t stream) {
+  if (ctx == nullptr) return ASP_ERR_INVALID_ARG;
+  ASP_TRY_HIP(hipEventRecord(ctx->joined, ctx->score));
+  ASP_TRY_HIP(hipStreamWaitEvent(stream, ctx->joined, 0));
+  return ASP_OK;
 }
 
 asp_status asp_step(asp_context* ctx, const asp_dims* dims, const asp_cfg* cfg, const float* q_cur, float* q_hist,
@@ -462,16 +473,18 @@ asp_status asp_step(asp_context* ctx, const asp_dims* dims, const asp_cfg* cfg, 
   const bool pipelined = idx_cur != nullptr;
   const bool two_streams = pipelined && sel_stream != nullptr && sel_stream != attn_stream;
   if (two_streams) {
-    if (ctx == nullptr || idx_cur_ready == nullptr) return ASP_ERR_INVALID_ARG;
+    // Under capture the caller may order the step itself (no idx_cur_ready).
+    if (ctx == nullptr) return ASP_ERR_INVALID_ARG;
+    if (idx_cur_ready == nullptr && !asp::capturing(attn_stream)) return ASP_ERR_INVALID_ARG;
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return ASP_ERR_HIP;
     if (dev != ctx->device) return ASP_ERR_INVALID_ARG;  // the context's stream is on another device
+    // Under capture the context's stream and sel_stream join the capture of
+    // attn_stream through the step's own events; sel_stream must not be
+    // capturing into another graph (or into one while attn_stream is not).
+    const unsigned long long sel_cap = asp::capture_id(sel_stream);
+    if (sel_cap != 0 && sel_cap != asp::capture_id(attn_stream)) return ASP_ERR_UNSUPPORTED;
   }
-  // With two streams the step forks onto the context's stream and waits on the
-  // caller's event: recording that into a graph is not supported.  The
-  // one-stream modes make plain launches (and an event record) on one stream
-  // and may be captured.
-  if (two_streams && (asp::capturing(attn_stream) || asp::capturing(sel_stream))) return ASP_ERR_UNSUPPORTED;
   const StepLayout lay = step_layout(s);
   if (ws == nullptr || ws_bytes < lay.total) return ASP_ERR_WORKSPACE;
   unsigned char* base = static_cast<unsigned char*>(ws);
@@ -513,7 +526,7 @@ asp_status asp_step(asp_context* ctx, const asp_dims* dims, const asp_cfg* cfg, 
   // waits: when the GPU is idle (the first steps of a run) it then starts
   // right after the predictor instead of after the host's waits, and the next
   // step's predictor, queued behind it, is not held back.
-  ASP_TRY_HIP(hipStreamWaitEvent(attn_stream, idx_cur_ready, 0));
+  if (idx_cur_ready != nullptr) ASP_TRY_HIP(hipStreamWaitEvent(attn_stream, idx_cur_ready, 0));
   ASP_TRY_HIP(asp::launch_predict(s, q_hist, hist_newest, hist_len, q_cur, q_pred, attn_stream, ctx->pred));
   ASP_TRY_HIP(asp::launch_attend(s, q_cur, k, v, seq_lens, idx_cur, n_sel_cur, out, partials, attn_stream));
   ASP_TRY_HIP(hipStreamWaitEvent(ctx->score, ctx->pred, 0));

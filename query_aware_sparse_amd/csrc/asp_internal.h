@@ -104,6 +104,14 @@ inline bool capturing(hipStream_t st) {
   return hipStreamIsCapturing(st, &cs) == hipSuccess && cs == hipStreamCaptureStatusActive;
 }
 
+// The id of the capture `st` takes part in, 0 when it is not being captured.
+inline unsigned long long capture_id(hipStream_t st) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  unsigned long long id = 0;
+  if (hipStreamGetCaptureInfo(st, &cs, &id) != hipSuccess || cs != hipStreamCaptureStatusActive) return 0;
+  return id;
+}
+
 // Launch that records `done` (nullable) when the kernel completes.  The event
 // rides on the kernel's own completion signal (hipExtLaunchKernelGGL), so it
 // costs no extra queue packet.  While `st` is being captured into a graph the

@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
         "asp_workspace_size", "asp_status_string", "asp_push_query", "asp_predict_query", "asp_score_keys",
         "asp_select_topc", "asp_score_candidates", "asp_select_candidates", "asp_sparse_decode", "asp_step",
         "asp_selection_overlap", "asp_context_create", "asp_context_destroy", "asp_sparse_decode_static",
-        "asp_check_device_args", "asp_page_summary_size",
+        "asp_check_device_args", "asp_context_join", "asp_page_summary_size",
         "asp_page_summary",
         "asp_page_scores", "asp_page_select_workspace_size", "asp_page_select"])
 
@@ -50,6 +50,7 @@ def test_context_argument_checks(lib):
     assert h.value is None  # *ctx is cleared on failure
     assert lib.asp_context_create(0, 0x80000000, ctypes.byref(h)) == 1
     assert lib.asp_context_destroy(None) == 0
+    assert lib.asp_context_join(None, None) == 1
 
 
 def test_status_strings(lib):

@@ -8,7 +8,9 @@ synchronisation between replays; after every replay the attention output,
 the selection and the query ring must equal, bit for bit, the same entry
 points run eagerly on a second copy of the state.  The same holds for
 asp_step in its one-stream pipelined mode (two steps captured, with their
-selection events), while a two-stream asp_step refuses capture with
+selection events) and in its two-stream mode (two layers in rotation, two
+steps each, one context joined back before the capture ends).  A two-stream
+step whose selection stream is capturing into another graph is refused with
 ASP_ERR_UNSUPPORTED and enqueues nothing.
 """
 import numpy as np
@@ -205,26 +207,102 @@ def test_captured_one_stream_asp_step_replays_match_eager(wl_name):
             np.testing.assert_array_equal(np_(gs["n_sel"][i]), np_(es["n_sel"][i]), err_msg="replay %d n" % rep)
 
 
-def test_two_stream_asp_step_refuses_capture():
+@pytest.mark.parametrize("ctx_flags", [A.CTX_SCORE_ALL_CUS, 0], ids=["all-cus", "masked"])
+@pytest.mark.parametrize("wl_name", ["g4-recent", "g8-d64-w64"])
+def test_captured_two_stream_steps_replay_match_eager(wl_name, ctx_flags):
+    # Two layers, each bootstrapped eagerly; then two pipelined two-stream
+    # steps of each layer (layers in rotation, one shared context) captured
+    # with attn as the origin: the first steps order themselves after the
+    # selection they read by the graph's replay order (no idx_cur_ready), the
+    # second ones wait for the events the first recorded in the capture; the
+    # context's stream and sel join attn before the capture ends.  Every
+    # replay, with new queries, equals the same steps made eagerly on copies.
+    require_gpu()
+    wl = SMALL_STEP_CASES[wl_name]
+    L, n_rep = 2, 3
+    probs = [Problem(wl, kv_device=DEV, layer=l, n_steps=2 * n_rep + 2, lens=STEP_LENS.get(wl_name))
+             for l in range(L)]
+    for p in probs:
+        p.fill_history()
+    torch.cuda.synchronize()
+    t0 = wl.history_steps
+    gs = [_step_state(p) for p in probs]
+    es = [_step_state(p) for p in probs]
+    attn, sel = torch.cuda.Stream(), torch.cuda.Stream()
+    attn.wait_stream(torch.cuda.current_stream())
+    for l, p in enumerate(probs):  # bootstrap steps (selection 1), eager on both copies
+        q0 = p.queries[t0].to(DEV)
+        for st in (gs[l], es[l]):
+            _asp_step(p, st, q0, 0, attn, bootstrap=True)
+    torch.cuda.synchronize()
+    shape = (wl.batch, wl.n_q_heads, wl.head_dim)
+    q_buf = [[torch.empty(shape, device=DEV) for _ in range(2)] for _ in range(L)]
+    ctx_g, ctx_e = A.AspContext(flags=ctx_flags), A.AspContext(flags=ctx_flags)
+
+    def two_stream_step(p, st, q, cur, ctx, wait):
+        nxt = 1 - cur
+        A.asp_step(p.dims, p.cfg, q, st["q_hist"], st["newest"], st["length"], p.k, p.v, p.seq_lens,
+                   st["idx"][cur], st["n_sel"][cur], st["idx"][nxt], st["n_sel"][nxt], st["out"], st["ws"],
+                   attn_stream=attn, sel_stream=sel, ctx=ctx, idx_cur_ready=st["ev"][cur] if wait else None,
+                   idx_next_ready=st["ev"][nxt])
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=attn):
+        for j, cur in enumerate((1, 0)):  # selection 1 -> 0, then 0 -> 1
+            for l, p in enumerate(probs):
+                two_stream_step(p, gs[l], q_buf[l][j], cur, ctx_g, wait=j > 0)
+        ctx_g.join(attn)
+        attn.wait_stream(sel)
+    torch.cuda.synchronize()
+    for rep in range(n_rep):
+        qs = [[p.queries[t0 + 1 + 2 * rep + j].to(DEV) for j in range(2)] for p in probs]
+        for l in range(L):
+            for j in range(2):
+                q_buf[l][j].copy_(qs[l][j])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        attn.wait_stream(torch.cuda.current_stream())
+        for j, cur in enumerate((1, 0)):
+            for l, p in enumerate(probs):
+                two_stream_step(p, es[l], qs[l][j], cur, ctx_e, wait=True)
+        attn.wait_stream(sel)
+        torch.cuda.synchronize()
+        for l in range(L):
+            for name in ("out", "q_hist", "newest", "length"):
+                np.testing.assert_array_equal(np_(gs[l][name]), np_(es[l][name]),
+                                              err_msg="replay %d layer %d %s" % (rep, l, name))
+            for i in (0, 1):
+                np.testing.assert_array_equal(np_(gs[l]["idx"][i]), np_(es[l]["idx"][i]),
+                                              err_msg="replay %d layer %d idx" % (rep, l))
+                np.testing.assert_array_equal(np_(gs[l]["n_sel"][i]), np_(es[l]["n_sel"][i]),
+                                              err_msg="replay %d layer %d n_sel" % (rep, l))
+    ctx_g.close()
+    ctx_e.close()
+
+
+def test_two_stream_step_refuses_a_selection_stream_in_another_capture():
+    # sel_stream capturing while attn_stream is not: refused before anything is enqueued
     require_gpu()
     wl = SMALL_STEP_CASES["g4-recent"]
     p = Problem(wl, kv_device=DEV, n_steps=3, lens=STEP_LENS.get("g4-recent"))
     p.fill_history()
     st = _step_state(p)
-    side, sel = torch.cuda.Stream(), torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
+    attn, sel = torch.cuda.Stream(), torch.cuda.Stream()
+    attn.wait_stream(torch.cuda.current_stream())
     q = p.queries[wl.history_steps].to(DEV)
-    _asp_step(p, st, q, 0, side, bootstrap=True)
+    _asp_step(p, st, q, 0, attn, bootstrap=True)
     torch.cuda.synchronize()
     ctx = A.AspContext()
     before = np_(st["idx"][0]).copy()
     g = torch.cuda.CUDAGraph()
     with pytest.raises(A.AspError) as e:
-        with torch.cuda.graph(g, stream=side):
+        with torch.cuda.graph(g, stream=sel):
             A.asp_step(p.dims, p.cfg, q, st["q_hist"], st["newest"], st["length"], p.k, p.v, p.seq_lens,
                        st["idx"][1], st["n_sel"][1], st["idx"][0], st["n_sel"][0], st["out"], st["ws"],
-                       attn_stream=side, sel_stream=sel, ctx=ctx, idx_cur_ready=st["ev"][1],
+                       attn_stream=attn, sel_stream=sel, ctx=ctx, idx_cur_ready=st["ev"][1],
                        idx_next_ready=st["ev"][0])
     assert e.value.status == 2  # ASP_ERR_UNSUPPORTED
     torch.cuda.synchronize()
     np.testing.assert_array_equal(np_(st["idx"][0]), before)  # nothing ran
+    ctx.close()
