@@ -33,7 +33,7 @@ def assert_pred_close(gpu: np.ndarray, orc: np.ndarray, rel: float = 1e-4):
     B, Hq, D = orc.shape
     err = np.abs(gpu.astype(np.float64) - orc).max(axis=2)
     ref = np.abs(orc).max(axis=2)
-    bad = err > rel * np.maximum(ref, 1e-30)
+    bad = ~(err <= rel * np.maximum(ref, 1e-30))  # a NaN on either side counts as a mismatch
     assert not bad.any(), "predictor mismatch at %s: err %s ref %s" % (np.argwhere(bad)[:5], err[bad][:5], ref[bad][:5])
 
 

@@ -7,12 +7,18 @@ window 4-32, ragged lengths that include 0 and t_cap, sometimes the newest-token
 window.  Per case:
   * ring push and predictor against the oracle (push bit-exact, prediction
     within 1e-4 of max|q| per head);
-  * scores within 1e-5 of max|score| per unit;
+  * scores within the bound their arithmetic guarantees: per key, 2^-15 of
+    the largest sum over the group's heads of |q_d k_d| (q carried as two bf16
+    terms, fp32 accumulation); the fixed-shape tests use the tighter
+    1e-5 * max|score| per unit, which a unit with one or a few keys whose
+    score cancels need not meet;
   * the top-C selection bit-exact against the oracle on the GPU's own fp32
     scores, and the candidate route (with a random threshold hint) equal to it
     bit for bit;
   * the attention over that selection within 1e-2 (observed ~1e-6).
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -24,7 +30,7 @@ from asp_testutil import assert_pred_close, dims_for, kv_np, np_, require_gpu
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-N_CASES = 64
+N_CASES = int(os.environ.get("ASP_RANDOM_SHAPES", "64"))  # more cases: set the variable
 
 
 def draw(seed: int) -> dict:
@@ -84,12 +90,18 @@ def test_random_shape_end_to_end(seed):
     A.asp_score_keys(dims, q_pred, kd, lens, scores)
     got = np_(scores).astype(np.float64)
     ref = oracle.score(np_(q_pred), kv_np(k), lens_np)
+    qa = np.abs(np_(q_pred).astype(np.float64))
+    ka = np.abs(k.float().numpy().astype(np.float64))
     for b in range(B):
         T = int(lens_np[b])
-        if T == 0:
-            continue
-        err = np.abs(got[b, :, :T] - ref[b, :, :T]).max(axis=1)
-        assert (err <= 1e-5 * np.abs(ref[b, :, :T]).max(axis=1)).all(), (b, err)
+        for g in range(Hkv):
+            # the arithmetic's bound per key: q is carried as two bf16 terms
+            # (residual <= 2^-18 |q|) and 2D exact products accumulate in
+            # fp32 (<= 2D 2^-24 of their magnitude), together <= 2^-15 of
+            # max over the group's heads of sum_d |q_d k_d|
+            mag = (ka[b, g, :T] @ qa[b, g * G:(g + 1) * G].T).max(axis=1) if T else np.zeros(0)
+            err = np.abs(got[b, g, :T] - ref[b, g, :T])
+            assert (err <= 2.0 ** -15 * mag + 1e-30).all(), (b, g, err.max(), mag[err.argmax()] if T else 0)
     idx = torch.full((B, Hkv, C), -9, dtype=torch.int32, device=DEV)
     n_sel = torch.full((B, Hkv), -9, dtype=torch.int32, device=DEV)
     A.asp_select_topc(dims, cfg, scores, lens, idx, n_sel)

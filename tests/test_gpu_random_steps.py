@@ -6,6 +6,8 @@ of test_gpu_random_shapes: group, head_dim, K/V dtype, t_cap, C, window, a ring
 that is or is not full when the steps start, ragged lengths including 0 and
 t_cap, sometimes the newest-token window.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -14,7 +16,7 @@ from query_aware_sparse_amd import workload as wk
 from test_gpu_step import DEV, Problem, _manual_run, _step_run
 
 pytestmark = pytest.mark.gpu
-N_CASES = 32
+N_CASES = int(os.environ.get("ASP_RANDOM_STEPS", "32"))  # more cases: set the variable
 
 
 def draw(seed: int):
