@@ -61,7 +61,7 @@ typedef enum {
   ASP_OK = 0,
   ASP_ERR_INVALID_ARG = 1, /* a dimension, config value or pointer is invalid */
   ASP_ERR_UNSUPPORTED = 2, /* valid in principle, not implemented (e.g. head_dim 96) */
-  ASP_ERR_WORKSPACE = 3,   /* ws is NULL or ws_bytes < asp_workspace_size(...) */
+  ASP_ERR_WORKSPACE = 3,   /* ws is NULL, not 16-byte aligned, or ws_bytes < asp_workspace_size(...) */
   ASP_ERR_HIP = 4,         /* a HIP launch / event / stream call failed */
   ASP_ERR_HOST_MEMORY = 5, /* a host allocation failed (asp_context_create) */
   ASP_ERR_SCRATCH = 6      /* more scratch than ASP_STATIC_SCRATCH_BYTES (asp_sparse_decode_static) */

@@ -221,7 +221,7 @@ const char* asp_status_string(asp_status status) {
     case ASP_OK: return "ok";
     case ASP_ERR_INVALID_ARG: return "invalid argument (dimension, configuration value or null pointer)";
     case ASP_ERR_UNSUPPORTED: return "unsupported shape (head_dim must be 64 or 128, GQA group 1, 2, 4 or 8)";
-    case ASP_ERR_WORKSPACE: return "workspace missing or smaller than asp_workspace_size()";
+    case ASP_ERR_WORKSPACE: return "workspace missing, not 16-byte aligned or smaller than asp_workspace_size()";
     case ASP_ERR_HIP: return "a HIP kernel launch, event or stream call failed";
     case ASP_ERR_HOST_MEMORY: return "host memory allocation failed";
     case ASP_ERR_SCRATCH:
@@ -236,7 +236,8 @@ asp_status asp_push_query(const asp_dims* dims, const asp_cfg* cfg, const float*
   asp_status st = check_all(dims, cfg, &s);
   if (st != ASP_OK) return st;
   if (!q_cur || !q_hist || !hist_newest || !hist_len) return ASP_ERR_INVALID_ARG;
-  if (!aligned16(q_cur) || !aligned16(q_hist)) return ASP_ERR_INVALID_ARG;
+  if (!aligned16(q_cur) || !aligned16(q_hist) || !aligned4(hist_newest) || !aligned4(hist_len))
+    return ASP_ERR_INVALID_ARG;
   return hip_status(asp::launch_push(s, q_cur, q_hist, hist_newest, hist_len, stream));
 }
 
@@ -247,7 +248,8 @@ asp_status asp_predict_query(const asp_dims* dims, const asp_cfg* cfg, const flo
   asp_status st = check_all(dims, cfg, &s);
   if (st != ASP_OK) return st;
   if (!q_hist || !hist_newest || !hist_len || !q_pred) return ASP_ERR_INVALID_ARG;
-  if (!aligned16(q_hist) || !aligned4(q_pred)) return ASP_ERR_INVALID_ARG;
+  if (!aligned16(q_hist) || !aligned4(q_pred) || !aligned4(hist_newest) || !aligned4(hist_len))
+    return ASP_ERR_INVALID_ARG;
   return hip_status(asp::launch_predict(s, const_cast<float*>(q_hist), hist_newest, hist_len, nullptr, q_pred,
                                         stream));
 }
@@ -258,7 +260,8 @@ asp_status asp_score_keys(const asp_dims* dims, const float* q_pred, const void*
   asp_status st = check_dims(dims, &s);
   if (st != ASP_OK) return st;
   if (!q_pred || !k || !seq_lens || !scores) return ASP_ERR_INVALID_ARG;
-  if (!aligned16(k) || !aligned4(q_pred) || !aligned4(scores) || !aligned16(hist)) return ASP_ERR_INVALID_ARG;
+  if (!aligned16(k) || !aligned4(q_pred) || !aligned4(seq_lens) || !aligned4(scores) || !aligned16(hist))
+    return ASP_ERR_INVALID_ARG;
   if (hist != nullptr)  // the score launch adds to the histograms
     ASP_TRY_HIP(asp::launch_clear_u32(hist, (size_t)s.B * s.Hkv * asp::HIST_BINS, stream));
   return hip_status(asp::launch_score(s, q_pred, k, seq_lens, scores, hist, stream));
@@ -271,7 +274,8 @@ asp_status asp_select_topc(const asp_dims* dims, const asp_cfg* cfg, const float
   asp_status st = check_all(dims, cfg, &s);
   if (st != ASP_OK) return st;
   if (!scores || !seq_lens || !idx || !n_sel) return ASP_ERR_INVALID_ARG;
-  if (!aligned4(scores) || !aligned16(hist)) return ASP_ERR_INVALID_ARG;
+  if (!aligned4(scores) || !aligned16(hist) || !aligned4(seq_lens) || !aligned4(idx) || !aligned4(n_sel))
+    return ASP_ERR_INVALID_ARG;
   const size_t need = ws_bytes_for(s, ASP_OP_SELECT);
   if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return ASP_ERR_WORKSPACE;
   return hip_status(asp::launch_select(s, scores, hist, seq_lens, idx, n_sel, nullptr, nullptr, ws, stream));
@@ -340,9 +344,11 @@ asp_status asp_sparse_decode(const asp_dims* dims, const asp_cfg* cfg, const flo
   if (st != ASP_OK) return st;
   if (!q || !k || !v || !idx || !n_sel || !out) return ASP_ERR_INVALID_ARG;
   if (s.R > 0 && seq_lens == nullptr) return ASP_ERR_INVALID_ARG;
-  if (!aligned16(k) || !aligned16(v) || !aligned4(q) || !aligned4(out)) return ASP_ERR_INVALID_ARG;
+  if (!aligned16(k) || !aligned16(v) || !aligned4(q) || !aligned4(out) || !aligned4(seq_lens) || !aligned4(idx) ||
+      !aligned4(n_sel))
+    return ASP_ERR_INVALID_ARG;
   const size_t need = ws_bytes_for(s, ASP_OP_DECODE);
-  if (ws == nullptr || ws_bytes < need) return ASP_ERR_WORKSPACE;
+  if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return ASP_ERR_WORKSPACE;
   return hip_status(asp::launch_attend(s, q, k, v, seq_lens, idx, n_sel, out, ws, stream));
 }
 
@@ -354,7 +360,9 @@ asp_status asp_sparse_decode_static(const asp_dims* dims, const asp_cfg* cfg, co
   if (st != ASP_OK) return st;
   if (!q || !k || !v || !idx || !n_sel || !out) return ASP_ERR_INVALID_ARG;
   if (s.R > 0 && seq_lens == nullptr) return ASP_ERR_INVALID_ARG;
-  if (!aligned16(k) || !aligned16(v) || !aligned4(q) || !aligned4(out)) return ASP_ERR_INVALID_ARG;
+  if (!aligned16(k) || !aligned16(v) || !aligned4(q) || !aligned4(out) || !aligned4(seq_lens) || !aligned4(idx) ||
+      !aligned4(n_sel))
+    return ASP_ERR_INVALID_ARG;
   if (asp::attend_partials_bytes(s) > (size_t)ASP_STATIC_SCRATCH_BYTES) return ASP_ERR_SCRATCH;
   void* partials = nullptr;
   st = scratch_on_current_device(&partials);
@@ -467,7 +475,9 @@ asp_status asp_step(asp_context* ctx, const asp_dims* dims, const asp_cfg* cfg, 
   if (!q_cur || !q_hist || !hist_newest || !hist_len || !k || !v || !seq_lens || !idx_next || !n_sel_next || !out)
     return ASP_ERR_INVALID_ARG;
   if ((idx_cur == nullptr) != (n_sel_cur == nullptr)) return ASP_ERR_INVALID_ARG;
-  if (!aligned16(q_cur) || !aligned16(q_hist) || !aligned16(k) || !aligned16(v) || !aligned4(out))
+  if (!aligned16(q_cur) || !aligned16(q_hist) || !aligned16(k) || !aligned16(v) || !aligned4(out) ||
+      !aligned4(hist_newest) || !aligned4(hist_len) || !aligned4(seq_lens) || !aligned4(idx_cur) ||
+      !aligned4(n_sel_cur) || !aligned4(idx_next) || !aligned4(n_sel_next))
     return ASP_ERR_INVALID_ARG;
   if (!aligned16(ws)) return ASP_ERR_WORKSPACE;
   const bool pipelined = idx_cur != nullptr;

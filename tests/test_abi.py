@@ -180,6 +180,51 @@ def test_null_pointers_and_short_workspace_rejected(lib):
                         None, None) == 1
 
 
+# Array arguments per entry point after (dims[, cfg]): "16" must be 16-byte
+# aligned, "4" 4-byte aligned, "ws" is a workspace (16), "n" a byte count or
+# other scalar, "-" an optional pointer left NULL.
+ALIGNED_ARGS = {
+    "asp_push_query": ("dc", ["16", "16", "4", "4"]),
+    "asp_predict_query": ("dc", ["16", "4", "4", "4"]),
+    "asp_score_keys": ("d", ["4", "16", "4", "4", "-"]),
+    "asp_select_topc": ("dc", ["4", "-", "4", "4", "4", "ws", "n"]),
+    "asp_score_candidates": ("dc", ["4", "16", "4", "ws", "n"]),
+    "asp_select_candidates": ("dc", ["4", "16", "4", "4", "4", "ws", "n"]),
+    "asp_selection_overlap": ("dc", ["4", "4", "4", "4", "4"]),
+    "asp_sparse_decode": ("dc", ["4", "16", "16", "4", "4", "4", "4", "ws", "n"]),
+    "asp_sparse_decode_static": ("dc", ["4", "16", "16", "4", "4", "4", "4"]),
+    # pipelined on one stream: q_cur .. n_sel_next, out, ws, ws_bytes
+    "asp_step": ("xdc", ["16", "16", "4", "4", "16", "16", "4", "4", "4", "4", "4", "4", "ws", "n"]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ALIGNED_ARGS))
+def test_every_misaligned_array_is_rejected_before_any_launch(lib, name):
+    # One argument at a time moved off its alignment (by 2 bytes for 4-byte
+    # arrays, by 4 for 16-byte ones): ASP_ERR_INVALID_ARG, or ASP_ERR_WORKSPACE
+    # for a workspace, before anything reaches HIP (no GPU is needed here).
+    d, c = _dims(), A.Cfg(16, 2048, 1e-2)
+    lead, kinds = ALIGNED_ARGS[name]
+    fn = getattr(lib, name)
+    for i, kind in enumerate(kinds):
+        if kind in ("n", "-"):
+            continue
+        args = []
+        for j, kj in enumerate(kinds):
+            if kj == "n":
+                args.append(1 << 40)
+            elif kj == "-":
+                args.append(None)
+            elif j == i:
+                args.append(ctypes.c_void_p(4096 + (2 if kj == "4" else 4)))
+            else:
+                args.append(ctypes.c_void_p(4096))
+        head = {"x": None, "d": ctypes.byref(d), "c": ctypes.byref(c)}
+        tail = [None] * (4 if name == "asp_step" else 1)  # streams (and the step's events)
+        got = fn(*([head[ch] for ch in lead] + args + tail))
+        assert got == (3 if kind == "ws" else 1), (name, i, kind, got)
+
+
 def test_device_argument_check_rejects_bad_host_arguments(lib):
     # rejected on the host before any HIP call
     d, c = _dims(), A.Cfg(16, 2048, 1e-2)
