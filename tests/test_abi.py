@@ -181,8 +181,10 @@ def test_null_pointers_and_short_workspace_rejected(lib):
 
 
 # Array arguments per entry point after (dims[, cfg]): "16" must be 16-byte
-# aligned, "4" 4-byte aligned, "ws" is a workspace (16), "n" a byte count or
-# other scalar, "-" an optional pointer left NULL.
+# aligned, "4" 4-byte aligned, "o4" 4-byte aligned and may be NULL here (the
+# sequence lengths of an attention without the newest-token window), "ws" is a
+# workspace (16), "n" a byte count or other scalar, "-" an optional pointer
+# left NULL.
 ALIGNED_ARGS = {
     "asp_push_query": ("dc", ["16", "16", "4", "4"]),
     "asp_predict_query": ("dc", ["16", "4", "4", "4"]),
@@ -191,23 +193,25 @@ ALIGNED_ARGS = {
     "asp_score_candidates": ("dc", ["4", "16", "4", "ws", "n"]),
     "asp_select_candidates": ("dc", ["4", "16", "4", "4", "4", "ws", "n"]),
     "asp_selection_overlap": ("dc", ["4", "4", "4", "4", "4"]),
-    "asp_sparse_decode": ("dc", ["4", "16", "16", "4", "4", "4", "4", "ws", "n"]),
-    "asp_sparse_decode_static": ("dc", ["4", "16", "16", "4", "4", "4", "4"]),
+    "asp_sparse_decode": ("dc", ["4", "16", "16", "o4", "4", "4", "4", "ws", "n"]),
+    "asp_sparse_decode_static": ("dc", ["4", "16", "16", "o4", "4", "4", "4"]),
     # pipelined on one stream: q_cur .. n_sel_next, out, ws, ws_bytes
     "asp_step": ("xdc", ["16", "16", "4", "4", "16", "16", "4", "4", "4", "4", "4", "4", "ws", "n"]),
 }
 
 
 @pytest.mark.parametrize("name", sorted(ALIGNED_ARGS))
-def test_every_misaligned_array_is_rejected_before_any_launch(lib, name):
+@pytest.mark.parametrize("fault", ["misaligned", "null"])
+def test_every_bad_array_pointer_is_rejected_before_any_launch(lib, name, fault):
     # One argument at a time moved off its alignment (by 2 bytes for 4-byte
-    # arrays, by 4 for 16-byte ones): ASP_ERR_INVALID_ARG, or ASP_ERR_WORKSPACE
-    # for a workspace, before anything reaches HIP (no GPU is needed here).
+    # arrays, by 4 for 16-byte ones), or one required pointer NULL:
+    # ASP_ERR_INVALID_ARG, or ASP_ERR_WORKSPACE for a workspace, before
+    # anything reaches HIP (no GPU is needed here).
     d, c = _dims(), A.Cfg(16, 2048, 1e-2)
     lead, kinds = ALIGNED_ARGS[name]
     fn = getattr(lib, name)
     for i, kind in enumerate(kinds):
-        if kind in ("n", "-"):
+        if kind in ("n", "-") or (fault == "null" and kind == "o4"):
             continue
         args = []
         for j, kj in enumerate(kinds):
@@ -216,13 +220,13 @@ def test_every_misaligned_array_is_rejected_before_any_launch(lib, name):
             elif kj == "-":
                 args.append(None)
             elif j == i:
-                args.append(ctypes.c_void_p(4096 + (2 if kj == "4" else 4)))
+                args.append(None if fault == "null" else ctypes.c_void_p(4096 + (2 if kj in ("4", "o4") else 4)))
             else:
                 args.append(ctypes.c_void_p(4096))
         head = {"x": None, "d": ctypes.byref(d), "c": ctypes.byref(c)}
         tail = [None] * (4 if name == "asp_step" else 1)  # streams (and the step's events)
         got = fn(*([head[ch] for ch in lead] + args + tail))
-        assert got == (3 if kind == "ws" else 1), (name, i, kind, got)
+        assert got == (3 if kind == "ws" else 1), (name, fault, i, kind, got)
 
 
 def test_device_argument_check_rejects_bad_host_arguments(lib):
