@@ -446,6 +446,8 @@ def main() -> int:
         ev1.record(attn)
         torch.cuda.synchronize()
         wall = time.perf_counter() - w0
+        if args.hold_us > 0:
+            hold(attn, 1.0)  # a marker in kernel traces: the timed steps end here
         for i in range(args.warmup + args.steps):  # the layers' state moves on
             lay = layers[i % L]
             lay["cur"], lay["t"] = 1 - lay["cur"], lay["t"] + 1

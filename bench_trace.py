@@ -4,9 +4,10 @@ on the machine that took them).
   python3 bench_trace.py trace DIR OUT.json
       DIR holds a --kernel-trace [--stats] run of bench.py with --hold-us.
       Per kernel: the launches of the timed steps (from the end of the
-      bench_hold kernel to 1 ms after the last step score launch, which runs
-      on a queue other than the held attention stream) and those of the
-      per-entry-point timing loops after them (calls, average, median, min,
+      first bench_hold kernel to the start of the short one bench.py launches
+      after the timed steps; for traces without it, to 1 ms after the last
+      step score launch, which runs on a queue other than the held attention
+      stream) and those of the per-entry-point timing loops after them (calls, average, median, min,
       max in us); on the score launches' queue, the median period and the
       median gap between consecutive step score launches, the median time
       from the end of each score launch's own predictor launch to its start
@@ -46,8 +47,11 @@ def trace(d: str, out: str) -> None:
     steps = [k for k in ks if "score_mfma_kernel<" in k[2] and k[2].endswith(", 1>")]
     if holds and steps:
         h_end, attn_q = holds[0][1], holds[0][3]
-        sl = [k for k in steps if k[0] >= h_end and k[3] != attn_q]
-        hi = sl[-1][1] + 1_000_000 if sl else h_end
+        # the timed steps end where bench.py's marker (a second, short hold)
+        # starts; without one, 1 ms after the last step score launch
+        marker = holds[1][0] if len(holds) > 1 else None
+        sl = [k for k in steps if k[0] >= h_end and k[3] != attn_q and (marker is None or k[0] < marker)]
+        hi = marker if marker is not None else (sl[-1][1] + 1_000_000 if sl else h_end)
         in_step, rest = defaultdict(list), defaultdict(list)
         for k in ks:
             if "hold_kernel" in k[2]:
