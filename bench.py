@@ -22,7 +22,10 @@ that the host's issue cost can be told from the GPU's time.
 
 Beside the step, the page-level (Quest) baseline is timed on the same layers
 ("page_baseline"): page scoring with the current query, top C / P pages and
-attention over their tokens, all on one stream (--page-size, 0 skips it).
+attention over their tokens, all on one stream (--page-size, 0 skips it).  So
+is dense decode attention over every cached token ("dense_baseline"): the
+attention entry point given each unit's whole token list (--no-dense-baseline
+skips it; null when the cache is longer than the attention's longest list).
 
 Prints one JSON line on stdout.  Everything else goes to stderr.
 """
@@ -321,6 +324,39 @@ def page_baseline(A, dims, cfg, wl, layers, P, time_entry, out, ws_dec, attn, n)
     return res
 
 
+def dense_baseline(A, dims, wl, layers, time_entry, out, attn, n):
+    """Dense decode attention on the same layers: asp_sparse_decode with each
+    unit's whole token list 0 .. seq_len - 1, so every cached K and V row is
+    read (the full attention the pages compare against).  None when the cache
+    is longer than the longest list the attention takes."""
+    import torch
+    B, Hq, Hkv, D, T = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.t_cap
+    cfg_d = A.Cfg(wl.window, T, wl.lam, 0)
+    need = A.asp_workspace_size(dims, cfg_d, A.OP_DECODE)
+    if need == 0:
+        return None
+    dev = layers[0]["k"].device
+    L = len(layers)
+    idx = torch.arange(T, dtype=torch.int32, device=dev).expand(B, Hkv, T).contiguous()
+    nsel = [lay["seq_lens"].view(B, 1).expand(B, Hkv).contiguous() for lay in layers]  # the whole list
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
+    def q_of(i):
+        lay = layers[i % L]
+        return lay["qs"][lay["t"]]
+
+    us = time_entry(
+        lambda i: A.asp_sparse_decode(dims, cfg_d, q_of(i), layers[i % L]["k"], layers[i % L]["v"],
+                                      layers[i % L]["seq_lens"], idx, nsel[i % L], out, ws, stream=attn), n,
+        lambda i: raw_call(A, "asp_sparse_decode", dims, cfg_d, q_of(i), layers[i]["k"], layers[i]["v"],
+                           layers[i]["seq_lens"], idx, nsel[i], out, ws, ws.numel(), attn))
+    esize = 2 if wl.kv_dtype == "bf16" else 4
+    G = Hq // Hkv
+    lens = [int(x) for x in layers[0]["seq_lens"].tolist()]
+    nbytes = sum(Hkv * (2 * t * D * esize + 4 * t + 2 * G * D * 4) for t in lens)  # K, V, indices, q, out
+    return {"attend_us": round(us, 2), "bytes_per_layer": nbytes, "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -338,6 +374,8 @@ def main() -> int:
     ap.add_argument("--page-size", type=int, default=16,
                     help="page size of the page-level (Quest) baseline timed beside the step (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense-baseline", dest="dense_baseline", action="store_false",
+                    help="skip the dense decode attention over every cached token")
     ap.add_argument("--hold-us", type=float, default=0.0,
                     help="hold the attention stream this long before each timed loop (a bounded wait kernel), so "
                          "that the host queues the timed steps first and the GPU sets their pace; for kernel traces, "
@@ -591,6 +629,15 @@ def main() -> int:
         page = page_baseline(A, dims, cfg, wl, layers, args.page_size, time_entry, out, ws_dec, attn, n)
         log("page baseline: %s" % json.dumps(page))
 
+    dense = None
+    if args.dense_baseline:
+        dense = dense_baseline(A, dims, wl, layers, time_entry, out, attn, n)
+        if dense is not None:
+            # the overlapped step (scan, selection and sparse attention) against dense attention alone
+            dense["step_over_dense"] = round(ms_per_step * 1e3 / dense["attend_us"], 3)
+            dense["sparse_attention_over_dense"] = round(kern["attend_us"] / dense["attend_us"], 3)
+        log("dense baseline: %s" % json.dumps(dense))
+
     cpu = None
     if not args.no_cpu_baseline:
         lay = layers[0]
@@ -618,6 +665,7 @@ def main() -> int:
         "kernels_us": {k_: round(v_, 2) for k_, v_ in kern.items()},
         "roofline": roofline,
         "page_baseline": page,
+        "dense_baseline": dense,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
