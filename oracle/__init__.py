@@ -77,7 +77,11 @@ def _ptr(a: np.ndarray):
 
 
 def _c(a, dtype) -> np.ndarray:
-    return np.ascontiguousarray(a, dtype=dtype)
+    # Rows past a sequence's length may hold any bits (the GPU path leaves them
+    # unwritten, and the oracle never reads them): widening a signalling NaN
+    # there is not worth a warning.
+    with np.errstate(invalid="ignore"):
+        return np.ascontiguousarray(a, dtype=dtype)
 
 
 def _kv(a: np.ndarray):

@@ -281,6 +281,7 @@ def test_captured_two_stream_steps_replay_match_eager(wl_name, ctx_flags):
     ctx_e.close()
 
 
+@pytest.mark.filterwarnings("ignore:The CUDA Graph is empty")  # the refused step enqueues nothing
 def test_two_stream_step_refuses_a_selection_stream_in_another_capture():
     # sel_stream capturing while attn_stream is not: refused before anything is enqueued
     require_gpu()
